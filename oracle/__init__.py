@@ -1,0 +1,103 @@
+"""ctypes front end of the plain-C CPU oracle (oracle.c).
+
+TEST INFRASTRUCTURE ONLY: imported by the test suite, the smoke entry point and
+the benchmark's CPU-baseline leg, never by the library.  It shares no code with
+the HIP path; inputs come from the seeded generator.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "oracle.c")
+LIB = os.path.join(HERE, "liboracle.so")
+
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile oracle.c with gcc (plain C11, OpenMP, no fused multiply-add)."""
+    if force or not os.path.exists(LIB):
+        tmp = LIB + ".tmp"
+        subprocess.check_call(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fPIC",
+                               "-shared", "-D_POSIX_C_SOURCE=200809L", SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, LIB)
+    return LIB
+
+
+def lib():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB):
+            build()
+        L = ctypes.CDLL(LIB)
+        P = ctypes.c_void_p
+        i64 = ctypes.c_int64
+        L.oracle_rows.restype = ctypes.c_int
+        L.oracle_rows.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                  ctypes.c_double, P, P, P, i64, P, i64, P, P, P, P, i64, P, P, P,
+                                  P, i64, P]
+        L.oracle_topk.restype = i64
+        L.oracle_topk.argtypes = [P, i64, i64, P]
+        L.oracle_max_threads.restype = ctypes.c_int
+        L.oracle_set_threads.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"]
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def topk(scores: np.ndarray, k: int) -> np.ndarray:
+    """Top-k of one row of fp32 scores: ascending positions, -1 padded."""
+    s = np.ascontiguousarray(scores, dtype=np.float32)
+    out = np.empty(k, dtype=np.int32)
+    if lib().oracle_topk(_p(s), s.shape[0], k, _p(out)) < 0:
+        raise RuntimeError("oracle_topk failed")
+    return out
+
+
+def run(w: dict, rows=None, want_scores: bool = False, stage_seconds=None):
+    """Run the oracle on the listed query rows of workload `w` (a dict from
+    the synth module).  Returns dict(topk, out, lse[, scores]) with one entry per
+    listed row; out/lse are float64."""
+    sh = w["shape"]
+    mode = 0 if w["mode"] == "decode" else 1
+    T = w["rows"]
+    rows = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    nr = len(rows)
+    tk = np.empty((nr, sh.topk), dtype=np.int32)
+    o = np.empty((nr, sh.num_heads, sh.v_dim), dtype=np.float64)
+    lse = np.empty((nr, sh.num_heads), dtype=np.float64)
+    ctx = np.ascontiguousarray(w["context_lens"], dtype=np.int32)
+    stride = int(ctx.max()) if len(ctx) else 1
+    sc = np.full((nr, max(stride, 1)), np.nan, dtype=np.float32) if want_scores else None
+    st = np.zeros(3, dtype=np.float64)
+    rc = lib().oracle_rows(mode, sh.num_heads, sh.qk_dim, sh.v_dim, sh.idx_heads, sh.idx_dim,
+                           sh.block_size, sh.topk, sh.idx_relu, float(np.float32(sh.softmax_scale)),
+                           _p(w["kv"]), _p(w["idx_k"]), _p(w["block_table"]), w["block_table"].shape[1],
+                           _p(ctx), w["q_start"], _p(w["q"]), _p(w["idx_q"]), _p(w["idx_w"]),
+                           _p(rows), nr, _p(tk), _p(o), _p(lse),
+                           _p(sc) if sc is not None else None, max(stride, 1), _p(st))
+    if rc != 0:
+        raise RuntimeError("oracle_rows failed")
+    if stage_seconds is not None:
+        stage_seconds += st
+    res = dict(topk=tk, out=o, lse=lse, rows=rows)
+    if sc is not None:
+        res["scores"] = sc
+    return res
+
+
+def max_threads() -> int:
+    return lib().oracle_max_threads()
+
+
+def set_threads(n: int) -> None:
+    lib().oracle_set_threads(n)
