@@ -1,0 +1,58 @@
+// Device-side helpers shared by the gfx950 kernels of libsparse_attn.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sa {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+#define SA_LDS __attribute__((address_space(3)))
+
+constexpr int kWave = 64;
+
+// D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).  Lane l supplies row l%32 of A
+// and column l%32 of B, each with the 8 consecutive k values 8*(l/32)..8*(l/32)+7.
+// Lane l receives column l%32 of D at rows 8*(i/4) + 4*(l/32) + i%4, i = 0..15.
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c)
+{
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// row of the 32x32 accumulator held in register i by a lane in half `half` (= lane/32)
+__device__ __forceinline__ constexpr int acc_row(int i, int half)
+{
+    return 8 * (i >> 2) + 4 * half + (i & 3);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    f2 v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
+}
+
+// Order-preserving map from an fp32 score to uint32: a larger key is a larger
+// score; -0 is folded into +0 first so the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    f = f + 0.0f;
+    uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace sa

@@ -1,0 +1,456 @@
+// libsparse_attn: C ABI (include/sparse_attn.h) over the gfx950 kernels.
+//
+// Every check runs before the first HIP call; the library never allocates,
+// never synchronises and keeps no mutable global state.  Work is queued on the
+// caller's stream in this order:
+//   decode : indexer scan -> per-row top-k -> split attention -> split merge
+//   prefill: per chunk of rows { indexer tile scan -> per-row top-k },
+//            then attention over all rows (split + merge only when k > 2048)
+// The decode/prefill separation over one cache and one index format follows
+// "Day-0 Adaptation: Running Trillion-Parameter Models on Domestic AI
+// Accelerators", sections 3.1 and 3.3.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+
+#include "../../include/sparse_attn.h"
+#include "attention.hpp"
+#include "indexer.hpp"
+#include "topk.hpp"
+
+namespace {
+
+using namespace sa;
+
+constexpr int kMaxTopk = 16384;
+constexpr int kTargetAttnBlocks = 256;        // one attention workgroup per CU of an MI355X
+constexpr int kTargetIndexerWaves = 4096;     // 16 waves per CU for the decode key scan
+constexpr size_t kPrefillScoreBudget = size_t(256) << 20;  // bytes of scores per prefill chunk
+constexpr size_t kPrefillPartialBudget = size_t(256) << 20;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+int ilog2(int x)
+{
+    int l = 0;
+    while ((1 << l) < x) ++l;
+    return l;
+}
+
+bool is_pow2(int x) { return x > 0 && (x & (x - 1)) == 0; }
+
+sa_status check_params(const sa_params *p)
+{
+    if (!p) return SA_ERR_NULL;
+    if (p->num_heads < 1 || p->qk_dim < 1 || p->v_dim < 1 || p->v_dim > p->qk_dim || p->idx_heads < 1 ||
+        p->idx_dim < 1 || p->block_size < 1 || p->topk < 1 || !std::isfinite(p->softmax_scale) ||
+        (p->idx_relu != 0 && p->idx_relu != 1) || (p->out_dtype != SA_OUT_F32 && p->out_dtype != SA_OUT_BF16))
+        return SA_ERR_SHAPE;
+    const bool attn_family = (p->qk_dim == 576 && p->v_dim == 512) || (p->qk_dim == 64 && p->v_dim == 64);
+    const bool idx_family = p->idx_dim == 128 || p->idx_dim == 32;
+    if (!attn_family || !idx_family || p->num_heads > 128 || p->idx_heads > 64 || !is_pow2(p->block_size) ||
+        p->block_size > 1024 || p->topk > kMaxTopk)
+        return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+sa_status check_cache(const sa_params *p, const sa_paged_cache *c, bool need_kv, bool need_idx, bool need_ctx)
+{
+    if (!c) return SA_ERR_NULL;
+    if ((need_kv && !c->kv) || (need_idx && !c->idx_k) || !c->block_table || (need_ctx && !c->context_lens))
+        return SA_ERR_NULL;
+    if (c->num_blocks < 1 || c->max_blocks_per_seq < 1) return SA_ERR_SHAPE;
+    if (c->num_blocks * (int64_t)p->block_size > INT32_MAX) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+// ------------------------------------------------------------------ plans --
+struct DecodePlan {
+    int64_t score_stride;
+    int splits, tokens_per_split, keys_per_wave;
+    size_t off_scores, off_part_o, off_part_ml, total;
+};
+
+DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
+{
+    DecodePlan d{};
+    d.score_stride = round_up(max_ctx > 0 ? max_ctx : 1, 64);
+    const int k = p->topk;
+    int splits = (kTargetAttnBlocks + batch - 1) / batch;
+    splits = std::max(1, std::min(splits, (k + 31) / 32));
+    splits = std::max(splits, (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens);
+    int tps = (int)round_up((k + splits - 1) / splits, 32);
+    tps = std::min(tps, kAttnMaxSplitTokens);
+    splits = (k + tps - 1) / tps;
+    d.splits = splits;
+    d.tokens_per_split = tps;
+    const int64_t keys = (int64_t)batch * std::max(max_ctx, 1);
+    int64_t kpw = keys / kTargetIndexerWaves;
+    int kp = 32;
+    while (kp < 1024 && (int64_t)kp * 2 <= kpw) kp *= 2;
+    d.keys_per_wave = kp;
+    size_t off = 0;
+    d.off_scores = off;
+    off = align_up(off + (size_t)batch * d.score_stride * 4, kAlign);
+    d.off_part_o = off;
+    if (splits > 1) {
+        off = align_up(off + (size_t)batch * splits * p->num_heads * p->v_dim * 4, kAlign);
+        d.off_part_ml = off;
+        off = align_up(off + (size_t)batch * splits * p->num_heads * 8, kAlign);
+    } else {
+        d.off_part_ml = off;
+    }
+    d.total = std::max(off, kAlign);
+    return d;
+}
+
+struct PrefillPlan {
+    int64_t score_stride;
+    int chunk_rows;          // rows per indexer/top-k chunk
+    int splits, tokens_per_split;
+    int attn_chunk_rows;     // rows per attention launch when splits > 1
+    size_t off_scores, off_part_o, off_part_ml, total;
+};
+
+PrefillPlan plan_prefill(const sa_params *p, int num_rows, int q_start)
+{
+    PrefillPlan d{};
+    const int64_t ctx = (int64_t)q_start + num_rows;
+    d.score_stride = round_up(ctx, 64);
+    int64_t rows = (int64_t)(kPrefillScoreBudget / (size_t)(d.score_stride * 4));
+    rows = std::max<int64_t>(kPrefillRowsPerBlock, rows / kPrefillRowsPerBlock * kPrefillRowsPerBlock);
+    d.chunk_rows = (int)std::min<int64_t>(rows, round_up(num_rows, kPrefillRowsPerBlock));
+    const int k = p->topk;
+    d.splits = (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens;
+    d.tokens_per_split = (int)round_up((k + d.splits - 1) / d.splits, 32);
+    size_t off = 0;
+    d.off_scores = off;
+    off = align_up(off + (size_t)d.chunk_rows * d.score_stride * 4, kAlign);
+    d.off_part_o = off;
+    d.attn_chunk_rows = num_rows;
+    if (d.splits > 1) {
+        const size_t per_row = (size_t)d.splits * p->num_heads * (p->v_dim * 4 + 8);
+        d.attn_chunk_rows = (int)std::max<size_t>(1, std::min<size_t>(num_rows, kPrefillPartialBudget / per_row));
+        off = align_up(off + (size_t)d.attn_chunk_rows * d.splits * p->num_heads * p->v_dim * 4, kAlign);
+        d.off_part_ml = off;
+        off = align_up(off + (size_t)d.attn_chunk_rows * d.splits * p->num_heads * 8, kAlign);
+    } else {
+        d.off_part_ml = off;
+    }
+    d.total = std::max(off, kAlign);
+    return d;
+}
+
+sa_status check_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, bool kv, bool idx)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!c) return SA_ERR_NULL;
+    s = check_cache(p, c, kv, idx, true);
+    if (s != SA_OK) return s;
+    if (batch < 1 || max_ctx < 0 || (int64_t)max_ctx > (int64_t)c->max_blocks_per_seq * p->block_size)
+        return SA_ERR_SHAPE;
+    return SA_OK;
+}
+
+sa_status check_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, bool kv, bool idx)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!c) return SA_ERR_NULL;
+    s = check_cache(p, c, kv, idx, false);
+    if (s != SA_OK) return s;
+    if (num_rows < 1 || q_start < 0 ||
+        (int64_t)q_start + num_rows > (int64_t)c->max_blocks_per_seq * p->block_size ||
+        (int64_t)q_start + num_rows > INT32_MAX - 64)
+        return SA_ERR_SHAPE;
+    return SA_OK;
+}
+
+sa_status check_ws(const void *ws, size_t have, size_t need)
+{
+    if (!ws) return SA_ERR_NULL;
+    if (have < need) return SA_ERR_WORKSPACE;
+    return SA_OK;
+}
+
+void clear_hip_error() { (void)hipGetLastError(); }
+
+sa_status launched()
+{
+    return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
+}
+
+// --------------------------------------------------------------- launches --
+template <int D, int T>
+void launch_idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
+                       const float *idx_w, float *scores, int64_t stride, int kpw, hipStream_t st)
+{
+    const int per_block = 4 * kpw;
+    dim3 grid((max_ctx + per_block - 1) / per_block, batch);
+    if (grid.x == 0) return;
+    hipLaunchKernelGGL((idx_score_decode_kernel<D, T>), grid, dim3(256), 0, st,
+                       (const uint16_t *)c->idx_k, c->block_table, c->max_blocks_per_seq, ilog2(p->block_size),
+                       c->context_lens, (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, kpw);
+}
+
+void idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
+                const float *idx_w, float *scores, int64_t stride, int kpw, hipStream_t st)
+{
+    const bool two = p->idx_heads > 32;
+    if (p->idx_dim == 128) {
+        if (two) launch_idx_decode<128, 2>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
+        else launch_idx_decode<128, 1>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
+    } else {
+        if (two) launch_idx_decode<32, 2>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
+        else launch_idx_decode<32, 1>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
+    }
+}
+
+template <int D, int T>
+void launch_idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w,
+                        int pos0, int nrows, float *scores, int64_t stride, hipStream_t st)
+{
+    dim3 grid((nrows + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock);
+    hipLaunchKernelGGL((idx_score_prefill_kernel<D, T>), grid, dim3(512), 0, st, (const uint16_t *)c->idx_k,
+                       c->block_table, ilog2(p->block_size), idx_q, idx_w, p->idx_heads, p->idx_relu, pos0, nrows,
+                       scores, stride);
+}
+
+void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w, int pos0,
+                 int nrows, float *scores, int64_t stride, hipStream_t st)
+{
+    const bool two = p->idx_heads > 32;
+    if (p->idx_dim == 128) {
+        if (two) launch_idx_prefill<128, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
+        else launch_idx_prefill<128, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
+    } else {
+        if (two) launch_idx_prefill<32, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
+        else launch_idx_prefill<32, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
+    }
+}
+
+void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st)
+{
+    const int threads = 64 * ((p->num_heads + 31) / 32);
+    dim3 grid(a.splits * (p->v_dim > 256 ? 2 : 1), rows);
+    if (p->qk_dim == 576)
+        hipLaunchKernelGGL((attend_kernel<576, 512>), grid, dim3(threads), 0, st, a);
+    else
+        hipLaunchKernelGGL((attend_kernel<64, 64>), grid, dim3(threads), 0, st, a);
+    if (a.splits > 1) {
+        dim3 cg(p->num_heads, rows);
+        if (p->v_dim == 512)
+            hipLaunchKernelGGL((combine_kernel<512>), cg, dim3(128), 0, st, a.part_o, a.part_ml, a.splits,
+                               p->num_heads, a.out, a.out_bf16, a.lse);
+        else
+            hipLaunchKernelGGL((combine_kernel<64>), cg, dim3(64), 0, st, a.part_o, a.part_ml, a.splits,
+                               p->num_heads, a.out, a.out_bf16, a.lse);
+    }
+}
+
+AttnArgs attn_args(const sa_params *p, const sa_paged_cache *c, const void *q, const int32_t *topk_idx, void *out,
+                   float *lse)
+{
+    AttnArgs a{};
+    a.q = (const uint16_t *)q;
+    a.kv = (const uint16_t *)c->kv;
+    a.block_table = c->block_table;
+    a.topk_idx = topk_idx;
+    a.ctx_lens = c->context_lens;
+    a.out = out;
+    a.lse = lse;
+    a.num_blocks = c->num_blocks;
+    a.num_heads = p->num_heads;
+    a.max_blocks = c->max_blocks_per_seq;
+    a.bs_log2 = ilog2(p->block_size);
+    a.k = p->topk;
+    a.out_bf16 = p->out_dtype == SA_OUT_BF16;
+    a.scale_log2 = p->softmax_scale * 1.4426950408889634f;
+    return a;
+}
+
+sa_status select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
+                        const float *idx_w, int32_t *topk_idx, void *ws, const DecodePlan &d, hipStream_t st)
+{
+    float *scores = (float *)((char *)ws + d.off_scores);
+    if (max_ctx > p->topk)
+        idx_decode(p, c, batch, max_ctx, idx_q, idx_w, scores, d.score_stride, d.keys_per_wave, st);
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
+                       c->context_lens, 0, p->topk, topk_idx);
+    return SA_OK;
+}
+
+void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *q, const int32_t *topk_idx,
+                   void *out, float *lse, void *ws, const DecodePlan &d, hipStream_t st)
+{
+    AttnArgs a = attn_args(p, c, q, topk_idx, out, lse);
+    a.decode = 1;
+    a.tokens_per_split = d.tokens_per_split;
+    a.splits = d.splits;
+    a.part_o = (float *)((char *)ws + d.off_part_o);
+    a.part_ml = (float *)((char *)ws + d.off_part_ml);
+    attend(p, a, batch, st);
+}
+
+void select_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *idx_q,
+                    const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d, hipStream_t st)
+{
+    float *scores = (float *)((char *)ws + d.off_scores);
+    for (int r0 = 0; r0 < num_rows; r0 += d.chunk_rows) {
+        const int nr = std::min(d.chunk_rows, num_rows - r0);
+        const int pos0 = q_start + r0;
+        // rows whose whole context fits in k need no scores
+        if (pos0 + nr > p->topk)
+            idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
+                        idx_w + (int64_t)r0 * p->idx_heads, pos0, nr, scores, d.score_stride, st);
+        hipLaunchKernelGGL(topk_rows_kernel, dim3(nr), dim3(kTopkThreads), 0, st, scores, d.score_stride,
+                           (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk);
+    }
+}
+
+void attend_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *q,
+                    const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d, hipStream_t st)
+{
+    for (int r0 = 0; r0 < num_rows; r0 += d.attn_chunk_rows) {
+        const int nr = std::min(d.attn_chunk_rows, num_rows - r0);
+        AttnArgs a = attn_args(p, c, (const uint16_t *)q + (int64_t)r0 * p->num_heads * p->qk_dim,
+                               topk_idx + (int64_t)r0 * p->topk,
+                               (char *)out + (int64_t)r0 * p->num_heads * p->v_dim * (p->out_dtype ? 2 : 4),
+                               lse ? lse + (int64_t)r0 * p->num_heads : nullptr);
+        a.decode = 0;
+        a.limit_base = q_start + r0;
+        a.tokens_per_split = d.tokens_per_split;
+        a.splits = d.splits;
+        a.part_o = (float *)((char *)ws + d.off_part_o);
+        a.part_ml = (float *)((char *)ws + d.off_part_ml);
+        attend(p, a, nr, st);
+    }
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------- C ABI --
+extern "C" {
+
+int32_t sa_abi_version(void) { return SA_ABI_VERSION; }
+
+const char *sa_status_string(sa_status s)
+{
+    switch (s) {
+    case SA_OK: return "ok";
+    case SA_ERR_NULL: return "required pointer is NULL";
+    case SA_ERR_SHAPE: return "inconsistent or out-of-range sizes";
+    case SA_ERR_UNSUPPORTED: return "parameters outside the compiled kernel families";
+    case SA_ERR_WORKSPACE: return "workspace too small";
+    case SA_ERR_HIP: return "HIP runtime reported a launch error";
+    }
+    return "unknown status";
+}
+
+sa_status sa_decode_workspace_size(const sa_params *p, int32_t batch, int32_t max_ctx, size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    if (batch < 1 || max_ctx < 0) return SA_ERR_SHAPE;
+    *bytes = plan_decode(p, batch, max_ctx).total;
+    return SA_OK;
+}
+
+sa_status sa_prefill_workspace_size(const sa_params *p, int32_t num_rows, int32_t q_start, size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    if (num_rows < 1 || q_start < 0 || (int64_t)q_start + num_rows > INT32_MAX - 64) return SA_ERR_SHAPE;
+    *bytes = plan_prefill(p, num_rows, q_start).total;
+    return SA_OK;
+}
+
+sa_status sparse_attn_select_decode(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                    const void *idx_q, const float *idx_w, int32_t *topk_idx, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_decode(p, c, batch, max_ctx, false, true);
+    if (s != SA_OK) return s;
+    if (!idx_q || !idx_w || !topk_idx) return SA_ERR_NULL;
+    const DecodePlan d = plan_decode(p, batch, max_ctx);
+    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
+    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream);
+    return launched();
+}
+
+sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                    const void *q, const int32_t *topk_idx, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_decode(p, c, batch, max_ctx, true, false);
+    if (s != SA_OK) return s;
+    if (!q || !topk_idx || !out) return SA_ERR_NULL;
+    const DecodePlan d = plan_decode(p, batch, max_ctx);
+    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
+    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream);
+    return launched();
+}
+
+sa_status sparse_attn_decode(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                             const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_decode(p, c, batch, max_ctx, true, true);
+    if (s != SA_OK) return s;
+    if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
+    const DecodePlan d = plan_decode(p, batch, max_ctx);
+    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, st);
+    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, st);
+    return launched();
+}
+
+sa_status sparse_attn_select_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
+                                     const void *idx_q, const float *idx_w, int32_t *topk_idx, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_prefill(p, c, num_rows, q_start, false, true);
+    if (s != SA_OK) return s;
+    if (!idx_q || !idx_w || !topk_idx) return SA_ERR_NULL;
+    const PrefillPlan d = plan_prefill(p, num_rows, q_start);
+    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
+    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream);
+    return launched();
+}
+
+sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
+                                     const void *q, const int32_t *topk_idx, void *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_prefill(p, c, num_rows, q_start, true, false);
+    if (s != SA_OK) return s;
+    if (!q || !topk_idx || !out) return SA_ERR_NULL;
+    const PrefillPlan d = plan_prefill(p, num_rows, q_start);
+    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
+    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream);
+    return launched();
+}
+
+sa_status sparse_attn_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
+                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                              float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_prefill(p, c, num_rows, q_start, true, true);
+    if (s != SA_OK) return s;
+    if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
+    const PrefillPlan d = plan_prefill(p, num_rows, q_start);
+    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, st);
+    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, st);
+    return launched();
+}
+
+}  // extern "C"

@@ -1,0 +1,302 @@
+"""Thin Python binding of libsparse_attn.so (include/sparse_attn.h).
+
+Argument marshalling only: torch supplies device memory and the current stream,
+every step of the computation runs in the library's HIP kernels.  Functions
+carry the C entry points' names.  There is no fallback: if the library is not
+built, or a call returns an error status, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
+
+SA_OK, SA_ERR_NULL, SA_ERR_SHAPE, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE, SA_ERR_HIP = range(6)
+SA_OUT_F32, SA_OUT_BF16 = 0, 1
+
+EXPORTS = (
+    "sa_abi_version", "sa_status_string",
+    "sa_decode_workspace_size", "sparse_attn_decode", "sparse_attn_select_decode", "sparse_attn_attend_decode",
+    "sa_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_select_prefill", "sparse_attn_attend_prefill",
+)
+
+
+class sa_params(ctypes.Structure):
+    _fields_ = [("num_heads", ctypes.c_int32), ("qk_dim", ctypes.c_int32), ("v_dim", ctypes.c_int32),
+                ("idx_heads", ctypes.c_int32), ("idx_dim", ctypes.c_int32), ("block_size", ctypes.c_int32),
+                ("topk", ctypes.c_int32), ("softmax_scale", ctypes.c_float), ("idx_relu", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32)]
+
+
+class sa_paged_cache(ctypes.Structure):
+    _fields_ = [("kv", ctypes.c_void_p), ("idx_k", ctypes.c_void_p), ("num_blocks", ctypes.c_int64),
+                ("block_table", ctypes.c_void_p), ("max_blocks_per_seq", ctypes.c_int32),
+                ("context_lens", ctypes.c_void_p)]
+
+
+class SparseAttnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib():
+    """Load libsparse_attn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with dsa_sparse_attention_02_amd.build.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P = ctypes.c_void_p
+        i32, sz = ctypes.c_int32, ctypes.c_size_t
+        pp, pc = ctypes.POINTER(sa_params), ctypes.POINTER(sa_paged_cache)
+        sig = {
+            "sa_abi_version": (i32, []),
+            "sa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+            "sa_decode_workspace_size": (ctypes.c_int, [pp, i32, i32, ctypes.POINTER(sz)]),
+            "sa_prefill_workspace_size": (ctypes.c_int, [pp, i32, i32, ctypes.POINTER(sz)]),
+            "sparse_attn_decode": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P]),
+            "sparse_attn_select_decode": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, sz, P]),
+            "sparse_attn_attend_decode": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, sz, P]),
+            "sparse_attn_prefill": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P]),
+            "sparse_attn_select_prefill": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, sz, P]),
+            "sparse_attn_attend_prefill": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, sz, P]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return lib().sa_status_string(status).decode()
+
+
+def _check(status: int, where: str):
+    if status != SA_OK:
+        raise SparseAttnError(status, where)
+
+
+@dataclass(frozen=True)
+class Params:
+    num_heads: int
+    qk_dim: int
+    v_dim: int
+    idx_heads: int
+    idx_dim: int
+    block_size: int
+    topk: int
+    softmax_scale: float
+    idx_relu: int = 1
+    out_bf16: bool = False
+
+    @staticmethod
+    def from_shape(shape, out_bf16: bool = False) -> "Params":
+        return Params(shape.num_heads, shape.qk_dim, shape.v_dim, shape.idx_heads, shape.idx_dim,
+                      shape.block_size, shape.topk, float(shape.softmax_scale), shape.idx_relu, out_bf16)
+
+    def c(self) -> sa_params:
+        return sa_params(self.num_heads, self.qk_dim, self.v_dim, self.idx_heads, self.idx_dim, self.block_size,
+                         self.topk, self.softmax_scale, self.idx_relu, SA_OUT_BF16 if self.out_bf16 else SA_OUT_F32)
+
+
+# ------------------------------------------------------------ torch layer --
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t, name, dtypes, shape=None):
+    torch = _torch()
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.dtype not in dtypes:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected one of {dtypes}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+def _bf16_types():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16, torch.uint16)
+
+
+@dataclass
+class PagedCache:
+    """Device tensors of a paged cache: kv [num_blocks][bs][qk_dim] bf16,
+    idx_k [num_blocks][bs][idx_dim] bf16, block_table [seqs][max_blocks] int32,
+    context_lens [seqs] int32 (decode)."""
+    kv: object
+    idx_k: object
+    block_table: object
+    context_lens: object = None
+
+    def c(self) -> sa_paged_cache:
+        torch = _torch()
+        bt = _dev(self.block_table, "block_table", (torch.int32,))
+        kv = self.kv if self.kv is not None else self.idx_k
+        cl = None
+        if self.context_lens is not None:
+            cl = _dev(self.context_lens, "context_lens", (torch.int32,))
+        return sa_paged_cache(_ptr(self.kv), _ptr(self.idx_k), int(kv.shape[0]), bt.data_ptr(), int(bt.shape[1]),
+                              _ptr(cl))
+
+
+def _stream(stream):
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device):
+    torch = _torch()
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def decode_workspace_size(p: Params, batch: int, max_ctx: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sa_decode_workspace_size(ctypes.byref(p.c()), batch, max_ctx, ctypes.byref(n)),
+           "sa_decode_workspace_size")
+    return n.value
+
+
+def prefill_workspace_size(p: Params, num_rows: int, q_start: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sa_prefill_workspace_size(ctypes.byref(p.c()), num_rows, q_start, ctypes.byref(n)),
+           "sa_prefill_workspace_size")
+    return n.value
+
+
+def _outputs(p: Params, rows: int, device, want_lse: bool):
+    torch = _torch()
+    topk_idx = torch.empty((rows, p.topk), dtype=torch.int32, device=device)
+    out = torch.empty((rows, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
+                      device=device)
+    lse = torch.empty((rows, p.num_heads), dtype=torch.float32, device=device) if want_lse else None
+    return topk_idx, out, lse
+
+
+def sparse_attn_decode(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, want_lse=True,
+                       workspace=None, outputs=None, stream=None):
+    """Indexer -> top-k -> sparse attention for one query row per sequence.
+    Returns (topk_idx [B][k] int32, out [B][H][D_v], lse [B][H] or None)."""
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    _check(lib().sparse_attn_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
+                                    idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
+                                    _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode")
+    return topk_idx, out, lse
+
+
+def sparse_attn_select_decode(p: Params, cache: PagedCache, max_ctx: int, idx_q, idx_w, *, workspace=None,
+                              topk_idx=None, stream=None):
+    torch = _torch()
+    B = idx_q.shape[0]
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    if topk_idx is None:
+        topk_idx = torch.empty((B, p.topk), dtype=torch.int32, device=idx_q.device)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), idx_q.device)
+    _check(lib().sparse_attn_select_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
+                                           idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), ws.data_ptr(),
+                                           ws.numel(), _stream(stream)), "sparse_attn_select_decode")
+    return topk_idx
+
+
+def sparse_attn_attend_decode(p: Params, cache: PagedCache, max_ctx: int, q, topk_idx, *, want_lse=True,
+                              workspace=None, stream=None):
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(topk_idx, "topk_idx", (torch.int32,), (B, p.topk))
+    _, out, lse = _outputs(p, 0, q.device, False)
+    out = torch.empty((B, p.num_heads, p.v_dim), dtype=out.dtype, device=q.device)
+    lse = torch.empty((B, p.num_heads), dtype=torch.float32, device=q.device) if want_lse else None
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    _check(lib().sparse_attn_attend_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
+                                           topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
+                                           ws.numel(), _stream(stream)), "sparse_attn_attend_decode")
+    return out, lse
+
+
+def sparse_attn_prefill(p: Params, cache: PagedCache, q_start: int, q, idx_q, idx_w, *, want_lse=True,
+                        workspace=None, outputs=None, stream=None):
+    """Indexer -> top-k -> sparse attention for rows q_start .. q_start+L-1 of sequence 0."""
+    torch = _torch()
+    L = q.shape[0]
+    _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device)
+    _check(lib().sparse_attn_prefill(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start, q.data_ptr(),
+                                     idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
+                                     _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_prefill")
+    return topk_idx, out, lse
+
+
+def sparse_attn_select_prefill(p: Params, cache: PagedCache, q_start: int, idx_q, idx_w, *, workspace=None,
+                               stream=None):
+    torch = _torch()
+    L = idx_q.shape[0]
+    _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
+    topk_idx = torch.empty((L, p.topk), dtype=torch.int32, device=idx_q.device)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), idx_q.device)
+    _check(lib().sparse_attn_select_prefill(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start,
+                                            idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), ws.data_ptr(),
+                                            ws.numel(), _stream(stream)), "sparse_attn_select_prefill")
+    return topk_idx
+
+
+def sparse_attn_attend_prefill(p: Params, cache: PagedCache, q_start: int, q, topk_idx, *, want_lse=True,
+                               workspace=None, stream=None):
+    torch = _torch()
+    L = q.shape[0]
+    _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
+    _dev(topk_idx, "topk_idx", (torch.int32,), (L, p.topk))
+    out = torch.empty((L, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
+                      device=q.device)
+    lse = torch.empty((L, p.num_heads), dtype=torch.float32, device=q.device) if want_lse else None
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device)
+    _check(lib().sparse_attn_attend_prefill(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start, q.data_ptr(),
+                                            topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
+                                            ws.numel(), _stream(stream)), "sparse_attn_attend_prefill")
+    return out, lse
+
+
+def to_device(w: dict, device="cuda"):
+    """Copy a synth workload's arrays to `device` (bf16 data keeps its bit patterns)."""
+    torch = _torch()
+    import numpy as np
+
+    def t(a, dt=None):
+        x = torch.from_numpy(np.ascontiguousarray(a))
+        if dt is not None:
+            x = x.view(dt)
+        return x.to(device)
+
+    return dict(q=t(w["q"], torch.bfloat16), idx_q=t(w["idx_q"], torch.bfloat16), idx_w=t(w["idx_w"]),
+                cache=PagedCache(kv=t(w["kv"], torch.bfloat16), idx_k=t(w["idx_k"], torch.bfloat16),
+                                 block_table=t(w["block_table"]), context_lens=t(w["context_lens"])))

@@ -1,0 +1,175 @@
+/*
+ * sparse_attn.h -- C ABI of libsparse_attn.so: DSA-style sparse attention over a
+ * paged latent KV cache for AMD Instinct MI355X (gfx950).
+ *
+ * The method has three stages per query row:
+ *   1. an indexer scores every visible cached key,
+ *   2. a per-query top-k keeps the k best keys under the causal limit
+ *      (ties broken by the lower position),
+ *   3. softmax attention runs over the gathered latent rows of the kept keys.
+ * Sources: "Day-0 Adaptation for LLMs: Implementing Sparse Attention and
+ * Low-Precision Weights" (section III.1 and the decode pseudocode: indexer ->
+ * top-k -> gather -> attention); "Day-0 Adaptation: Running
+ * Trillion-Parameter Models on Domestic AI Accelerators" (section 3.1: a
+ * two-call interface, index selection followed by sparse attention, both over
+ * one block table; section 3.3: separate prefill and decode paths over the same
+ * cache and index structures); "Day-0 Model Adaptation Depends on the Compute
+ * Software Stack" (Operator Library Abstraction: the sparse-attention operator
+ * takes queries, keys/values and index lists and returns the context vectors).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ *  - Pointers marked (device) are HIP device pointers; everything else,
+ *    including the two structs below, is host memory read only during the call.
+ *  - bf16 tensors are raw bfloat16 bit patterns (uint16), row-major, densely
+ *    packed in the layouts given below.
+ *  - Ownership: the caller allocates and frees every buffer, including the
+ *    workspace, whose size comes from the matching *_workspace_size call.  The
+ *    library never allocates or frees device memory and keeps no mutable global
+ *    state; calls on different streams with different workspaces may overlap.
+ *  - Streams: all work is queued on `stream` (a hipStream_t; NULL = the null
+ *    stream).  No call synchronises; SA_OK means "queued".
+ *  - Errors: every argument check runs before the first HIP call, so a
+ *    rejected call touches no device state.  NULL required pointer ->
+ *    SA_ERR_NULL; inconsistent sizes -> SA_ERR_SHAPE; a valid parameter set the
+ *    compiled kernels do not cover -> SA_ERR_UNSUPPORTED; workspace too small ->
+ *    SA_ERR_WORKSPACE; a launch failure reported by the HIP runtime ->
+ *    SA_ERR_HIP.  Device-resident values (context lengths, block-table
+ *    entries, indices) are not checked on the host; see the cache struct.
+ *  - Outputs are fully overwritten.  Rows with an empty context yield indices
+ *    -1, output 0 and lse -inf.
+ */
+#ifndef SPARSE_ATTN_H
+#define SPARSE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SA_ABI_VERSION 1
+
+typedef enum {
+    SA_OK = 0,
+    SA_ERR_NULL = 1,
+    SA_ERR_SHAPE = 2,
+    SA_ERR_UNSUPPORTED = 3,
+    SA_ERR_WORKSPACE = 4,
+    SA_ERR_HIP = 5
+} sa_status;
+
+typedef enum { SA_OUT_F32 = 0, SA_OUT_BF16 = 1 } sa_out_dtype;
+
+/*
+ * Layer shape and method parameters.
+ * Supported (compiled) families:
+ *   qk_dim/v_dim in {576/512, 64/64}; idx_dim in {128, 32};
+ *   1 <= num_heads <= 128; 1 <= idx_heads <= 64; block_size a power of two
+ *   in [1, 1024]; 1 <= topk <= 16384.
+ * The key of the attention is latent[0:qk_dim] and the value is
+ * latent[0:v_dim] of one shared latent row per token (v_dim <= qk_dim).
+ */
+typedef struct {
+    int32_t num_heads;      /* H: attention query heads */
+    int32_t qk_dim;         /* D_qk: latent width used for q.k */
+    int32_t v_dim;          /* D_v: leading latent width used as the value */
+    int32_t idx_heads;      /* H_idx: indexer query heads */
+    int32_t idx_dim;        /* D_idx: indexer q/k width (one key vector per token) */
+    int32_t block_size;     /* tokens per cache block */
+    int32_t topk;           /* k: keys kept per query row */
+    float softmax_scale;    /* logits are softmax_scale * q.k */
+    int32_t idx_relu;       /* 1: ReLU on each indexer head's dot product; 0: none */
+    int32_t out_dtype;      /* sa_out_dtype of `out` */
+} sa_params;
+
+/*
+ * Paged cache (section 3.2 of the page on domestic AI accelerators: fixed-size
+ * blocks addressed through a block table).  Token s of sequence b lives in
+ * physical block block_table[b * max_blocks_per_seq + s / block_size] at slot
+ * s % block_size.
+ *   kv          (device) bf16 [num_blocks][block_size][qk_dim]  latent rows
+ *   idx_k       (device) bf16 [num_blocks][block_size][idx_dim] indexer keys
+ *   block_table (device) int32 [num_seqs][max_blocks_per_seq]
+ *   context_lens(device) int32 [num_seqs]  (decode only; may be NULL for prefill)
+ * Contract on device-resident values: context_lens[b] <= max_ctx and
+ * <= max_blocks_per_seq * block_size; the block-table entries that cover
+ * tokens [0, context_lens[b]) are valid block ids < num_blocks.  Entries past a
+ * sequence's last block are never read.  Slots past a sequence's length are
+ * never read.
+ */
+typedef struct {
+    const void *kv;
+    const void *idx_k;
+    int64_t num_blocks;
+    const int32_t *block_table;
+    int32_t max_blocks_per_seq;
+    const int32_t *context_lens;
+} sa_paged_cache;
+
+int32_t sa_abi_version(void);
+const char *sa_status_string(sa_status s);
+
+/* ---------------------------------------------------------------- decode --
+ * One query row per sequence b = 0..batch-1, at position context_lens[b]-1
+ * (the cache already holds the current token); it sees keys [0, context_lens[b]).
+ *   q       (device) bf16 [batch][num_heads][qk_dim]
+ *   idx_q   (device) bf16 [batch][idx_heads][idx_dim]
+ *   idx_w   (device) fp32 [batch][idx_heads]   indexer head weights
+ *   topk_idx(device, out) int32 [batch][topk]: the kept logical positions in
+ *           ascending order, -1 padded when fewer than topk keys are visible
+ *   out     (device, out) fp32 or bf16 [batch][num_heads][v_dim]
+ *   lse     (device, out, nullable) fp32 [batch][num_heads], natural-log
+ *           log-sum-exp of the scaled logits over the kept keys
+ * max_ctx is a host-side upper bound on every context_lens[b]; it sizes the
+ * workspace and the launch grids.
+ */
+sa_status sa_decode_workspace_size(const sa_params *p, int32_t batch, int32_t max_ctx,
+                                   size_t *bytes /* host, out */);
+sa_status sparse_attn_decode(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
+                             int32_t max_ctx, const void *q, const void *idx_q,
+                             const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                             void *workspace, size_t workspace_bytes, void *stream);
+/* The two stages of sparse_attn_decode as separate calls over the same block
+ * mapping (the index-select / sparse-attention pair of section 3.1).  The
+ * select call writes topk_idx; the attend call reads it.  Attend treats any
+ * index outside [0, context_lens[b]) as padding.  Both take the decode
+ * workspace. */
+sa_status sparse_attn_select_decode(const sa_params *p, const sa_paged_cache *cache,
+                                    int32_t batch, int32_t max_ctx, const void *idx_q,
+                                    const float *idx_w, int32_t *topk_idx, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *cache,
+                                    int32_t batch, int32_t max_ctx, const void *q,
+                                    const int32_t *topk_idx, void *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/* --------------------------------------------------------------- prefill --
+ * num_rows query rows of sequence 0 (block_table row 0); row i sits at
+ * position q_start + i and sees keys [0, q_start + i] (causal limit, itself
+ * included).  The cache must hold at least q_start + num_rows tokens.
+ * Layouts as for decode with batch replaced by num_rows.  Rows whose visible
+ * key count is at most topk attend to all of their keys.
+ */
+sa_status sa_prefill_workspace_size(const sa_params *p, int32_t num_rows, int32_t q_start,
+                                    size_t *bytes /* host, out */);
+sa_status sparse_attn_prefill(const sa_params *p, const sa_paged_cache *cache, int32_t num_rows,
+                              int32_t q_start, const void *q, const void *idx_q,
+                              const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                              void *workspace, size_t workspace_bytes, void *stream);
+sa_status sparse_attn_select_prefill(const sa_params *p, const sa_paged_cache *cache,
+                                     int32_t num_rows, int32_t q_start, const void *idx_q,
+                                     const float *idx_w, int32_t *topk_idx, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+/* Attend treats any index outside [0, q_start + i] of row i as padding. */
+sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *cache,
+                                     int32_t num_rows, int32_t q_start, const void *q,
+                                     const int32_t *topk_idx, void *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPARSE_ATTN_H */

@@ -1,0 +1,166 @@
+"""Parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: selected indices bit-exact (the indexer inputs are small integers, so every
+score is exact in fp32 on both sides); attention output within 2e-2 max-abs and
+2e-3 mean-abs error relative to the oracle output's RMS; lse within 1e-3
+absolute.  Full-size workloads run in the same launch configuration as the
+benchmark and compare the rows the oracle can afford, one by one.
+"""
+import os
+import sys
+from dataclasses import replace
+
+import numpy as np
+import pytest
+
+import oracle
+from dsa_sparse_attention_02_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+MAX_REL, MEAN_REL, LSE_ABS = 2e-2, 2e-3, 1e-3
+
+
+def say(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from dsa_sparse_attention_02_amd import sparse_attn as sa
+    sa.lib()
+    return torch, sa
+
+
+def run_gpu(dev, w, out_bf16=False, staged=False):
+    torch, sa = dev
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"], out_bf16=out_bf16)
+    if w["mode"] == "decode":
+        max_ctx = int(w["context_lens"].max())
+        if staged:
+            tk = sa.sparse_attn_select_decode(p, d["cache"], max_ctx, d["idx_q"], d["idx_w"])
+            out, lse = sa.sparse_attn_attend_decode(p, d["cache"], max_ctx, d["q"], tk)
+            res = (tk, out, lse)
+        else:
+            res = sa.sparse_attn_decode(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"])
+    else:
+        if staged:
+            tk = sa.sparse_attn_select_prefill(p, d["cache"], w["q_start"], d["idx_q"], d["idx_w"])
+            out, lse = sa.sparse_attn_attend_prefill(p, d["cache"], w["q_start"], d["q"], tk)
+            res = (tk, out, lse)
+        else:
+            res = sa.sparse_attn_prefill(p, d["cache"], w["q_start"], d["q"], d["idx_q"], d["idx_w"])
+    torch.cuda.synchronize()
+    return res
+
+
+def compare(w, res, rows=None, tag=""):
+    tk_all, out_all, lse_all = res
+    ref = oracle.run(w, rows=rows)
+    rows = ref["rows"]
+    idx = __import__("torch").as_tensor(rows, device=tk_all.device)
+    tk = tk_all.index_select(0, idx).cpu().numpy()
+    out = out_all.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    lse = lse_all.index_select(0, idx).cpu().numpy().astype(np.float64)
+    bad = np.nonzero(~np.all(tk == ref["topk"], axis=1))[0]
+    assert len(bad) == 0, f"{tag}: indices differ on rows {rows[bad][:8]}"
+    assert np.isfinite(out).all(), f"{tag}: non-finite output"
+    rms = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    err = np.abs(out - ref["out"]) / rms
+    empty = np.isneginf(ref["lse"])
+    assert np.array_equal(np.isneginf(lse), empty), f"{tag}: empty-context rows disagree"
+    lerr = np.abs(np.where(empty, 0, lse) - np.where(empty, 0, ref["lse"]))
+    say(f"  {tag}: rows {len(rows)} out err max {err.max():.3e} mean {err.mean():.3e} (rms {rms:.3f}), "
+        f"lse err max {lerr.max():.2e}")
+    assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, tag
+    assert lerr.max() <= LSE_ABS, tag
+    return ref
+
+
+MLA = synth.MLA
+
+
+CASES = {
+    "tiny_prefill_L256": lambda: synth.WORKLOADS["tiny_prefill_L256"],
+    "decode_ragged": lambda: synth.small_decode("decode_ragged", MLA,
+                                                [0, 1, 31, 32, 33, 64, 2047, 2048, 2049, 3000, 5000, 9001], seed=101),
+    "decode_k1": lambda: synth.small_decode("decode_k1", MLA, [1, 5, 700, 4099], seed=102, topk=1),
+    "decode_k64_ties": lambda: synth.small_decode("decode_k64", MLA, [63, 64, 65, 4000, 12345], seed=103, topk=64,
+                                                  idx_int_max=1),
+    "decode_k3000_splits": lambda: synth.small_decode("decode_k3000", MLA, [2999, 3000, 3001, 7000], seed=104,
+                                                      topk=3000),
+    "decode_tiny_shape": lambda: synth.small_decode("decode_tiny", synth.TINY, [0, 3, 16, 64, 65, 300], seed=105),
+    "prefill_2500": lambda: synth.small_prefill("prefill_2500", MLA, rows=2500, seed=106),
+    "prefill_qstart": lambda: synth.small_prefill("prefill_qstart", MLA, rows=700, q_start=1900, seed=107),
+    "prefill_tiny_qstart": lambda: synth.small_prefill("prefill_tiny_qs", synth.TINY, rows=100, q_start=37, seed=108),
+    "prefill_k4100": lambda: synth.small_prefill("prefill_k4100", MLA, rows=300, q_start=4000, seed=109, topk=4100),
+}
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_parity_small(dev, name):
+    spec = CASES[name]()
+    say(f"[gpu] parity {name}: mode {spec.mode} seed {spec.seed}")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w), tag=name)
+
+
+@pytest.mark.parametrize("name", ["decode_ragged", "prefill_2500", "tiny_prefill_L256"])
+def test_staged_equals_fused_and_deterministic(dev, name):
+    spec = CASES[name]()
+    say(f"[gpu] staged/fused/determinism {name}")
+    w = synth.make(spec)
+    a = run_gpu(dev, w)
+    b = run_gpu(dev, w)
+    c = run_gpu(dev, w, staged=True)
+    for x, y in ((a, b), (a, c)):
+        assert np.array_equal(x[0].cpu().numpy(), y[0].cpu().numpy())
+        assert np.array_equal(x[1].cpu().numpy(), y[1].cpu().numpy())
+        assert np.array_equal(x[2].cpu().numpy(), y[2].cpu().numpy())
+
+
+def test_block_relabelling_invariance_gpu(dev):
+    spec = CASES["decode_ragged"]()
+    say("[gpu] block relabelling invariance")
+    w = synth.make(spec)
+    pool = w["kv"].shape[0]
+    perm = np.random.default_rng(17).permutation(pool)
+    kv, ik = np.empty_like(w["kv"]), np.empty_like(w["idx_k"])
+    kv[perm], ik[perm] = w["kv"], w["idx_k"]
+    w2 = dict(w, kv=kv, idx_k=ik, block_table=perm[w["block_table"]].astype(np.int32))
+    a, b = run_gpu(dev, w), run_gpu(dev, w2)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
+
+
+def test_bf16_output(dev):
+    spec = CASES["decode_ragged"]()
+    say("[gpu] bf16 output")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w, out_bf16=True), tag="decode_ragged bf16 out")
+
+
+# ------------------------------------------------------- full-size workloads --
+FULL_ROWS = {
+    "tiny_prefill_L256": None,                       # every row
+    "decode_b32_ctx8k": None,                        # every row
+    "decode_b64_ctx16k_128k": "ends",                # shortest, longest and a few more
+    "decode_b4_ctx1m": [0, 3],
+    "prefill_L32k": [0, 1, 2046, 2047, 2048, 2049, 4095, 16000, 31999, 32767],
+}
+
+
+@pytest.mark.parametrize("name", list(FULL_ROWS))
+def test_parity_full_size(dev, name):
+    spec = synth.WORKLOADS[name]
+    say(f"[gpu] full-size parity {name}")
+    w = synth.make(spec)
+    rows = FULL_ROWS[name]
+    if rows == "ends":
+        ctx = w["context_lens"]
+        rows = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 63})
+    compare(w, run_gpu(dev, w), rows=rows, tag=name)
