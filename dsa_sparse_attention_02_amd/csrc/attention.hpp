@@ -35,6 +35,7 @@
 //     the output accumulators rare;
 //   * the S^T accumulator already has the register layout of the B operand of
 //     O^T[v][head] += V^T[v][token] . P^T[token][head]: P is only rounded to bf16.
+//     The softmax denominator sums the same rounded P.
 //     The V^T operand is gathered from LDS as dwords (two adjacent v of one
 //     token) and split with byte permutes into an "even v" and an "odd v"
 //     operand, so every LDS byte read is used.
@@ -54,7 +55,7 @@ struct AttnArgs {
     const int32_t *topk_idx;     // [rows][k]
     const int32_t *ctx_lens;     // decode: [rows]
     float *part_o;               // splits > 1: [rows][splits][H][V]
-    float *part_ml;              // splits > 1: [rows][splits][H][2]  (max in log2 units, sum)
+    float *part_ml;              // splits > 1: [rows][splits][H][4]  (max in log2 units, rounded sum, exact sum, 0)
     void *out;                   // splits == 1: [rows][H][V]
     float *lse;                  // splits == 1, nullable: [rows][H]
     int64_t num_blocks;
@@ -142,7 +143,9 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
         oe[vp] = f32x16{};
         oo[vp] = f32x16{};
     }
-    float m = -INFINITY, l = 0.0f;
+    // m: reference max (log2 units); l: sum of the bf16-rounded weights (output
+    // normaliser); le: sum of the unrounded weights (log-sum-exp)
+    float m = -INFINITY, l = 0.0f, le = 0.0f;
     __syncthreads();
 
     auto issue_tile = [&](int t, int buf) {
@@ -202,6 +205,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
         if (__any(moved)) {
             const float alpha = moved ? exp2f(m - mnew) : 1.0f;
             l *= alpha;
+            le *= alpha;
 #pragma unroll
             for (int vp = 0; vp < VP; ++vp) {
                 oe[vp] *= alpha;
@@ -217,8 +221,12 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
             for (int jj = 0; jj < 4; ++jj) {
                 const float p0 = (m == -INFINITY) ? 0.0f : exp2f(s[8 * k2 + 2 * jj] - m);
                 const float p1 = (m == -INFINITY) ? 0.0f : exp2f(s[8 * k2 + 2 * jj + 1] - m);
-                l += p0 + p1;
                 w[jj] = pack_bf16x2(p0, p1);
+                // the normaliser sums the same bf16-rounded weights the MFMA
+                // multiplies V by, so the output is an exact weighted mean of
+                // the kept rows up to fp32 accumulation
+                l += __uint_as_float(w[jj] << 16) + __uint_as_float(w[jj] & 0xFFFF0000u);
+                le += p0 + p1;
             }
             pb[k2] = as_bf16x8(w);
         }
@@ -251,6 +259,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
     }
 
     const float lt = l + __shfl_xor(l, 32);
+    const float lte = le + __shfl_xor(le, 32);
     if (!hok) return;
     if (a.splits == 1) {
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
                     *reinterpret_cast<f32x2 *>(reinterpret_cast<float *>(a.out) + obase + v) = f32x2{e0, e1};
             }
         if (a.lse && half == 0 && vh == 0)
-            a.lse[(int64_t)r * a.num_heads + head] = lt > 0.0f ? (m + log2f(lt)) * 0.69314718055994531f : -INFINITY;
+            a.lse[(int64_t)r * a.num_heads + head] = lt > 0.0f ? (m + log2f(lte)) * 0.69314718055994531f : -INFINITY;
     } else {
         const int64_t pbase = (((int64_t)r * a.splits + split) * a.num_heads + head);
         float *po = a.part_o + pbase * V + vh * VW;
@@ -278,12 +287,13 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
                 const int v = 64 * vp + 2 * acc_row(i, half);
                 *reinterpret_cast<f32x2 *>(po + v) = f32x2{oe[vp][i], oo[vp][i]};
             }
-        if (half == 0 && vh == 0) *reinterpret_cast<f32x2 *>(a.part_ml + pbase * 2) = f32x2{m, lt};
+        if (half == 0 && vh == 0) *reinterpret_cast<f32x4 *>(a.part_ml + pbase * 4) = f32x4{m, lt, lte, 0.0f};
     }
 }
 
 // Merge the split partials of one (row, head): with M the largest partial max,
-// o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i and lse = (M + log2 L) ln 2.
+// o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i and
+// lse = (M + log2 sum_i 2^(m_i - M) le_i) ln 2.
 template <int V>
 __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_ml, int splits,
@@ -294,13 +304,17 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
     const int64_t base = (int64_t)r * splits * num_heads + h;  // partial (r, split 0, h)
     float M = -INFINITY;
     for (int s = 0; s < splits; ++s) {
-        const f32x2 ml = *reinterpret_cast<const f32x2 *>(part_ml + (base + (int64_t)s * num_heads) * 2);
+        const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + (base + (int64_t)s * num_heads) * 4);
         if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
     }
-    float L = 0.0f;
+    float L = 0.0f, Le = 0.0f;
     for (int s = 0; s < splits; ++s) {
-        const f32x2 ml = *reinterpret_cast<const f32x2 *>(part_ml + (base + (int64_t)s * num_heads) * 2);
-        if (ml[1] > 0.0f) L += ml[1] * exp2f(ml[0] - M);
+        const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + (base + (int64_t)s * num_heads) * 4);
+        if (ml[1] > 0.0f) {
+            const float f = exp2f(ml[0] - M);
+            L += ml[1] * f;
+            Le += ml[2] * f;
+        }
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
     const int64_t obase = ((int64_t)r * num_heads + h) * V;
@@ -308,7 +322,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
         for (int s = 0; s < splits; ++s) {
             const int64_t ps = base + (int64_t)s * num_heads;
-            const f32x2 ml = *reinterpret_cast<const f32x2 *>(part_ml + ps * 2);
+            const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + ps * 4);
             if (ml[1] > 0.0f) acc += exp2f(ml[0] - M) * *reinterpret_cast<const f32x4 *>(part_o + ps * V + v);
         }
         acc *= inv;
@@ -321,7 +335,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
         }
     }
     if (lse && threadIdx.x == 0)
-        lse[(int64_t)r * num_heads + h] = L > 0.0f ? (M + log2f(L)) * 0.69314718055994531f : -INFINITY;
+        lse[(int64_t)r * num_heads + h] = L > 0.0f ? (M + log2f(Le)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace sa

@@ -99,7 +99,7 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
     if (splits > 1) {
         off = align_up(off + (size_t)batch * splits * p->num_heads * p->v_dim * 4, kAlign);
         d.off_part_ml = off;
-        off = align_up(off + (size_t)batch * splits * p->num_heads * 8, kAlign);
+        off = align_up(off + (size_t)batch * splits * p->num_heads * 16, kAlign);
     } else {
         d.off_part_ml = off;
     }
@@ -132,11 +132,11 @@ PrefillPlan plan_prefill(const sa_params *p, int num_rows, int q_start)
     d.off_part_o = off;
     d.attn_chunk_rows = num_rows;
     if (d.splits > 1) {
-        const size_t per_row = (size_t)d.splits * p->num_heads * (p->v_dim * 4 + 8);
+        const size_t per_row = (size_t)d.splits * p->num_heads * (p->v_dim * 4 + 16);
         d.attn_chunk_rows = (int)std::max<size_t>(1, std::min<size_t>(num_rows, kPrefillPartialBudget / per_row));
         off = align_up(off + (size_t)d.attn_chunk_rows * d.splits * p->num_heads * p->v_dim * 4, kAlign);
         d.off_part_ml = off;
-        off = align_up(off + (size_t)d.attn_chunk_rows * d.splits * p->num_heads * 8, kAlign);
+        off = align_up(off + (size_t)d.attn_chunk_rows * d.splits * p->num_heads * 16, kAlign);
     } else {
         d.off_part_ml = off;
     }

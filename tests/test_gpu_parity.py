@@ -2,8 +2,10 @@
 
 Bar: selected indices bit-exact (the indexer inputs are small integers, so every
 score is exact in fp32 on both sides); attention output within 2e-2 max-abs and
-2e-3 mean-abs error relative to the oracle output's RMS; lse within 1e-3
-absolute.  Full-size workloads run in the same launch configuration as the
+2e-3 mean-abs error, each query row's error measured relative to the RMS of that
+row's oracle output (a prefill row that keeps one key outputs a V row, RMS ~1,
+one that averages 2048 keys has RMS ~0.05, so one RMS for the whole tensor would
+weigh rows by their scale); lse within 1e-3 absolute.  Full-size workloads run in the same launch configuration as the
 benchmark and compare the rows the oracle can afford, one by one.
 """
 import os
@@ -69,13 +71,16 @@ def compare(w, res, rows=None, tag=""):
     bad = np.nonzero(~np.all(tk == ref["topk"], axis=1))[0]
     assert len(bad) == 0, f"{tag}: indices differ on rows {rows[bad][:8]}"
     assert np.isfinite(out).all(), f"{tag}: non-finite output"
-    rms = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    rms_all = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    rms = np.sqrt(np.mean(ref["out"] ** 2, axis=(1, 2), keepdims=True))
+    rms = np.where(rms > 0, rms, 1.0)  # empty-context rows: output 0 on both sides
     err = np.abs(out - ref["out"]) / rms
+    gerr = np.abs(out - ref["out"]) / rms_all
     empty = np.isneginf(ref["lse"])
     assert np.array_equal(np.isneginf(lse), empty), f"{tag}: empty-context rows disagree"
     lerr = np.abs(np.where(empty, 0, lse) - np.where(empty, 0, ref["lse"]))
-    say(f"  {tag}: rows {len(rows)} out err max {err.max():.3e} mean {err.mean():.3e} (rms {rms:.3f}), "
-        f"lse err max {lerr.max():.2e}")
+    say(f"  {tag}: rows {len(rows)} out err/row-rms max {err.max():.3e} mean {err.mean():.3e}; "
+        f"err/global-rms max {gerr.max():.3e} mean {gerr.mean():.3e} (rms {rms_all:.3f}); lse err max {lerr.max():.2e}")
     assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, tag
     assert lerr.max() <= LSE_ABS, tag
     return ref
