@@ -1,0 +1,279 @@
+#!/usr/bin/env python3
+"""Benchmark of DSA sparse attention (indexer -> top-k -> sparse MLA attention) on one MI355X.
+
+Headline: decode throughput (query tokens/s, one query row per sequence) and
+algorithmic HBM GB/s on the mixed-length workload (batch 64, contexts uniform in
+[16384, 131072], top-k 2048, 128 heads over a 576/512 latent, indexer 64 x 128,
+paged blocks of 64).  One step is one sparse_attn_decode call over the whole
+batch: indexer scan, top-k, attention and split merge, with every input already
+resident in HBM.  Secondary lines: prefill query-tokens/s on the L = 32768
+workload, and the CPU oracle timed on the host cores on a bounded sample.
+
+Per-kernel durations come from HIP events that the profiling entry point records
+on the library's stream between its kernels inside the timed region.
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
+METRIC = "decode tokens/s + HBM GB/s at 128K ctx, top-k=2048; prefill query-tokens/s"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def decode_algorithmic(w):
+    """Bytes and flops the method must move/do for one decode call (fp32 output)."""
+    import numpy as np
+    sh = w["shape"]
+    ctx = w["context_lens"].astype(np.int64)
+    kept = np.minimum(ctx, sh.topk)
+    blocks = (ctx + sh.block_size - 1) // sh.block_size
+    scan = int((ctx * sh.idx_dim * 2).sum())
+    gather = int((kept * sh.qk_dim * 2).sum())
+    per_q = sh.num_heads * sh.qk_dim * 2 + sh.num_heads * sh.v_dim * 4 + sh.num_heads * 4 + \
+        sh.idx_heads * (2 * sh.idx_dim + 4)
+    total = scan + gather + len(ctx) * per_q + int((4 * kept).sum()) + int((4 * blocks).sum())
+    flops = int((2 * ctx * sh.idx_heads * sh.idx_dim).sum() + (2 * kept * sh.num_heads * (sh.qk_dim + sh.v_dim)).sum())
+    # the indexer kernel alone: key rows + score writes + per-row query/weights + block table
+    idx_bytes = int((ctx * (sh.idx_dim * 2 + 4)).sum() + len(ctx) * sh.idx_heads * (2 * sh.idx_dim + 4) +
+                    (4 * blocks).sum())
+    return dict(bytes=total, scan=scan, gather=gather, flops=flops, indexer_bytes=idx_bytes)
+
+
+def source_hash(*names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "dsa_sparse_attention_02_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_key, launches_per_step):
+    """HBM bytes per launch from the committed counter summary, or None if the
+    kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_key)
+    if not e or e.get("source_hash") != source_hash(*e.get("sources", [])):
+        return None
+    return e.get("bytes_per_launch")
+
+
+def run_decode(args, torch, sa, synth):
+    spec = synth.WORKLOADS[args.workload]
+    log(f"generating {spec.name} (seed {spec.seed})")
+    t = time.time()
+    w = synth.make(spec)
+    log(f"generated in {time.time() - t:.1f}s; copying to the device")
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    B = spec.batch
+    max_ctx = int(w["context_lens"].max())
+    ws = torch.empty(sa.decode_workspace_size(p, B, max_ctx), dtype=torch.uint8, device="cuda")
+    outs = sa._outputs(p, B, "cuda", True)
+    call = lambda ev: sa.sparse_attn_decode_profiled(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], ev,
+                                                     workspace=ws, outputs=outs)
+    n_marks = call([])[3]
+    kernels = ["indexer", "topk", "attention", "merge"][:n_marks - 1] if max_ctx > p.topk else \
+        ["topk", "attention", "merge"][:n_marks - 1]
+    log(f"warmup {args.warmup} steps ({n_marks - 1} kernels per step: {', '.join(kernels)})")
+    for _ in range(args.warmup):
+        call([])
+    torch.cuda.synchronize()
+    events = [[sa.HipEvent() for _ in range(n_marks)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        call(events[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+    per_kernel = {k: [] for k in kernels}
+    for ev in events:
+        for i, k in enumerate(kernels):
+            per_kernel[k].append(ev[i].elapsed_ms(ev[i + 1]))
+    stages = {k: statistics.mean(v) for k, v in per_kernel.items()}
+    log(f"timed {args.steps} steps: {ms:.3f} ms/step; stages " +
+        ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in stages.items()))
+
+    # the same step with a 1 GiB write between steps (HBM-cold caches), events only
+    cold = []
+    if args.flush_steps > 0:
+        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+        for _ in range(args.flush_steps):
+            flush.fill_(1.0)
+            ev = [sa.HipEvent() for _ in range(n_marks)]
+            call(ev)
+            torch.cuda.synchronize()
+            cold.append(ev[0].elapsed_ms(ev[-1]))
+        del flush
+    alg = decode_algorithmic(w)
+    return w, dict(ms=ms, stages=stages, cold_ms=statistics.median(cold) if cold else None, alg=alg,
+                   per_kernel=per_kernel)
+
+
+def run_prefill(args, torch, sa, synth):
+    spec = synth.WORKLOADS["prefill_L32k"]
+    log(f"generating {spec.name}")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    L = spec.rows
+    ws = torch.empty(sa.prefill_workspace_size(p, L, 0), dtype=torch.uint8, device="cuda")
+    outs = sa._outputs(p, L, "cuda", True)
+    call = lambda ev: sa.sparse_attn_prefill_profiled(p, d["cache"], 0, d["q"], d["idx_q"], d["idx_w"], ev,
+                                                      workspace=ws, outputs=outs)
+    n_marks = call([])[3]
+    torch.cuda.synchronize()
+    steps = max(1, args.prefill_steps)
+    evs = [[sa.HipEvent() for _ in range(n_marks)] for _ in range(steps)]
+    t0 = time.perf_counter()
+    for s in range(steps):
+        call(evs[s])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # launch order: per chunk [indexer?, topk], then attention (+ merge)
+    sh = w["shape"]
+    plan_rows = sa_chunk_rows(sa, p, L)
+    names = []
+    for r0 in range(0, L, plan_rows):
+        if r0 + min(plan_rows, L - r0) > p.topk:
+            names.append("indexer")
+        names.append("topk")
+    names += ["attention"] * (n_marks - 1 - len(names))
+    tot = {}
+    for ev in evs:
+        for i, k in enumerate(names):
+            tot[k] = tot.get(k, 0.0) + ev[i].elapsed_ms(ev[i + 1]) / steps
+    idx_flops = 2.0 * sh.idx_heads * sh.idx_dim * L * (L + 1) / 2
+    attn_flops = 2.0 * sh.num_heads * (sh.qk_dim + sh.v_dim) * sum(min(i + 1, sh.topk) for i in range(L))
+    res = dict(workload=spec.name, ms_per_step=round(ms, 3), value=round(L / (ms / 1e3), 1), unit="query tokens/s",
+               stages_ms={k: round(v, 3) for k, v in tot.items()},
+               indexer_tflops=round(idx_flops / (tot.get("indexer", float("nan")) / 1e3) / 1e12, 1),
+               attention_tflops=round(attn_flops / (tot["attention"] / 1e3) / 1e12, 1))
+    res["indexer_mfma_frac"] = round(res["indexer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    res["attention_mfma_frac"] = round(res["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
+    log(f"prefill: {ms:.2f} ms/step, stages {res['stages_ms']}")
+    return res
+
+
+def sa_chunk_rows(sa, p, L):
+    """Rows per prefill indexer/top-k chunk (mirrors the library's planning: scores of
+    a chunk take at most 256 MiB, in multiples of 16 rows)."""
+    stride = (L + 63) // 64 * 64
+    rows = max(16, ((256 << 20) // (stride * 4)) // 16 * 16)
+    return min(rows, (L + 15) // 16 * 16)
+
+
+def cpu_baseline(args, w):
+    import oracle
+    import numpy as np
+    ctx = w["context_lens"]
+    order = np.argsort(ctx)[::-1]  # start with the longest rows: the costliest per token
+    rows, t0 = [], time.perf_counter()
+    stage = np.zeros(3)
+    for r in order:
+        oracle.run(w, rows=[int(r)], stage_seconds=stage)
+        rows.append(int(r))
+        if time.perf_counter() - t0 >= args.cpu_seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": round(len(rows) / el, 3), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{len(rows)} of {len(ctx)} decode rows of {args.workload} (longest first, ctx "
+                      f"{int(ctx[rows].min())}-{int(ctx[rows].max())}); {el:.1f}s: indexer {stage[0]:.1f}s, "
+                      f"sort {stage[1]:.1f}s, attention {stage[2]:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode_b64_ctx16k_128k")
+    ap.add_argument("--flush-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush")
+    ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the sparse-attention path here is single-GPU "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from dsa_sparse_attention_02_amd import sparse_attn as sa
+    from dsa_sparse_attention_02_amd import synth
+    sa.lib()  # fail loudly if the library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 copies of 1 GiB")
+        del src, dst
+
+    w, dec = run_decode(args, torch, sa, synth)
+    sh = w["shape"]
+    B = len(w["context_lens"])
+    value = B / (dec["ms"] / 1e3)
+    alg = dec["alg"]
+    t_idx = dec["stages"].get("indexer")
+    roof = None
+    if t_idx:
+        achieved = alg["indexer_bytes"] / (t_idx / 1e3) / 1e9
+        traffic = traffic_from_profiles("idx_score_decode_kernel<128, 2>/" + args.workload, 1)
+        roof = {"bound": "hbm", "kernel": "idx_score_decode_kernel<128, 2>", "achieved": round(achieved, 1),
+                "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": traffic, "avg_ms": round(t_idx, 5)}
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": args.workload, "batch": B, "context": "uniform[16384,131072]" if
+                   args.workload == "decode_b64_ctx16k_128k" else int(w["context_lens"].max()),
+                   "topk": sh.topk, "heads": sh.num_heads, "qk_dim": sh.qk_dim, "v_dim": sh.v_dim,
+                   "indexer": f"{sh.idx_heads}x{sh.idx_dim}", "block_size": sh.block_size, "out": "fp32",
+                   "parallelism": "single GPU"},
+        "hbm_gbps": round(alg["bytes"] / (dec["ms"] / 1e3) / 1e9, 1),
+        "hbm_frac": round(alg["bytes"] / (dec["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes_per_step": alg["bytes"],
+        "stages_us": {k: round(v * 1e3, 2) for k, v in dec["stages"].items()},
+        "cold_cache_ms_per_step": round(dec["cold_ms"], 4) if dec["cold_ms"] else None,
+        "roofline": roof,
+    }
+    if not args.no_prefill:
+        line["prefill"] = run_prefill(args, torch, sa, synth)
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline: oracle on up to {args.cpu_seconds:.0f}s of rows")
+        line["cpu_baseline"] = cpu_baseline(args, w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

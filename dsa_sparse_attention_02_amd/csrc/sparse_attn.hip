@@ -184,6 +184,21 @@ sa_status launched()
     return hipGetLastError() == hipSuccess ? SA_OK : SA_ERR_HIP;
 }
 
+// Optional per-launch event marks (profiling entry points): marks[0] is recorded
+// before the first launch and marks[i] after the i-th launch, while capacity lasts;
+// `count` always advances so the caller learns how many marks a call takes.
+struct StageMarks {
+    void *const *events = nullptr;
+    int capacity = 0;
+    int count = 0;
+    hipStream_t stream = nullptr;
+    void mark()
+    {
+        if (events && count < capacity) (void)hipEventRecord((hipEvent_t)events[count], stream);
+        ++count;
+    }
+};
+
 // --------------------------------------------------------------- launches --
 template <int D, int T>
 void launch_idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
@@ -233,7 +248,7 @@ void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *id
     }
 }
 
-void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st)
+void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st, StageMarks *mk)
 {
     const int threads = 64 * ((p->num_heads + 31) / 32);
     dim3 grid(a.splits * (p->v_dim > 256 ? 2 : 1), rows);
@@ -241,6 +256,7 @@ void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st)
         hipLaunchKernelGGL((attend_kernel<576, 512>), grid, dim3(threads), 0, st, a);
     else
         hipLaunchKernelGGL((attend_kernel<64, 64>), grid, dim3(threads), 0, st, a);
+    if (mk) mk->mark();
     if (a.splits > 1) {
         dim3 cg(p->num_heads, rows);
         if (p->v_dim == 512)
@@ -249,6 +265,7 @@ void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st)
         else
             hipLaunchKernelGGL((combine_kernel<64>), cg, dim3(64), 0, st, a.part_o, a.part_ml, a.splits,
                                p->num_heads, a.out, a.out_bf16, a.lse);
+        if (mk) mk->mark();
     }
 }
 
@@ -273,19 +290,22 @@ AttnArgs attn_args(const sa_params *p, const sa_paged_cache *c, const void *q, c
     return a;
 }
 
-sa_status select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
-                        const float *idx_w, int32_t *topk_idx, void *ws, const DecodePlan &d, hipStream_t st)
+void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
+                   const float *idx_w, int32_t *topk_idx, void *ws, const DecodePlan &d, hipStream_t st,
+                   StageMarks *mk)
 {
     float *scores = (float *)((char *)ws + d.off_scores);
-    if (max_ctx > p->topk)
+    if (max_ctx > p->topk) {
         idx_decode(p, c, batch, max_ctx, idx_q, idx_w, scores, d.score_stride, d.keys_per_wave, st);
+        if (mk) mk->mark();
+    }
     hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
                        c->context_lens, 0, p->topk, topk_idx);
-    return SA_OK;
+    if (mk) mk->mark();
 }
 
 void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *q, const int32_t *topk_idx,
-                   void *out, float *lse, void *ws, const DecodePlan &d, hipStream_t st)
+                   void *out, float *lse, void *ws, const DecodePlan &d, hipStream_t st, StageMarks *mk)
 {
     AttnArgs a = attn_args(p, c, q, topk_idx, out, lse);
     a.decode = 1;
@@ -293,27 +313,32 @@ void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const
     a.splits = d.splits;
     a.part_o = (float *)((char *)ws + d.off_part_o);
     a.part_ml = (float *)((char *)ws + d.off_part_ml);
-    attend(p, a, batch, st);
+    attend(p, a, batch, st, mk);
 }
 
 void select_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *idx_q,
-                    const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d, hipStream_t st)
+                    const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d, hipStream_t st,
+                    StageMarks *mk)
 {
     float *scores = (float *)((char *)ws + d.off_scores);
     for (int r0 = 0; r0 < num_rows; r0 += d.chunk_rows) {
         const int nr = std::min(d.chunk_rows, num_rows - r0);
         const int pos0 = q_start + r0;
         // rows whose whole context fits in k need no scores
-        if (pos0 + nr > p->topk)
+        if (pos0 + nr > p->topk) {
             idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
                         idx_w + (int64_t)r0 * p->idx_heads, pos0, nr, scores, d.score_stride, st);
+            if (mk) mk->mark();
+        }
         hipLaunchKernelGGL(topk_rows_kernel, dim3(nr), dim3(kTopkThreads), 0, st, scores, d.score_stride,
                            (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk);
+        if (mk) mk->mark();
     }
 }
 
 void attend_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *q,
-                    const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d, hipStream_t st)
+                    const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d, hipStream_t st,
+                    StageMarks *mk)
 {
     for (int r0 = 0; r0 < num_rows; r0 += d.attn_chunk_rows) {
         const int nr = std::min(d.attn_chunk_rows, num_rows - r0);
@@ -327,7 +352,7 @@ void attend_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, i
         a.splits = d.splits;
         a.part_o = (float *)((char *)ws + d.off_part_o);
         a.part_ml = (float *)((char *)ws + d.off_part_ml);
-        attend(p, a, nr, st);
+        attend(p, a, nr, st, mk);
     }
 }
 
@@ -380,7 +405,8 @@ sa_status sparse_attn_select_decode(const sa_params *p, const sa_paged_cache *c,
     if (!idx_q || !idx_w || !topk_idx) return SA_ERR_NULL;
     const DecodePlan d = plan_decode(p, batch, max_ctx);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
-    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream);
+    clear_hip_error();
+    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream, nullptr);
     return launched();
 }
 
@@ -393,13 +419,14 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *c,
     if (!q || !topk_idx || !out) return SA_ERR_NULL;
     const DecodePlan d = plan_decode(p, batch, max_ctx);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
-    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream);
+    clear_hip_error();
+    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream, nullptr);
     return launched();
 }
 
-sa_status sparse_attn_decode(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
-                             float *lse, void *workspace, size_t workspace_bytes, void *stream)
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk)
 {
     sa_status s = check_decode(p, c, batch, max_ctx, true, true);
     if (s != SA_OK) return s;
@@ -407,9 +434,37 @@ sa_status sparse_attn_decode(const sa_params *p, const sa_paged_cache *c, int32_
     const DecodePlan d = plan_decode(p, batch, max_ctx);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
-    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, st);
-    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, st);
+    clear_hip_error();
+    if (mk) {
+        mk->stream = st;
+        mk->mark();
+    }
+    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, st, mk);
+    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, st, mk);
     return launched();
+}
+
+sa_status sparse_attn_decode(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                             const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
+                       nullptr);
+}
+
+sa_status sparse_attn_decode_profiled(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                      const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx,
+                                      void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                                      void *const *events, int32_t num_events, int32_t *num_marks)
+{
+    if (!num_marks || (num_events > 0 && !events)) return SA_ERR_NULL;
+    StageMarks mk;
+    mk.events = events;
+    mk.capacity = num_events;
+    const sa_status s = decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                                    workspace_bytes, stream, &mk);
+    *num_marks = mk.count;
+    return s;
 }
 
 sa_status sparse_attn_select_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
@@ -421,7 +476,8 @@ sa_status sparse_attn_select_prefill(const sa_params *p, const sa_paged_cache *c
     if (!idx_q || !idx_w || !topk_idx) return SA_ERR_NULL;
     const PrefillPlan d = plan_prefill(p, num_rows, q_start);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
-    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream);
+    clear_hip_error();
+    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream, nullptr);
     return launched();
 }
 
@@ -434,13 +490,14 @@ sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *c
     if (!q || !topk_idx || !out) return SA_ERR_NULL;
     const PrefillPlan d = plan_prefill(p, num_rows, q_start);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
-    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream);
+    clear_hip_error();
+    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream, nullptr);
     return launched();
 }
 
-sa_status sparse_attn_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
+static sa_status prefill_impl(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
                               const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
-                              float *lse, void *workspace, size_t workspace_bytes, void *stream)
+                              float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk)
 {
     sa_status s = check_prefill(p, c, num_rows, q_start, true, true);
     if (s != SA_OK) return s;
@@ -448,9 +505,38 @@ sa_status sparse_attn_prefill(const sa_params *p, const sa_paged_cache *c, int32
     const PrefillPlan d = plan_prefill(p, num_rows, q_start);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
-    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, st);
-    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, st);
+    clear_hip_error();
+    if (mk) {
+        mk->stream = st;
+        mk->mark();
+    }
+    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, st, mk);
+    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, st, mk);
     return launched();
+}
+
+sa_status sparse_attn_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
+                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                              float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    return prefill_impl(p, c, num_rows, q_start, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes,
+                        stream, nullptr);
+}
+
+sa_status sparse_attn_prefill_profiled(const sa_params *p, const sa_paged_cache *c, int32_t num_rows,
+                                       int32_t q_start, const void *q, const void *idx_q, const float *idx_w,
+                                       int32_t *topk_idx, void *out, float *lse, void *workspace,
+                                       size_t workspace_bytes, void *stream, void *const *events,
+                                       int32_t num_events, int32_t *num_marks)
+{
+    if (!num_marks || (num_events > 0 && !events)) return SA_ERR_NULL;
+    StageMarks mk;
+    mk.events = events;
+    mk.capacity = num_events;
+    const sa_status s = prefill_impl(p, c, num_rows, q_start, q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                                     workspace_bytes, stream, &mk);
+    *num_marks = mk.count;
+    return s;
 }
 
 }  // extern "C"

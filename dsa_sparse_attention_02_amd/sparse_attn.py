@@ -22,6 +22,7 @@ EXPORTS = (
     "sa_abi_version", "sa_status_string",
     "sa_decode_workspace_size", "sparse_attn_decode", "sparse_attn_select_decode", "sparse_attn_attend_decode",
     "sa_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_select_prefill", "sparse_attn_attend_prefill",
+    "sparse_attn_decode_profiled", "sparse_attn_prefill_profiled",
 )
 
 
@@ -68,6 +69,10 @@ def lib():
             "sparse_attn_prefill": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P]),
             "sparse_attn_select_prefill": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, sz, P]),
             "sparse_attn_attend_prefill": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, sz, P]),
+            "sparse_attn_decode_profiled": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P, P, i32,
+                                                           ctypes.POINTER(i32)]),
+            "sparse_attn_prefill_profiled": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P, P, i32,
+                                                            ctypes.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -207,6 +212,86 @@ def sparse_attn_decode(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx
                                     idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
                                     _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode")
     return topk_idx, out, lse
+
+
+def sparse_attn_decode_profiled(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, events, *,
+                                want_lse=True, workspace=None, outputs=None, stream=None):
+    """sparse_attn_decode that also records `events` (HipEvents) around its kernels.
+    Returns (topk_idx, out, lse, number of marks the call takes)."""
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    ev = (ctypes.c_void_p * max(1, len(events)))(*[e.handle for e in events])
+    n = ctypes.c_int32()
+    _check(lib().sparse_attn_decode_profiled(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
+                                             q.data_ptr(), idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(),
+                                             out.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream),
+                                             ev, len(events), ctypes.byref(n)), "sparse_attn_decode_profiled")
+    return topk_idx, out, lse, n.value
+
+
+def sparse_attn_prefill_profiled(p: Params, cache: PagedCache, q_start: int, q, idx_q, idx_w, events, *,
+                                 want_lse=True, workspace=None, outputs=None, stream=None):
+    """sparse_attn_prefill that also records `events` around its kernels."""
+    torch = _torch()
+    L = q.shape[0]
+    _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device)
+    ev = (ctypes.c_void_p * max(1, len(events)))(*[e.handle for e in events])
+    n = ctypes.c_int32()
+    _check(lib().sparse_attn_prefill_profiled(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start,
+                                              q.data_ptr(), idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(),
+                                              out.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream),
+                                              ev, len(events), ctypes.byref(n)), "sparse_attn_prefill_profiled")
+    return topk_idx, out, lse, n.value
+
+
+class HipEvent:
+    """A raw hipEvent_t (created with the HIP runtime) for the profiling entry points."""
+    _hip = None
+
+    @classmethod
+    def hip(cls):
+        if cls._hip is None:
+            # use the HIP runtime already mapped into the process (torch's), never a second copy
+            lib()
+            path = "libamdhip64.so.7"
+            with open("/proc/self/maps") as f:
+                for line in f:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            h = ctypes.CDLL(path)
+            h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        h = ctypes.c_void_p()
+        if self.hip().hipEventCreate(ctypes.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.handle = h.value
+
+    def elapsed_ms(self, later: "HipEvent") -> float:
+        t = ctypes.c_float()
+        if self.hip().hipEventSynchronize(later.handle) != 0 or \
+                self.hip().hipEventElapsedTime(ctypes.byref(t), self.handle, later.handle) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return t.value
+
+    def __del__(self):
+        if getattr(self, "handle", None) and self._hip is not None:
+            self._hip.hipEventDestroy(self.handle)
 
 
 def sparse_attn_select_decode(p: Params, cache: PagedCache, max_ctx: int, idx_q, idx_w, *, workspace=None,

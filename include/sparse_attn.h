@@ -145,6 +145,22 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *ca
                                     const int32_t *topk_idx, void *out, float *lse,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* Profiling variant of sparse_attn_decode: identical work, and additionally
+ * records caller-created HIP events (hipEvent_t handles in events[0 ..
+ * num_events)) on `stream`: events[0] before the first kernel and events[i]
+ * after the i-th kernel launch, while capacity lasts.  *num_marks (host, out)
+ * receives the number of marks the call takes (kernels + 1), whether or not
+ * they all fitted.  Kernel order: indexer scan (omitted when max_ctx <= topk),
+ * top-k, attention, split merge (omitted when one split covers topk).  The
+ * pages recommend profiling the time split across stages ("Day-0 Model
+ * Adaptation Depends on the Compute Software Stack", From Adaptation to
+ * Maturity).  events may be NULL when num_events is 0; num_marks is required. */
+sa_status sparse_attn_decode_profiled(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
+                                      int32_t max_ctx, const void *q, const void *idx_q,
+                                      const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                      void *workspace, size_t workspace_bytes, void *stream,
+                                      void *const *events, int32_t num_events, int32_t *num_marks);
+
 /* --------------------------------------------------------------- prefill --
  * num_rows query rows of sequence 0 (block_table row 0); row i sits at
  * position q_start + i and sees keys [0, q_start + i] (causal limit, itself
@@ -162,6 +178,16 @@ sa_status sparse_attn_select_prefill(const sa_params *p, const sa_paged_cache *c
                                      int32_t num_rows, int32_t q_start, const void *idx_q,
                                      const float *idx_w, int32_t *topk_idx, void *workspace,
                                      size_t workspace_bytes, void *stream);
+/* Profiling variant of sparse_attn_prefill (marks as for the decode variant).
+ * Kernel order: per chunk of rows, indexer tile scan (omitted while every row
+ * of the chunk sees at most topk keys) then top-k; then the attention kernel
+ * (and the split merge when topk > 2048), once per attention chunk. */
+sa_status sparse_attn_prefill_profiled(const sa_params *p, const sa_paged_cache *cache,
+                                       int32_t num_rows, int32_t q_start, const void *q,
+                                       const void *idx_q, const float *idx_w, int32_t *topk_idx,
+                                       void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                       void *stream, void *const *events, int32_t num_events,
+                                       int32_t *num_marks);
 /* Attend treats any index outside [0, q_start + i] of row i as padding. */
 sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *cache,
                                      int32_t num_rows, int32_t q_start, const void *q,
