@@ -29,6 +29,11 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError("hipcc failed to build libsparse_attn.so")
     if verbose:
         sys.stderr.write(res.stderr)
+    # every kernel's host launch stub must be defined in the library
+    nm = subprocess.run(["nm", "-D", "--undefined-only", tmp], capture_output=True, text=True)
+    missing = [l.split()[-1] for l in nm.stdout.splitlines() if "__device_stub__" in l]
+    if nm.returncode != 0 or missing:
+        raise RuntimeError(f"libsparse_attn.so has undefined kernel stubs: {missing[:4]}")
     os.replace(tmp, LIB)
     return LIB
 

@@ -21,8 +21,8 @@
 // tile of 32 kept tokens:
 //   * the 32 latent rows are copied HBM -> LDS by the LDS-DMA path
 //     (global_load_lds_dwordx4), 16-byte pieces XOR-swizzled by token so that
-//     MFMA operand reads do not collide on LDS banks; the next tile's copy is
-//     issued before the current tile's math;
+//     MFMA operand reads do not collide on LDS banks; a ring of 4 tile buffers
+//     keeps 3 tiles' copies in flight while one tile is computed;
 //   * the query of 32 heads (QK = 576: 144 registers per lane) and the 32 x 512
 //     fp32 output accumulators (256 registers) of one wave do not fit in the
 //     512-entry register file next to the q.k accumulator, so for V = 512 two
@@ -30,9 +30,10 @@
 //     computing the logits itself;
 //   * S^T[token][head] = K . Q^T on 32x32x16 bf16 MFMAs (K from LDS, Q^T from
 //     registers, contraction over QK in 16-wide steps);
-//   * online softmax in base 2 in fp32; the reference max only moves when the
-//     tile max exceeds it by more than 8 (so P <= 256), which keeps rescales of
-//     the output accumulators rare;
+//   * softmax in base 2 in fp32 against a per-head reference max taken from
+//     the first tile with a valid token; it never moves, so the output
+//     accumulators are touched only by MFMAs (a split whose logits outgrow the
+//     reference by more than 64 is recomputed exactly with its true max);
 //   * the S^T accumulator already has the register layout of the B operand of
 //     O^T[v][head] += V^T[v][token] . P^T[token][head]: P is only rounded to bf16.
 //     The softmax denominator sums the same rounded P.
@@ -66,6 +67,20 @@ struct AttnArgs {
     float scale_log2;            // softmax_scale * log2(e)
 };
 
+constexpr int kAttnBuffers = 4;  // tile ring: kAttnBuffers - 1 tiles in flight while one is computed
+
+// s_barrier without the memory fence __syncthreads adds (which would wait for
+// every LDS-DMA copy in flight); the asm memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void attn_wait_vmcnt()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
 template <int QK, int V>
 struct AttnShape {
     static constexpr int KS = QK / 16;                   // MFMA steps of q.k
@@ -74,6 +89,7 @@ struct AttnShape {
     static constexpr int VP = VW / 64;                   // 64-wide v groups (even + odd tiles)
     static constexpr int PIECES = QK / 8;                // 16-byte pieces per latent row
     static constexpr int TILE_BYTES = 32 * PIECES * 16;
+    static constexpr int DMA_PER_TILE = 32 * PIECES / 64;   // wave instructions per tile
     static_assert(QK % 16 == 0 && PIECES % 8 == 0 && VW % 64 == 0 && V <= QK, "shape family");
 };
 
@@ -88,9 +104,10 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
 {
     using S = AttnShape<QK, V>;
     constexpr int KS = S::KS, VP = S::VP, VW = S::VW, PIECES = S::PIECES;
-    __shared__ __attribute__((aligned(1024))) uint8_t tile[2][S::TILE_BYTES];
+    __shared__ __attribute__((aligned(1024))) uint8_t tile[kAttnBuffers][S::TILE_BYTES];
     __shared__ uint32_t rows[kAttnMaxSplitTokens];
     __shared__ uint32_t vbits[kAttnMaxSplitTokens / 32];
+    __shared__ int last_tile, overflow_flag;
 
     const int split = blockIdx.x / S::VSPLIT, vh = blockIdx.x % S::VSPLIT, r = blockIdx.y;
     const int nthreads = blockDim.x, nw = nthreads >> 6;
@@ -122,9 +139,13 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
         if (lane == 0) vbits[jb >> 5] = (uint32_t)m;
         if (lane == 32 && jb + 32 < ntiles * 32) vbits[(jb >> 5) + 1] = (uint32_t)(m >> 32);
     }
-    // zero both tile buffers: slots of padding tokens are never copied into, and
+    if (threadIdx.x == 0) {
+        last_tile = -1;
+        overflow_flag = 0;
+    }
+    // zero the tile buffers: slots of padding tokens are never copied into, and
     // they are multiplied by P = 0, so they must hold finite values
-    for (int e = threadIdx.x; e < 2 * S::TILE_BYTES / 16; e += nthreads)
+    for (int e = threadIdx.x; e < kAttnBuffers * S::TILE_BYTES / 16; e += nthreads)
         reinterpret_cast<u32x4 *>(&tile[0][0])[e] = u32x4{0, 0, 0, 0};
 
     const int head = 32 * wave + col;
@@ -146,7 +167,12 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
     // m: reference max (log2 units); l: sum of the bf16-rounded weights (output
     // normaliser); le: sum of the unrounded weights (log-sum-exp)
     float m = -INFINITY, l = 0.0f, le = 0.0f;
+    bool ovf = false;
     __syncthreads();
+    for (int t = threadIdx.x; t < ntiles; t += nthreads)
+        if (vbits[t]) atomicMax(&last_tile, t);
+    __syncthreads();
+    const int nt_eff = last_tile + 1;  // tiles after the last valid token are skipped
 
     auto issue_tile = [&](int t, int buf) {
         for (int ii = wave; ii < 32 * PIECES / 64; ii += nw) {
@@ -154,8 +180,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
             const int tj = L / PIECES, p = tile_slot(tj, L % PIECES);
             const uint32_t row = rows[t * 32 + tj];
             if (row != kNoRow)
-                __builtin_amdgcn_global_load_lds(a.kv + (int64_t)row * QK + p * 8,
-                                                 (SA_LDS void *)&tile[buf][ii * 1024], 16, 0, 0);
+                dma16_to_lds(a.kv + (int64_t)row * QK + p * 8, (SA_LDS void *)&tile[buf][ii * 1024]);
         }
     };
 
@@ -185,12 +210,15 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
             }
         }
         const uint8_t *tb = tile[buf];
-        f32x16 s = f32x16{};
+        // two accumulators (even / odd steps) halve the dependent MFMA chain
+        f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff[ks & 3] + 128 * (ks >> 2)));
-            s = mfma_32x32x16(ka, qb[ks], s);
+            if (ks & 1) s1 = mfma_32x32x16(ka, qb[ks], s1);
+            else s0 = mfma_32x32x16(ka, qb[ks], s0);
         }
+        f32x16 s = s0 + s1;
         const uint32_t vb = vbits[t] >> (4 * hf);  // bit acc_row(i, hf) - 4hf = 8(i/4) + i%4
         float tmax = -INFINITY;
 #pragma unroll
@@ -200,27 +228,23 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
             tmax = fmaxf(tmax, s[i]);
         }
         tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-        const float mnew = tmax > m + 8.0f ? tmax : m;
-        const bool moved = mnew != m;
-        if (__any(moved)) {
-            const float alpha = moved ? exp2f(m - mnew) : 1.0f;
-            l *= alpha;
-            le *= alpha;
-#pragma unroll
-            for (int vp = 0; vp < VP; ++vp) {
-                oe[vp] *= alpha;
-                oo[vp] *= alpha;
-            }
-        }
-        m = mnew;
+        // The reference max is fixed by the first tile with a valid token for this
+        // head (until then O and l are 0, so nothing needs rescaling) and never
+        // moves afterwards: the output accumulators are only ever touched by the
+        // MFMAs.  Weights are exp2(min(s - m, 64)), finite in fp32 and bf16; a head
+        // whose logits outgrow its reference by more than 64 raises `ovf`, and the
+        // split is then recomputed exactly with its true max (below).
+        if (m == -INFINITY) m = tmax;
+        ovf |= tmax > m + 64.0f;
         bf16x8 pb[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             u32x4 w;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float p0 = (m == -INFINITY) ? 0.0f : exp2f(s[8 * k2 + 2 * jj] - m);
-                const float p1 = (m == -INFINITY) ? 0.0f : exp2f(s[8 * k2 + 2 * jj + 1] - m);
+                const float x0 = s[8 * k2 + 2 * jj], x1 = s[8 * k2 + 2 * jj + 1];
+                const float p0 = x0 == -INFINITY ? 0.0f : exp2f(fminf(x0 - m, 64.0f));
+                const float p1 = x1 == -INFINITY ? 0.0f : exp2f(fminf(x1 - m, 64.0f));
                 w[jj] = pack_bf16x2(p0, p1);
                 // the normaliser sums the same bf16-rounded weights the MFMA
                 // multiplies V by, so the output is an exact weighted mean of
@@ -250,12 +274,67 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
         }
     };
 
-    if (ntiles > 0 && vbits[0]) issue_tile(0, 0);
+    // Ring of kAttnBuffers tiles.  Iteration t: wait until this wave's copies of
+    // tile t have landed (at most the kAttnBuffers-2 younger tiles' copies still in
+    // flight), barrier (every wave's share of tile t is in LDS, and every wave is
+    // done reading tile t-1's buffer), refill that buffer with tile
+    // t+kAttnBuffers-1, then compute tile t.  Tiles of padding only are neither
+    // copied nor computed (block-uniform).  Each wave issues the same number of
+    // copies per tile only when nw divides DMA_PER_TILE; otherwise the wait count
+    // below is still an upper bound of the younger copies, so it only over-waits.
+    constexpr int DMA_W = (S::DMA_PER_TILE + 3) / 4;  // copies per wave per tile, 4 waves
+#pragma unroll
+    for (int j = 0; j < kAttnBuffers - 1; ++j)
+        if (j < nt_eff) issue_tile(j, j);
+    for (int t = 0; t < nt_eff; ++t) {
+        if (nw == 4) attn_wait_vmcnt<DMA_W * (kAttnBuffers - 2)>();
+        else attn_wait_vmcnt<0>();
+        barrier_no_fence();
+        const int tn = t + kAttnBuffers - 1;
+        if (tn < nt_eff) issue_tile(tn, tn % kAttnBuffers);
+        compute(t, t % kAttnBuffers);
+    }
+
+    // Exact recompute of the split when some head's logits outgrew its reference
+    // max by more than 64 (never for logits within a few dozen of each other):
+    // pass 1 finds every head's true max, pass 2 redoes the weighted sum with it.
+    if (ovf) overflow_flag = 1;
     __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
-        if (t + 1 < ntiles && vbits[t + 1]) issue_tile(t + 1, (t + 1) & 1);
-        if (vbits[t]) compute(t, t & 1);  // block-uniform: a tile of padding only is skipped
-        __syncthreads();
+    if (overflow_flag) {
+        float mt = -INFINITY;
+        for (int t = 0; t < nt_eff; ++t) {
+            issue_tile(t, 0);
+            __syncthreads();
+            const uint8_t *tb = tile[0];
+            f32x16 s0 = f32x16{};
+            const int xk = (col >> 1) & 7;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int slot = 8 * (ks >> 2) + ((2 * (ks & 3) + half) ^ xk);
+                s0 = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + (col * PIECES + slot) * 16)),
+                                   qb[ks], s0);
+            }
+            const uint32_t vb = vbits[t] >> (4 * half);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if ((vb >> (8 * (i >> 2) + (i & 3))) & 1u) mt = fmaxf(mt, s0[i] * a.scale_log2);
+            __syncthreads();
+        }
+        mt = fmaxf(mt, __shfl_xor(mt, 32));
+        m = mt;
+        l = 0.0f;
+        le = 0.0f;
+#pragma unroll
+        for (int vp = 0; vp < VP; ++vp) {
+            oe[vp] = f32x16{};
+            oo[vp] = f32x16{};
+        }
+        for (int t = 0; t < nt_eff; ++t) {
+            issue_tile(t, 0);
+            __syncthreads();
+            compute(t, 0);  // s <= m now, so no weight is clamped
+            __syncthreads();
+        }
     }
 
     const float lt = l + __shfl_xor(l, 32);

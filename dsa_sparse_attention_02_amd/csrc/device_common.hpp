@@ -46,6 +46,28 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
     return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, b2));
 }
 
+// Copy 16 bytes per lane from global memory straight into LDS (gfx950 LDS-DMA):
+// lane i of the wave writes lds_wave_base + 16*i.  The LDS base must be
+// wave-uniform.  Completion is counted by vmcnt; the compiler does not track
+// it for later LDS reads, so callers wait explicitly (or at a barrier).
+__device__ __forceinline__ void dma16_to_lds(const void *src, SA_LDS void *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
+}
+
+// Min and max of v over the 32 lanes of each wave half (every lane gets them);
+// lanes with valid == false are ignored.
+__device__ __forceinline__ f32x2 minmax32(float v, bool valid)
+{
+    float mn = valid ? v : INFINITY, mx = valid ? v : -INFINITY;
+#pragma unroll
+    for (int d = 16; d >= 1; d >>= 1) {
+        mn = fminf(mn, __shfl_xor(mn, d));
+        mx = fmaxf(mx, __shfl_xor(mx, d));
+    }
+    return f32x2{mn, mx};
+}
+
 // Order-preserving map from an fp32 score to uint32: a larger key is a larger
 // score; -0 is folded into +0 first so the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float f)

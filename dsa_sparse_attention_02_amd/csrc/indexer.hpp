@@ -21,86 +21,199 @@
 namespace sa {
 
 // ------------------------------------------------------------------ decode --
-// Grid (ceil(max_ctx / (4*keys_per_wave)), batch), 256 threads.  Wave w of
-// block x scans keys [(4x+w)*keys_per_wave, +keys_per_wave) of sequence
-// blockIdx.y, clipped to its context length, in tiles of 32 keys loaded
-// straight from the paged cache into MFMA operands (each key row is one
-// contiguous read per lane pair), with the next tile's loads issued before the
-// current tile's matrix work.
-template <int IDX_DIM, int IDX_TILES>
-__global__ __launch_bounds__(256) void idx_score_decode_kernel(
-    const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int max_blocks,
-    int bs_log2, const int32_t *__restrict__ ctx_lens, const uint16_t *__restrict__ idx_q,
-    const float *__restrict__ idx_w, int idx_heads, int relu, float *__restrict__ scores,
-    int64_t score_stride, int keys_per_wave)
+// Persistent key scan.  The visible keys of all rows form one list of 32-key
+// tiles (row-major, each row's tiles in key order); wave g of G takes the
+// contiguous tiles [g*T/G, (g+1)*T/G), so every wave moves the same number of
+// bytes whatever the context lengths.  Key tiles stream HBM -> LDS through the
+// LDS-DMA path (global_load_lds_dwordx4) in a kStages-deep per-wave ring: one DMA
+// instruction fetches four whole 256-byte key rows (1 KB contiguous per row
+// group), and the 16-byte pieces are XOR-swizzled so that the MFMA operand reads
+// (32 rows x one piece per half-wave) hit 16 distinct bank groups.  Waves never
+// share LDS, so the only synchronisation is each wave's own vmcnt wait.
+#ifndef SA_SCAN_STAGES
+#define SA_SCAN_STAGES 2
+#endif
+#ifndef SA_SCAN_WAVES
+#define SA_SCAN_WAVES 8
+#endif
+constexpr int kScanStages = SA_SCAN_STAGES;       // tiles per wave ring (stages-1 in flight while one is scored)
+constexpr int kScanWavesPerBlock = SA_SCAN_WAVES;
+
+// s_waitcnt vmcnt(n) that also fences the compiler: LDS written by the DMA path
+// is not tracked by the compiler's own wait insertion.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt()
 {
-    constexpr int KS = IDX_DIM / 16;
-    const int b = blockIdx.y;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// BLOCK_TILE: every cache block holds a whole number of 32-key tiles (block_size
+// >= 32), so a tile's 32 rows are contiguous and its block id is one scalar load.
+template <int IDX_DIM, int IDX_TILES, bool BLOCK_TILE>
+__global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kernel(
+    const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int max_blocks,
+    int bs_log2, const int32_t *__restrict__ ctx_lens, int batch, const uint16_t *__restrict__ idx_q,
+    const float *__restrict__ idx_w, int idx_heads, int relu, float *__restrict__ scores,
+    int64_t score_stride, f32x2 *__restrict__ tile_mm, int64_t mm_stride)
+{
+    constexpr int KS = IDX_DIM / 16;            // MFMA steps per key row
+    constexpr int PIECES = IDX_DIM / 8;         // 16-byte pieces per key row
+    constexpr int TILE = 32 * IDX_DIM * 2;      // bytes per 32-key tile
+    constexpr int DMA = TILE / 1024;            // DMA instructions per tile
+    static_assert(PIECES == 16 || PIECES == 4, "key row of 256 or 64 bytes");
+    constexpr int SW = PIECES - 1;              // swizzle mask
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[kScanWavesPerBlock][kScanStages][TILE];
+
+    // wave index made visibly wave-uniform so cursors live in scalar registers and
+    // context lengths / block-table entries are scalar loads
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
-    const int ctx = ctx_lens[b];
-    const int s_begin = (blockIdx.x * 4 + wave) * keys_per_wave;
-    if (s_begin >= ctx) return;  // wave-uniform; the kernel has no barriers
-    const int s_end = min(ctx, s_begin + keys_per_wave);
+    const int bmask = (1 << bs_log2) - 1;
+    uint8_t *my = &ring[wave][0][0];
+
+    // this wave's share [t_begin, t_end) of all tiles of all rows
+    int64_t total = 0;
+    for (int b = 0; b < batch; ++b) total += (ctx_lens[b] + 31) >> 5;
+    const int64_t G = (int64_t)gridDim.x * kScanWavesPerBlock;
+    const int64_t g = (int64_t)blockIdx.x * kScanWavesPerBlock + wave;
+    int64_t t_cur = total * g / G;
+    const int64_t t_end = total * (g + 1) / G;
+    if (t_cur >= t_end) return;
+    int b = 0;
+    int64_t row_first = 0;  // global index of row b's first tile
+    for (;; ++b) {
+        const int nt = (ctx_lens[b] + 31) >> 5;
+        if (t_cur < row_first + nt) break;
+        row_first += nt;
+    }
+
+    // the DMA lane map: instruction i, lane l writes slot 64i + l = PIECES*r + q, which
+    // holds piece q ^ (r & SW) of the tile's key row r
+    int dma_r[DMA], dma_piece[DMA];
+#pragma unroll
+    for (int i = 0; i < DMA; ++i) {
+        const int slot = 64 * i + lane;
+        dma_r[i] = slot / PIECES;
+        dma_piece[i] = (slot % PIECES) ^ (dma_r[i] & SW);
+    }
+    // lane (key col, half) reads piece half*KS + ks of its row at step ks
+    const int koff = col * PIECES * 16;
+    const int kx = col & SW;
 
     bf16x8 qa[IDX_TILES][KS];
     float wr[IDX_TILES][16];
-#pragma unroll
-    for (int t = 0; t < IDX_TILES; ++t) {
-        const int head = 32 * t + col;
-        const uint16_t *qp = idx_q + ((int64_t)b * idx_heads + head) * IDX_DIM + half * (IDX_DIM / 2);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qa[t][ks] = head < idx_heads ? as_bf16x8(load16(qp + 8 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const int hj = 32 * t + acc_row(i, half);
-            wr[t][i] = hj < idx_heads ? idx_w[(int64_t)b * idx_heads + hj] : 0.0f;
-        }
-    }
 
-    const int32_t *tbl = block_table + (int64_t)b * max_blocks;
-    const int bmask = (1 << bs_log2) - 1;
-    float *out = scores + (int64_t)b * score_stride;
-
-    auto load_tile = [&](int s0, u32x4 (&kb)[KS]) {
-        const int s = s0 + col;
-        if (s < s_end) {
-            const int64_t row = ((int64_t)tbl[s >> bs_log2] << bs_log2) | (s & bmask);
-            const uint16_t *kp = idx_k + row * IDX_DIM + half * (IDX_DIM / 2);
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kb[ks] = load16(kp + 8 * ks);
+    // per-segment state, read by the helpers below
+    int ctx = 0, nt = 0;
+    const int32_t *tbl = block_table;
+    // Physical row of a tile's first key (BLOCK_TILE).  A window of 64 block-table
+    // entries sits in one register (lane i holds entry lo + i) and is read with
+    // v_readlane, so the steady state issues no memory request for the table;
+    // the window is refilled once per 64 blocks.
+    int win_lo = -(1 << 30), win = 0;
+    auto tile_base = [&](int t) -> int64_t {
+        if constexpr (BLOCK_TILE) {
+            const int s0 = (t < nt - 1 ? t : nt - 1) * 32;
+            const int bi = s0 >> bs_log2;
+            if (bi < win_lo || bi >= win_lo + 64) {
+                win_lo = bi;
+                win = bi + lane < max_blocks ? tbl[bi + lane] : 0;
+            }
+            const int blk = __builtin_amdgcn_readlane(win, bi - win_lo);
+            return ((int64_t)blk << bs_log2) | (s0 & bmask);
         } else {
+            return 0;
+        }
+    };
+    auto issue = [&](int t, int stage, int64_t base) {
+        const int s0 = t * 32;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kb[ks] = u32x4{0, 0, 0, 0};
+        for (int i = 0; i < DMA; ++i) {
+            int s = s0 + dma_r[i];
+            s = s < ctx ? s : ctx - 1;  // rows past the context re-read the last key; never scored
+            int64_t row;
+            if constexpr (BLOCK_TILE) row = base + (s - s0);
+            else row = ((int64_t)tbl[s >> bs_log2] << bs_log2) | (s & bmask);
+            dma16_to_lds(idx_k + row * IDX_DIM + dma_piece[i] * 8, (SA_LDS void *)(my + stage * TILE + i * 1024));
         }
     };
 
-    u32x4 cur[KS], nxt[KS];
-    load_tile(s_begin, cur);
-    for (int s0 = s_begin; s0 < s_end; s0 += 32) {
-        if (s0 + 32 < s_end) load_tile(s0 + 32, nxt);
-        f32x16 acc[IDX_TILES];
+    // one row segment at a time: [t0, t1) tiles of row b
+    while (t_cur < t_end) {
+        ctx = ctx_lens[b];
+        nt = (ctx + 31) >> 5;
+        const int t0 = (int)(t_cur - row_first);
+        const int64_t rem = t_end - row_first;
+        const int t1 = rem < nt ? (int)rem : nt;
+        tbl = block_table + (int64_t)b * max_blocks;
+        win_lo = -(1 << 30);
+        float *out = scores + (int64_t)b * score_stride;
+
+        // queries and head weights of row b (waits for everything in flight: once per segment)
 #pragma unroll
-        for (int t = 0; t < IDX_TILES; ++t) acc[t] = f32x16{};
+        for (int t = 0; t < IDX_TILES; ++t) {
+            const int head = 32 * t + col;
+            const uint16_t *qp = idx_q + ((int64_t)b * idx_heads + head) * IDX_DIM + half * (IDX_DIM / 2);
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-#pragma unroll
-            for (int t = 0; t < IDX_TILES; ++t) acc[t] = mfma_32x32x16(qa[t][ks], as_bf16x8(cur[ks]), acc[t]);
-        float part = 0.0f;
-#pragma unroll
-        for (int t = 0; t < IDX_TILES; ++t)
+            for (int ks = 0; ks < KS; ++ks)
+                qa[t][ks] = head < idx_heads ? as_bf16x8(load16(qp + 8 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
-                float d = acc[t][i];
-                if (relu) d = fmaxf(d, 0.0f);
-                part = fmaf(wr[t][i], d, part);
+                const int hj = 32 * t + acc_row(i, half);
+                wr[t][i] = hj < idx_heads ? idx_w[(int64_t)b * idx_heads + hj] : 0.0f;
             }
-        const float tot = part + __shfl_xor(part, 32);
-        const int s = s0 + col;
-        if (half == 0 && s < s_end) out[s] = tot + 0.0f;
+        }
+
+        const int n = t1 - t0;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) cur[ks] = nxt[ks];
+        for (int j = 0; j < kScanStages - 1; ++j)
+            if (j < n) issue(t0 + j, j, tile_base(t0 + j));
+        int64_t base_next = tile_base(t0 + kScanStages - 1);
+        for (int j = 0; j < n; ++j) {
+            const int stage = j % kScanStages;
+            if (j + kScanStages - 1 < n) {
+                issue(t0 + j + kScanStages - 1, (j + kScanStages - 1) % kScanStages, base_next);
+                base_next = tile_base(t0 + j + kScanStages);
+                wait_vmcnt<DMA * (kScanStages - 1)>();
+            } else {
+                wait_vmcnt<0>();
+            }
+            const uint8_t *tb = my + stage * TILE;
+            // all B operands of the tile first, so the LDS reads overlap each other
+            bf16x8 kb[KS];
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+                kb[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff + (((half * KS + ks) ^ kx) * 16)));
+            // two accumulators per head tile (even / odd steps) halve the dependent MFMA chain
+            f32x16 acc[IDX_TILES][2];
+#pragma unroll
+            for (int t = 0; t < IDX_TILES; ++t) acc[t][0] = acc[t][1] = f32x16{};
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int t = 0; t < IDX_TILES; ++t) acc[t][ks & 1] = mfma_32x32x16(qa[t][ks], kb[ks], acc[t][ks & 1]);
+            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < IDX_TILES; ++t)
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    float d = acc[t][0][i] + acc[t][1][i];
+                    if (relu) d = fmaxf(d, 0.0f);
+                    part[i & 3] = fmaf(wr[t][i], d, part[i & 3]);
+                }
+            const float p = (part[0] + part[1]) + (part[2] + part[3]);
+            const float tot = p + __shfl_xor(p, 32);
+            const int s = (t0 + j) * 32 + col;
+            if (half == 0 && s < ctx) out[s] = tot + 0.0f;
+            // the tile's score range, for the range-binned top-k histogram
+            const f32x2 mm = minmax32(tot + 0.0f, s < ctx);
+            if (lane == 0) tile_mm[(int64_t)b * mm_stride + t0 + j] = mm;
+        }
+        t_cur = row_first + t1;
+        row_first += nt;
+        ++b;
+        while (t_cur < t_end && ((ctx_lens[b] + 31) >> 5) == 0) ++b;  // skip empty rows
     }
 }
 
@@ -117,7 +230,8 @@ template <int IDX_DIM, int IDX_TILES>
 __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
     const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int bs_log2,
     const uint16_t *__restrict__ idx_q, const float *__restrict__ idx_w, int idx_heads, int relu,
-    int pos0, int nrows, float *__restrict__ scores, int64_t score_stride)
+    int pos0, int nrows, float *__restrict__ scores, int64_t score_stride, f32x2 *__restrict__ tile_mm,
+    int64_t mm_stride)
 {
     constexpr int KS = IDX_DIM / 16;
     constexpr int ROW_BYTES = IDX_DIM * 2 + 16;  // +16: consecutive keys start 4 banks apart
@@ -172,6 +286,7 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
     };
 
     const int ntiles = (nkeys + 31) / 32;
+    float rlo[2] = {INFINITY, INFINITY}, rhi[2] = {-INFINITY, -INFINITY};
     stash(0, fetch(0));
     __syncthreads();
     for (int kt = 0; kt < ntiles; ++kt) {
@@ -211,10 +326,21 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
                 const float tot = part + __shfl_xor(part, 32);
                 const int s = s0 + col;
                 if (half == 0 && s <= pos[rr]) scores[(int64_t)(r0 + lr) * score_stride + s] = tot + 0.0f;
+                if (s <= pos[rr]) {  // lane-local running range of the row's scores
+                    rlo[rr] = fminf(rlo[rr], tot + 0.0f);
+                    rhi[rr] = fmaxf(rhi[rr], tot + 0.0f);
+                }
             }
         }
         if (kt + 1 < ntiles) stash(buf ^ 1, nxt);
         __syncthreads();
+    }
+    // each row's score range, stored as the row's first tile entry (the prefill
+    // top-k reads one range entry per row)
+#pragma unroll
+    for (int rr = 0; rr < 2; ++rr) {
+        const f32x2 lohi = minmax32(rlo[rr], true), hilo = minmax32(rhi[rr], true);
+        if (lane == 0 && pos[rr] >= 0) tile_mm[(int64_t)(r0 + 2 * wave + rr) * mm_stride] = f32x2{lohi[0], hilo[1]};
     }
 }
 

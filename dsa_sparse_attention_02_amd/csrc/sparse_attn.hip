@@ -26,7 +26,7 @@ using namespace sa;
 
 constexpr int kMaxTopk = 16384;
 constexpr int kTargetAttnBlocks = 256;        // one attention workgroup per CU of an MI355X
-constexpr int kTargetIndexerWaves = 4096;     // 16 waves per CU for the decode key scan
+constexpr int kCUs = 256;                     // compute units of an MI355X
 constexpr size_t kPrefillScoreBudget = size_t(256) << 20;  // bytes of scores per prefill chunk
 constexpr size_t kPrefillPartialBudget = size_t(256) << 20;
 constexpr size_t kAlign = 256;
@@ -69,9 +69,9 @@ sa_status check_cache(const sa_params *p, const sa_paged_cache *c, bool need_kv,
 
 // ------------------------------------------------------------------ plans --
 struct DecodePlan {
-    int64_t score_stride;
-    int splits, tokens_per_split, keys_per_wave;
-    size_t off_scores, off_part_o, off_part_ml, total;
+    int64_t score_stride, mm_stride;  // floats per score row; tiles per min/max row
+    int splits, tokens_per_split, scan_blocks;
+    size_t off_scores, off_mm, off_part_o, off_part_ml, total;
 };
 
 DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
@@ -79,7 +79,8 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
     DecodePlan d{};
     d.score_stride = round_up(max_ctx > 0 ? max_ctx : 1, 64);
     const int k = p->topk;
-    int splits = (kTargetAttnBlocks + batch - 1) / batch;
+    const int vsplit = p->v_dim > 256 ? 2 : 1;  // value halves per (row, split), as in the attention kernel
+    int splits = std::max(1, kTargetAttnBlocks / (batch * vsplit));
     splits = std::max(1, std::min(splits, (k + 31) / 32));
     splits = std::max(splits, (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens);
     int tps = (int)round_up((k + splits - 1) / splits, 32);
@@ -87,14 +88,15 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
     splits = (k + tps - 1) / tps;
     d.splits = splits;
     d.tokens_per_split = tps;
-    const int64_t keys = (int64_t)batch * std::max(max_ctx, 1);
-    int64_t kpw = keys / kTargetIndexerWaves;
-    int kp = 32;
-    while (kp < 1024 && (int64_t)kp * 2 <= kpw) kp *= 2;
-    d.keys_per_wave = kp;
+    // persistent scan: one block of 4 waves per CU, fewer when there are few tiles
+    const int64_t tiles = (int64_t)batch * ((std::max(max_ctx, 1) + 31) / 32);
+    d.scan_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(kCUs, (tiles + 31) / 32));
     size_t off = 0;
     d.off_scores = off;
     off = align_up(off + (size_t)batch * d.score_stride * 4, kAlign);
+    d.mm_stride = d.score_stride / 32;
+    d.off_mm = off;
+    off = align_up(off + (size_t)batch * d.mm_stride * 8, kAlign);
     d.off_part_o = off;
     if (splits > 1) {
         off = align_up(off + (size_t)batch * splits * p->num_heads * p->v_dim * 4, kAlign);
@@ -108,11 +110,11 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
 }
 
 struct PrefillPlan {
-    int64_t score_stride;
+    int64_t score_stride, mm_stride;
     int chunk_rows;          // rows per indexer/top-k chunk
     int splits, tokens_per_split;
     int attn_chunk_rows;     // rows per attention launch when splits > 1
-    size_t off_scores, off_part_o, off_part_ml, total;
+    size_t off_scores, off_mm, off_part_o, off_part_ml, total;
 };
 
 PrefillPlan plan_prefill(const sa_params *p, int num_rows, int q_start)
@@ -129,6 +131,9 @@ PrefillPlan plan_prefill(const sa_params *p, int num_rows, int q_start)
     size_t off = 0;
     d.off_scores = off;
     off = align_up(off + (size_t)d.chunk_rows * d.score_stride * 4, kAlign);
+    d.mm_stride = d.score_stride / 32;
+    d.off_mm = off;
+    off = align_up(off + (size_t)d.chunk_rows * d.mm_stride * 8, kAlign);
     d.off_part_o = off;
     d.attn_chunk_rows = num_rows;
     if (d.splits > 1) {
@@ -201,50 +206,55 @@ struct StageMarks {
 
 // --------------------------------------------------------------- launches --
 template <int D, int T>
-void launch_idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
-                       const float *idx_w, float *scores, int64_t stride, int kpw, hipStream_t st)
+void launch_idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *idx_q,
+                       const float *idx_w, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, int blocks,
+                       hipStream_t st)
 {
-    const int per_block = 4 * kpw;
-    dim3 grid((max_ctx + per_block - 1) / per_block, batch);
-    if (grid.x == 0) return;
-    hipLaunchKernelGGL((idx_score_decode_kernel<D, T>), grid, dim3(256), 0, st,
-                       (const uint16_t *)c->idx_k, c->block_table, c->max_blocks_per_seq, ilog2(p->block_size),
-                       c->context_lens, (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, kpw);
+    const dim3 grid(blocks), block(64 * kScanWavesPerBlock);
+    if (p->block_size >= 32)
+        hipLaunchKernelGGL((idx_score_decode_kernel<D, T, true>), grid, block, 0, st, (const uint16_t *)c->idx_k,
+                           c->block_table, c->max_blocks_per_seq, ilog2(p->block_size), c->context_lens, batch,
+                           (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, mm, mm_stride);
+    else
+        hipLaunchKernelGGL((idx_score_decode_kernel<D, T, false>), grid, block, 0, st, (const uint16_t *)c->idx_k,
+                           c->block_table, c->max_blocks_per_seq, ilog2(p->block_size), c->context_lens, batch,
+                           (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, mm, mm_stride);
 }
 
-void idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
-                const float *idx_w, float *scores, int64_t stride, int kpw, hipStream_t st)
+void idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *idx_q, const float *idx_w,
+                float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, int blocks, hipStream_t st)
 {
     const bool two = p->idx_heads > 32;
     if (p->idx_dim == 128) {
-        if (two) launch_idx_decode<128, 2>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
-        else launch_idx_decode<128, 1>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
+        if (two) launch_idx_decode<128, 2>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
+        else launch_idx_decode<128, 1>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
     } else {
-        if (two) launch_idx_decode<32, 2>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
-        else launch_idx_decode<32, 1>(p, c, batch, max_ctx, idx_q, idx_w, scores, stride, kpw, st);
+        if (two) launch_idx_decode<32, 2>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
+        else launch_idx_decode<32, 1>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
     }
 }
 
 template <int D, int T>
 void launch_idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w,
-                        int pos0, int nrows, float *scores, int64_t stride, hipStream_t st)
+                        int pos0, int nrows, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride,
+                        hipStream_t st)
 {
     dim3 grid((nrows + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock);
     hipLaunchKernelGGL((idx_score_prefill_kernel<D, T>), grid, dim3(512), 0, st, (const uint16_t *)c->idx_k,
                        c->block_table, ilog2(p->block_size), idx_q, idx_w, p->idx_heads, p->idx_relu, pos0, nrows,
-                       scores, stride);
+                       scores, stride, mm, mm_stride);
 }
 
 void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w, int pos0,
-                 int nrows, float *scores, int64_t stride, hipStream_t st)
+                 int nrows, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, hipStream_t st)
 {
     const bool two = p->idx_heads > 32;
     if (p->idx_dim == 128) {
-        if (two) launch_idx_prefill<128, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
-        else launch_idx_prefill<128, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
+        if (two) launch_idx_prefill<128, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
+        else launch_idx_prefill<128, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
     } else {
-        if (two) launch_idx_prefill<32, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
-        else launch_idx_prefill<32, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, st);
+        if (two) launch_idx_prefill<32, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
+        else launch_idx_prefill<32, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
     }
 }
 
@@ -295,12 +305,13 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
                    StageMarks *mk)
 {
     float *scores = (float *)((char *)ws + d.off_scores);
+    f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
     if (max_ctx > p->topk) {
-        idx_decode(p, c, batch, max_ctx, idx_q, idx_w, scores, d.score_stride, d.keys_per_wave, st);
+        idx_decode(p, c, batch, idx_q, idx_w, scores, d.score_stride, mm, d.mm_stride, d.scan_blocks, st);
         if (mk) mk->mark();
     }
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
-                       c->context_lens, 0, p->topk, topk_idx);
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
+                       d.mm_stride, 0, c->context_lens, 0, p->topk, topk_idx);
     if (mk) mk->mark();
 }
 
@@ -321,17 +332,18 @@ void select_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, i
                     StageMarks *mk)
 {
     float *scores = (float *)((char *)ws + d.off_scores);
+    f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
     for (int r0 = 0; r0 < num_rows; r0 += d.chunk_rows) {
         const int nr = std::min(d.chunk_rows, num_rows - r0);
         const int pos0 = q_start + r0;
         // rows whose whole context fits in k need no scores
         if (pos0 + nr > p->topk) {
             idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
-                        idx_w + (int64_t)r0 * p->idx_heads, pos0, nr, scores, d.score_stride, st);
+                        idx_w + (int64_t)r0 * p->idx_heads, pos0, nr, scores, d.score_stride, mm, d.mm_stride, st);
             if (mk) mk->mark();
         }
-        hipLaunchKernelGGL(topk_rows_kernel, dim3(nr), dim3(kTopkThreads), 0, st, scores, d.score_stride,
-                           (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk);
+        hipLaunchKernelGGL(topk_rows_kernel, dim3(nr), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
+                           d.mm_stride, 1, (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk);
         if (mk) mk->mark();
     }
 }

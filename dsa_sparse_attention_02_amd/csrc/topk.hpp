@@ -5,24 +5,35 @@
 // positions in ascending order (all n positions when n <= k, -1 padded).  The
 // pages ask for top-k over long rows that stays fast and stable at large k
 // ("Day-0 Adaptation for LLMs: Implementing Sparse Attention and Low-Precision
-// Weights", section III.1) and report that grouping the selection by row,
+// Weights", section III.1), name sorting or threshold filtering as the two ways
+// to select ("Day-0 Adaptation: Running Trillion-Parameter Models on Domestic
+// AI Accelerators", section 3.1), and report that grouping the selection by row,
 // buffering in on-chip shared memory and vectorised loads removed the thread
 // divergence of the data-dependent selection ("Engineering Practices for Day-0
 // Adaptation of Million-Token Context Models on Domestic AI Chips", Four Key
-// Layers item 1).  On gfx950 that becomes one 1024-thread workgroup per row with
-// LDS histograms and 16-byte score loads:
+// Layers item 1).  On gfx950: one 1024-thread workgroup per row, LDS histograms
+// and bitmaps, 16-byte score loads.
 //
-//  1. Radix select on order-preserving uint32 keys, 11 + 11 + 10 bits: each pass
-//     histograms (in LDS) the next digit of the keys that match the prefix found
-//     so far, and a suffix scan of the histogram picks the digit at which the
-//     running count from the top reaches k.  After three passes the exact
-//     threshold key T is known, with `gt` keys strictly above it and need = k - gt
-//     keys equal to T still to take.
-//  2. One ordered pass: a key is kept when key > T, or key == T and fewer than
-//     `need` equal keys precede it.  With G and E the counts of greater and equal
-//     keys before position s, a kept key lands at output slot G + min(E, need), so a
-//     single block-wide exclusive scan of packed (G, E) counts yields ascending
-//     output with the lowest-position tie-break, deterministically.
+// Threshold path (rows up to kBitmapKeys keys):
+//  1. The scoring kernels leave each 32-key tile's min and max; their reduction
+//     gives the row's score range [lo, hi] without touching the scores.
+//  2. Pass 1 histograms the scores into 2048 equal-width bins over [lo, hi]
+//     (a monotone map, so whole bins are ordered) and a suffix scan finds the bin
+//     T_bin holding the k-th largest score: `above` scores lie in higher bins,
+//     need = k - above must come from T_bin.
+//  3. Pass 2 marks every score of a higher bin in an LDS bitmap of positions and
+//     collects T_bin's scores (few: the bin is 1/2048 of the range) as
+//     (order-preserving key, position) pairs.
+//  4. A bitonic sort of the candidates by (key descending, position ascending)
+//     picks the `need` best; their bits join the bitmap.
+//  5. Walking the bitmap in order writes exactly k positions, ascending.
+// Radix path (longer rows, or more than kCandCap scores in T_bin, e.g. all
+// scores equal): three LDS-histogram passes over the order-preserving keys
+// (11 + 11 + 10 bits) pin the exact k-th key T; an ordered pass then keeps
+// key > T and the first `need` keys equal to T.  With G and E the counts of
+// greater and equal keys before a position, a kept key lands at slot
+// G + min(E, need), so one block-wide scan of packed (G, E) counts yields
+// ascending output with the lowest-position tie-break.
 #pragma once
 
 #include "device_common.hpp"
@@ -59,79 +70,88 @@ __device__ __forceinline__ uint32_t block_inclusive_scan(uint32_t v, uint32_t *w
     return v + before;
 }
 
-// Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
-// else n = n_base + r + 1 (prefill row at position n_base + r).
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
-    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens,
-    int n_base, int k, int32_t *__restrict__ out)
+constexpr int kBitmapKeys = 1 << 18;  // rows up to 262144 keys take the threshold path
+constexpr int kCandCap = 2048;          // candidates resolved in LDS
+constexpr int kBins = 2048;
+
+struct TopkShared {
+    uint32_t hist[kBins];
+    uint32_t wsum[kTopkWaves];
+    uint32_t pick[4];
+    float red[2][kTopkWaves];
+    uint32_t bitmap[kBitmapKeys / 32];
+    uint64_t cand[kCandCap];
+};
+
+// Finds the bin at which the count of keys in higher bins reaches `need`:
+// returns (bin, keys strictly above that bin).  Thread u owns bins
+// [nbins - per*(u+1), nbins - per*u) so a prefix scan over u is a suffix scan over bins.
+__device__ __forceinline__ void pick_bin(TopkShared &sh, int nbins, uint32_t need, uint32_t &bin, uint32_t &above,
+                                         uint32_t &count)
 {
-    __shared__ uint32_t hist[2048];
-    __shared__ uint32_t wsum[kTopkWaves];
-    __shared__ uint32_t pick[2];
-
-    const int r = blockIdx.x;
-    const int n = ctx_lens ? ctx_lens[r] : n_base + r + 1;
-    int32_t *o = out + (int64_t)r * k;
     const int tid = threadIdx.x;
-    if (n <= k) {
-        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
-        return;
+    const int per = nbins / kTopkThreads;
+    const int hi_bin = nbins - 1 - per * tid;
+    if (tid == 0) {
+        sh.pick[0] = 0;
+        sh.pick[1] = 0;
     }
-    const float *sr = scores + (int64_t)r * score_stride;
-    const int n4 = n & ~3;
+    uint32_t mine = 0;
+    for (int e = 0; e < per; ++e) mine += sh.hist[hi_bin - e];
+    uint32_t tot;
+    const uint32_t incl = block_inclusive_scan(mine, sh.wsum, &tot);
+    uint32_t ab = incl - mine;
+    for (int e = 0; e < per; ++e) {
+        const uint32_t c = sh.hist[hi_bin - e];
+        if (ab < need && ab + c >= need) {
+            sh.pick[0] = (uint32_t)(hi_bin - e);
+            sh.pick[1] = ab;
+            sh.pick[2] = c;
+        }
+        ab += c;
+    }
+    __syncthreads();
+    bin = sh.pick[0];
+    above = sh.pick[1];
+    count = sh.pick[2];
+    __syncthreads();  // pick[] and hist[] may be rewritten after this
+}
 
+// Radix path for one row: exact threshold key by three histogram passes, then
+// ordered compaction with the lowest-position tie-break.
+__device__ void topk_radix_row(TopkShared &sh, const float *__restrict__ sr, int n, int k, int32_t *__restrict__ o)
+{
+    const int tid = threadIdx.x;
+    const int n4 = n & ~3;
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)k;
 #pragma unroll 1
     for (int pass = 0; pass < 3; ++pass) {
         const int shift = pass == 0 ? 21 : (pass == 1 ? 10 : 0);
         const int nbins = pass == 2 ? 1024 : 2048;
-        for (int i = tid; i < nbins; i += kTopkThreads) hist[i] = 0;
-        if (tid == 0) {
-            pick[0] = 0;
-            pick[1] = 0;
-        }
+        for (int i = tid; i < nbins; i += kTopkThreads) sh.hist[i] = 0;
         __syncthreads();
         for (int i = 4 * tid; i < n4; i += 4 * kTopkThreads) {
             const f32x4 v = *reinterpret_cast<const f32x4 *>(sr + i);
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
                 const uint32_t key = score_key(v[e]);
-                if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1u);
+                if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nbins - 1)], 1u);
             }
         }
         for (int i = n4 + tid; i < n; i += kTopkThreads) {
             const uint32_t key = score_key(sr[i]);
-            if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & (nbins - 1)], 1u);
+            if ((key & pmask) == prefix) atomicAdd(&sh.hist[(key >> shift) & (nbins - 1)], 1u);
         }
         __syncthreads();
-        // thread u owns bins [nbins-2-2u, nbins-1-2u] (2048 bins) or bin nbins-1-u
-        // (1024 bins), so a prefix scan over u is a suffix scan over bins.
-        const int per = nbins / kTopkThreads;
-        const int hi_bin = nbins - 1 - per * tid;
-        uint32_t mine = 0;
-        for (int e = 0; e < per; ++e) mine += hist[hi_bin - e];
-        uint32_t tot;
-        const uint32_t incl = block_inclusive_scan(mine, wsum, &tot);
-        uint32_t above = incl - mine;  // keys in bins above this thread's bins
-        for (int e = 0; e < per; ++e) {
-            const uint32_t c = hist[hi_bin - e];
-            if (above < need && above + c >= need) {
-                pick[0] = (uint32_t)(hi_bin - e);
-                pick[1] = above;
-            }
-            above += c;
-        }
-        __syncthreads();
-        const uint32_t digit = pick[0];
-        need -= pick[1];
+        uint32_t digit, above, cnt;
+        pick_bin(sh, nbins, need, digit, above, cnt);
+        need -= above;
         prefix |= digit << shift;
         pmask |= (uint32_t)(nbins - 1) << shift;
-        __syncthreads();  // pick[] and hist[] are rewritten next pass
     }
     const uint32_t T = prefix;
 
-    // ordered compaction, 4 consecutive keys per thread per tile
     uint32_t base_g = 0, base_e = 0;
     for (int t0 = 0; t0 < n; t0 += 4 * kTopkThreads) {
         const int i0 = t0 + 4 * tid;
@@ -153,7 +173,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
         }
         const uint32_t packed = (cg << 16) | ce;
         uint32_t tot;
-        const uint32_t excl = block_inclusive_scan(packed, wsum, &tot) - packed;
+        const uint32_t excl = block_inclusive_scan(packed, sh.wsum, &tot) - packed;
         uint32_t G = base_g + (excl >> 16), E = base_e + (excl & 0xFFFFu);
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
@@ -171,6 +191,181 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
         }
         base_g += tot >> 16;
         base_e += tot & 0xFFFFu;
+    }
+}
+
+// Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
+// else n = n_base + r + 1 (prefill row at position n_base + r).  tile_mm holds
+// score ranges (min, max) at row stride mm_stride: one per 32-key tile
+// (mm_per_row == 0) or mm_per_row entries covering the whole row.
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
+    int mm_per_row, const int32_t *__restrict__ ctx_lens, int n_base, int k, int32_t *__restrict__ out)
+{
+    __shared__ TopkShared sh;
+    const int r = blockIdx.x;
+    const int n = ctx_lens ? ctx_lens[r] : n_base + r + 1;
+    int32_t *o = out + (int64_t)r * k;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const float *sr = scores + (int64_t)r * score_stride;
+    if (n > kBitmapKeys) {
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+    const int n4 = n & ~3;
+
+    // 1. score range of the row
+    float lo = INFINITY, hi = -INFINITY;
+    const f32x2 *mm = tile_mm + (int64_t)r * mm_stride;
+    const int nmm = mm_per_row ? mm_per_row : (n + 31) / 32;
+    for (int t = tid; t < nmm; t += kTopkThreads) {
+        const f32x2 v = mm[t];
+        lo = fminf(lo, v[0]);
+        hi = fmaxf(hi, v[1]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d));
+        hi = fmaxf(hi, __shfl_xor(hi, d));
+    }
+    if (lane == 0) {
+        sh.red[0][wv] = lo;
+        sh.red[1][wv] = hi;
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    lo = sh.red[0][0];
+    hi = sh.red[1][0];
+    for (int w = 1; w < kTopkWaves; ++w) {
+        lo = fminf(lo, sh.red[0][w]);
+        hi = fmaxf(hi, sh.red[1][w]);
+    }
+    const float span = hi - lo;
+    const float scale = (span > 0.0f && span < INFINITY) ? (float)kBins / span : 0.0f;
+    // monotone non-decreasing in the score (all steps are monotone in fp32)
+    auto bin_of = [&](float x) -> uint32_t {
+        const float f = fminf(fmaxf((x - lo) * scale, 0.0f), (float)(kBins - 1));
+        return (uint32_t)f;
+    };
+
+    // 2. histogram of the bins (four 16-byte loads in flight per thread)
+    constexpr int U = 4;
+    const int nU = n & ~(4 * U * kTopkThreads - 1);
+    for (int i = 4 * tid; i < nU; i += 4 * U * kTopkThreads) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const f32x4 *>(sr + i + u * 4 * kTopkThreads);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[bin_of(v[u][e])], 1u);
+    }
+    for (int i = nU + 4 * tid; i < n4; i += 4 * kTopkThreads) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(sr + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) atomicAdd(&sh.hist[bin_of(v[e])], 1u);
+    }
+    for (int i = n4 + tid; i < n; i += kTopkThreads) atomicAdd(&sh.hist[bin_of(sr[i])], 1u);
+    __syncthreads();
+    uint32_t tbin, above, m;
+    pick_bin(sh, kBins, (uint32_t)k, tbin, above, m);
+    const uint32_t need = (uint32_t)k - above;
+    if (m > (uint32_t)kCandCap) {  // block-uniform
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+
+    // 3. bitmap of the positions above T_bin; T_bin's candidates
+    const int words = (n + 31) / 32;
+    for (int i = tid; i < words; i += kTopkThreads) sh.bitmap[i] = 0;
+    if (tid == 0) sh.pick[3] = 0;
+    __syncthreads();
+    // called by all 64 lanes of a wave together (the ballot needs every lane)
+    auto visit = [&](float x, int i, bool valid) {
+        const uint32_t bi = bin_of(x);
+        if (valid && bi > tbin) atomicOr(&sh.bitmap[i >> 5], 1u << (i & 31));
+        const bool c = valid && bi == tbin;
+        const uint64_t mask = __ballot(c);
+        if (mask) {
+            uint32_t base = 0;
+            if (lane == 0) base = atomicAdd(&sh.pick[3], (uint32_t)__popcll(mask));
+            base = __shfl(base, 0);
+            if (c) {
+                const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                                __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+                const uint32_t slot = base + rank;
+                if (slot < (uint32_t)kCandCap)
+                    sh.cand[slot] = ((uint64_t)score_key(x) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+            }
+        }
+    };
+    // wave-uniform loop: a wave covers U x 256 keys per iteration (U loads in flight)
+    for (int wb = 4 * 64 * wv; wb < n; wb += 4 * U * kTopkThreads) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i0 = wb + u * 4 * kTopkThreads + 4 * lane;
+            v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            if (i0 + 3 < n) {
+                v[u] = *reinterpret_cast<const f32x4 *>(sr + i0);
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (i0 + e < n) v[u][e] = sr[i0 + e];
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int i0 = wb + u * 4 * kTopkThreads + 4 * lane;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) visit(v[u][e], i0 + e, i0 + e < n);
+        }
+    }
+    __syncthreads();
+
+    // 4. the need best candidates: bitonic sort, descending by (key, -position)
+    int P = 1;
+    while (P < (int)m) P <<= 1;
+    for (int i = (int)m + tid; i < P; i += kTopkThreads) sh.cand[i] = 0;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1)
+        for (int j = size >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P / 2; i += kTopkThreads) {
+                const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b = a | j;
+                const uint64_t x = sh.cand[a], y = sh.cand[b];
+                const bool desc = (a & size) == 0;  // the final pass (size == P) sorts descending
+                if (desc ? (x < y) : (x > y)) {
+                    sh.cand[a] = y;
+                    sh.cand[b] = x;
+                }
+            }
+            __syncthreads();
+        }
+    for (int i = tid; i < (int)need; i += kTopkThreads) {
+        const int pos = (int)(0xFFFFFFFFu - (uint32_t)sh.cand[i]);
+        atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
+    }
+    __syncthreads();
+
+    // 5. positions in ascending order: contiguous words per thread, scan of bit counts
+    const int per = (words + kTopkThreads - 1) / kTopkThreads;
+    const int w0 = tid * per, w1 = min(words, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sh.bitmap[w]);
+    uint32_t tot;
+    uint32_t pos = block_inclusive_scan(cnt, sh.wsum, &tot) - cnt;
+    for (int w = w0; w < w1; ++w) {
+        uint32_t bits = sh.bitmap[w];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (pos < (uint32_t)k) o[pos] = w * 32 + b;
+            ++pos;
+        }
     }
 }
 
