@@ -99,8 +99,9 @@ struct AttnShape {
 // inverse and never leaves p's aligned group of 8.
 __device__ __forceinline__ int tile_slot(int t, int p) { return p ^ ((t >> 1) & 7); }
 
-template <int QK, int V>
-__global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
+// NW waves per workgroup, wave w owning heads 32w..32w+31 (NW = ceil(H / 32)).
+template <int QK, int V, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
 {
     using S = AttnShape<QK, V>;
     constexpr int KS = S::KS, VP = S::VP, VW = S::VW, PIECES = S::PIECES;
@@ -110,7 +111,7 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
     __shared__ int last_tile, overflow_flag;
 
     const int split = blockIdx.x / S::VSPLIT, vh = blockIdx.x % S::VSPLIT, r = blockIdx.y;
-    const int nthreads = blockDim.x, nw = nthreads >> 6;
+    constexpr int nthreads = 64 * NW, nw = NW;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int seq = a.decode ? r : 0;
@@ -157,6 +158,8 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks)
             qb[ks] = hok ? as_bf16x8(load16(qp + 16 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
+#pragma unroll
+        for (int ks = KS; ks < KS; ++ks) asm volatile("" : "+a"(qb[ks]));
     }
     f32x16 oe[VP], oo[VP];
 #pragma unroll
@@ -174,13 +177,30 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
     __syncthreads();
     const int nt_eff = last_tile + 1;  // tiles after the last valid token are skipped
 
+    // A tile's copies.  Lane i first takes the row of token i % 32 (one LDS read
+    // per tile); a copy instruction's lanes then pick their token's row from it:
+    // with rows of >= 64 pieces an instruction spans at most two tokens, whose
+    // rows come from v_readlane (no memory access); shorter rows use a lane
+    // shuffle.  (LDS reads of rows[] could not overlap each other: none may pass
+    // a copy into LDS.)
+    constexpr int DMA_W = (S::DMA_PER_TILE + NW - 1) / NW;  // copies per wave per tile (at most)
     auto issue_tile = [&](int t, int buf) {
-        for (int ii = wave; ii < 32 * PIECES / 64; ii += nw) {
+        const int myrow = (int)rows[t * 32 + (lane & 31)];
+#pragma unroll 1
+        for (int ii = wave; ii < S::DMA_PER_TILE; ii += NW) {
             const int L = ii * 64 + lane;
             const int tj = L / PIECES, p = tile_slot(tj, L % PIECES);
-            const uint32_t row = rows[t * 32 + tj];
-            if (row != kNoRow)
-                dma16_to_lds(a.kv + (int64_t)row * QK + p * 8, (SA_LDS void *)&tile[buf][ii * 1024]);
+            int row;
+            if constexpr (PIECES >= 64) {
+                const int t0 = (ii * 64) / PIECES;  // wave-uniform
+                const int ra = __builtin_amdgcn_readlane(myrow, t0);
+                const int rb = __builtin_amdgcn_readlane(myrow, t0 + 1 < 32 ? t0 + 1 : 31);
+                row = tj == t0 ? ra : rb;
+            } else {
+                row = __shfl(myrow, tj);
+            }
+            if ((uint32_t)row != kNoRow)
+                dma16_to_lds(a.kv + (int64_t)(uint32_t)row * QK + p * 8, (SA_LDS void *)&tile[buf][ii * 1024]);
         }
     };
 
@@ -213,10 +233,19 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
         // two accumulators (even / odd steps) halve the dependent MFMA chain
         f32x16 s0 = f32x16{}, s1 = f32x16{};
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const bf16x8 ka = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff[ks & 3] + 128 * (ks >> 2)));
-            if (ks & 1) s1 = mfma_32x32x16(ka, qb[ks], s1);
-            else s0 = mfma_32x32x16(ka, qb[ks], s0);
+        for (int g = 0; g < KS; g += 4) {
+            bf16x8 ka[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (g + u < KS)
+                    ka[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff[(g + u) & 3] + 128 * ((g + u) >> 2)));
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int ks = g + u;
+                if (ks >= KS) break;
+                if (ks & 1) s1 = mfma_32x32x16(ka[u], qb[ks], s1);
+                else s0 = mfma_32x32x16(ka[u], qb[ks], s0);
+            }
         }
         f32x16 s = s0 + s1;
         const uint32_t vb = vbits[t] >> (4 * hf);  // bit acc_row(i, hf) - 4hf = 8(i/4) + i%4
@@ -280,15 +309,14 @@ __global__ __launch_bounds__(256, 1) void attend_kernel(const AttnArgs a)
     // done reading tile t-1's buffer), refill that buffer with tile
     // t+kAttnBuffers-1, then compute tile t.  Tiles of padding only are neither
     // copied nor computed (block-uniform).  Each wave issues the same number of
-    // copies per tile only when nw divides DMA_PER_TILE; otherwise the wait count
+    // copies per tile only when NW divides DMA_PER_TILE; otherwise the wait count
     // below is still an upper bound of the younger copies, so it only over-waits.
-    constexpr int DMA_W = (S::DMA_PER_TILE + 3) / 4;  // copies per wave per tile, 4 waves
 #pragma unroll
     for (int j = 0; j < kAttnBuffers - 1; ++j)
         if (j < nt_eff) issue_tile(j, j);
     for (int t = 0; t < nt_eff; ++t) {
-        if (nw == 4) attn_wait_vmcnt<DMA_W * (kAttnBuffers - 2)>();
-        else attn_wait_vmcnt<0>();
+        // (clamped to the counter's range: waiting for more copies is always safe)
+        attn_wait_vmcnt<(DMA_W * (kAttnBuffers - 2) < 63 ? DMA_W * (kAttnBuffers - 2) : 63)>();
         barrier_no_fence();
         const int tn = t + kAttnBuffers - 1;
         if (tn < nt_eff) issue_tile(tn, tn % kAttnBuffers);
