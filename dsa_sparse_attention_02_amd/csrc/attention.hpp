@@ -88,31 +88,73 @@ struct AttnShape {
     static constexpr int VW = V / VSPLIT;                // v columns per workgroup
     static constexpr int VP = VW / 64;                   // 64-wide v groups (even + odd tiles)
     static constexpr int PIECES = QK / 8;                // 16-byte pieces per latent row
-    static constexpr int TILE_BYTES = 32 * PIECES * 16;
-    static constexpr int DMA_PER_TILE = 32 * PIECES / 64;   // wave instructions per tile
-    static_assert(QK % 16 == 0 && PIECES % 8 == 0 && VW % 64 == 0 && V <= QK, "shape family");
+    // LDS image of a 32-token tile.  Main rows: pieces 0..63 of each token
+    // (one 1 KiB copy per token), MAIN_STRIDE bytes apart; the extra 16 bytes
+    // move each token to the next 16-byte bank group.  Tail: the remaining
+    // pieces, stored piece-major ([piece][32 tokens]), so one copy moves two
+    // pieces of all 32 tokens.  Rows shorter than 64 pieces live in the tail only.
+    static constexpr int MAIN = PIECES >= 64 ? 64 : 0;
+    static constexpr int TAIL = PIECES - MAIN;
+    static constexpr int MAIN_STRIDE = MAIN * 16 + 16;
+    static constexpr int TAIL_BASE = MAIN ? 32 * MAIN_STRIDE : 0;
+    static constexpr int TILE_BYTES = TAIL_BASE + TAIL * 32 * 16;
+    static constexpr int DMA_MAIN = MAIN ? 32 : 0;       // main-row copies per tile
+    static constexpr int DMA_TAIL = TAIL / 2;            // tail copies per tile
+    static constexpr int DMA_PER_TILE = DMA_MAIN + DMA_TAIL;
+    static_assert(QK % 16 == 0 && VW % 64 == 0 && V <= QK, "shape family");
+    static_assert(TAIL % 2 == 0 && (MAIN == 0 || V <= 8 * MAIN), "value columns must lie in the main rows");
 };
 
-// LDS slot of 16-byte piece p of tile token t.  Rows are PIECES long (a
-// multiple of 8); XOR-ing the low 3 bits with (t>>1)&7 puts the same piece of 16
-// consecutive tokens on 16 distinct 16-byte bank groups.  The map is its own
-// inverse and never leaves p's aligned group of 8.
-__device__ __forceinline__ int tile_slot(int t, int p) { return p ^ ((t >> 1) & 7); }
+// Row rho of a tile's S^T accumulator holds tile token row_token(rho) (bits 2
+// and 3 swapped).  Then the two half-waves of a V^T operand read tokens 8
+// apart, whose main rows sit 32 banks apart, while the K operand of 16
+// consecutive rows still covers 16 distinct 16-byte bank groups.
+__device__ __forceinline__ constexpr int row_token(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
+
+// Source of the copies of padding tokens: zeros, so that V of a slot that is
+// weighted by P = 0 is finite.
+__device__ __attribute__((aligned(16))) const uint8_t kZeroLatentRow[2048] = {};
+
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int l) { return __builtin_amdgcn_readlane(v, l); }
+__device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+// l + the two bf16 values packed in w (each times 1.0)
+__device__ __forceinline__ float add_bf16_pair(uint32_t w, float l)
+{
+    typedef __bf16 b2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), __builtin_bit_cast(b2, 0x3F803F80u), l, false);
+}
+
+// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedValu = 0x002;
+
+// Workgroup id -> logical block.  Workgroups are dealt to the 8 XCDs in turn
+// (id mod 8); this map gives each XCD a contiguous range of logical blocks, so
+// the blocks of one query row (its splits and value halves), which read the
+// same query and the same latent rows, share one L2.
+__device__ __forceinline__ int xcd_block(int id, int n)
+{
+    const int q = n >> 3, rem = n & 7, x = id & 7;
+    return x * q + min(x, rem) + (id >> 3);
+}
 
 // NW waves per workgroup, wave w owning heads 32w..32w+31 (NW = ceil(H / 32)).
+// One-dimensional grid of rows * splits * VSPLIT workgroups.
 template <int QK, int V, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
 {
     using S = AttnShape<QK, V>;
-    constexpr int KS = S::KS, VP = S::VP, VW = S::VW, PIECES = S::PIECES;
+    constexpr int KS = S::KS, VP = S::VP, VW = S::VW;
     __shared__ __attribute__((aligned(1024))) uint8_t tile[kAttnBuffers][S::TILE_BYTES];
     __shared__ uint32_t rows[kAttnMaxSplitTokens];
     __shared__ uint32_t vbits[kAttnMaxSplitTokens / 32];
     __shared__ int last_tile, overflow_flag;
 
-    const int split = blockIdx.x / S::VSPLIT, vh = blockIdx.x % S::VSPLIT, r = blockIdx.y;
-    constexpr int nthreads = 64 * NW, nw = NW;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int per_row = a.splits * S::VSPLIT;
+    const int lb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = lb / per_row, split = (lb % per_row) / S::VSPLIT, vh = lb % S::VSPLIT;
+    constexpr int nthreads = 64 * NW;
+    const int wave = wave_uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int seq = a.decode ? r : 0;
     const int limit = a.decode ? a.ctx_lens[r] : a.limit_base + r + 1;
@@ -123,43 +165,50 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     const int32_t *tbl = a.block_table + (int64_t)seq * a.max_blocks;
     const int bmask = (1 << a.bs_log2) - 1;
 
-    // physical row of every kept token of this split (kNoRow = padding), and a
-    // validity bit mask per 32-token tile
-    for (int jb = wave * 64; jb < ntiles * 32; jb += nthreads) {
-        const int j = jb + lane;
-        uint32_t row = kNoRow;
-        if (j < cnt) {
-            const int idx = sel[j];
-            if (idx >= 0 && idx < limit) {
-                const int blk = tbl[idx >> a.bs_log2];
-                if (blk >= 0 && blk < a.num_blocks) row = ((uint32_t)blk << a.bs_log2) | (uint32_t)(idx & bmask);
-            }
+    const int head = 32 * wave + col;
+    const bool hok = head < a.num_heads;
+    // q^T operand of step ks for this lane: q[head][16ks + 8half .. +7]
+    // (issued first: these loads overlap the row look-ups below).  Lanes of
+    // heads past num_heads load the last head instead: their S^T columns feed
+    // only their own, never stored, output columns.
+    bf16x8 qb[KS];
+    {
+        const int qhead = hok ? head : a.num_heads - 1;
+        const uint16_t *qp = a.q + ((int64_t)r * a.num_heads + qhead) * QK + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(load16(qp + 16 * ks));
+    }
+
+    // Physical row of every kept token of this split (kNoRow = padding) and a
+    // validity mask per 32-token tile.  Positions, then block-table entries, are
+    // loaded 8 per thread at a time, so the look-ups cost two memory round trips.
+    for (int jb = 0; jb < ntiles * 32; jb += 8 * nthreads) {
+        int idx[8], blk[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + u * nthreads + threadIdx.x;
+            idx[u] = j < cnt ? sel[j] : -1;
         }
-        const uint64_t m = __ballot(row != kNoRow);
-        if (j < ntiles * 32) rows[j] = row;
-        if (lane == 0) vbits[jb >> 5] = (uint32_t)m;
-        if (lane == 32 && jb + 32 < ntiles * 32) vbits[(jb >> 5) + 1] = (uint32_t)(m >> 32);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool ok = idx[u] >= 0 && idx[u] < limit;
+            blk[u] = ok ? tbl[idx[u] >> a.bs_log2] : -1;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = jb + u * nthreads + threadIdx.x;
+            const bool ok = blk[u] >= 0 && blk[u] < a.num_blocks;
+            const uint32_t row = ok ? ((uint32_t)blk[u] << a.bs_log2) | (uint32_t)(idx[u] & bmask) : kNoRow;
+            const uint64_t m = __ballot(row != kNoRow);
+            if (j < ntiles * 32) rows[j] = row;
+            const int w0 = (j - lane) >> 5;  // this wave's 64 tokens are tiles w0, w0 + 1
+            if (lane == 0 && w0 < ntiles) vbits[w0] = (uint32_t)m;
+            if (lane == 32 && w0 + 1 < ntiles) vbits[w0 + 1] = (uint32_t)(m >> 32);
+        }
     }
     if (threadIdx.x == 0) {
         last_tile = -1;
         overflow_flag = 0;
-    }
-    // zero the tile buffers: slots of padding tokens are never copied into, and
-    // they are multiplied by P = 0, so they must hold finite values
-    for (int e = threadIdx.x; e < kAttnBuffers * S::TILE_BYTES / 16; e += nthreads)
-        reinterpret_cast<u32x4 *>(&tile[0][0])[e] = u32x4{0, 0, 0, 0};
-
-    const int head = 32 * wave + col;
-    const bool hok = head < a.num_heads;
-    // q^T operand of step ks for this lane: q[head][16ks + 8half .. +7]
-    bf16x8 qb[KS];
-    {
-        const uint16_t *qp = a.q + ((int64_t)r * a.num_heads + head) * QK + 8 * half;
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks)
-            qb[ks] = hok ? as_bf16x8(load16(qp + 16 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
-#pragma unroll
-        for (int ks = KS; ks < KS; ++ks) asm volatile("" : "+a"(qb[ks]));
     }
     f32x16 oe[VP], oo[VP];
 #pragma unroll
@@ -177,34 +226,58 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     __syncthreads();
     const int nt_eff = last_tile + 1;  // tiles after the last valid token are skipped
 
-    // A tile's copies.  Lane i first takes the row of token i % 32 (one LDS read
-    // per tile); a copy instruction's lanes then pick their token's row from it:
-    // with rows of >= 64 pieces an instruction spans at most two tokens, whose
-    // rows come from v_readlane (no memory access); shorter rows use a lane
-    // shuffle.  (LDS reads of rows[] could not overlap each other: none may pass
-    // a copy into LDS.)
-    constexpr int DMA_W = (S::DMA_PER_TILE + NW - 1) / NW;  // copies per wave per tile (at most)
-    auto issue_tile = [&](int t, int buf) {
-        const int myrow = (int)rows[t * 32 + (lane & 31)];
-#pragma unroll 1
-        for (int ii = wave; ii < S::DMA_PER_TILE; ii += NW) {
-            const int L = ii * 64 + lane;
-            const int tj = L / PIECES, p = tile_slot(tj, L % PIECES);
-            int row;
-            if constexpr (PIECES >= 64) {
-                const int t0 = (ii * 64) / PIECES;  // wave-uniform
-                const int ra = __builtin_amdgcn_readlane(myrow, t0);
-                const int rb = __builtin_amdgcn_readlane(myrow, t0 + 1 < 32 ? t0 + 1 : 31);
-                row = tj == t0 ? ra : rb;
-            } else {
-                row = __shfl(myrow, tj);
-            }
-            if ((uint32_t)row != kNoRow)
-                dma16_to_lds(a.kv + (int64_t)(uint32_t)row * QK + p * 8, (SA_LDS void *)&tile[buf][ii * 1024]);
-        }
+    // Copies.  A tile is DMA_PER_TILE wave-wide 16-byte-per-lane copies: copy
+    // i < DMA_MAIN moves token i's main row (lane l: piece l, the row from
+    // v_readlane), tail copy j moves pieces MAIN + 2j and MAIN + 2j + 1 of all 32
+    // tokens (lane l: token l % 32, its own row).  Padding tokens, and tiles at
+    // or past nt_eff, copy zeros.  Wave w issues copies w, w + NW, ... and
+    // exactly DMA_W of them per tile (a surplus repeats the last copy, which
+    // writes the same bytes again), so the copy counter of every wave advances
+    // by DMA_W per tile.  `myrow` is the row of token lane % 32 of the tile.
+    constexpr int DMA_W = (S::DMA_PER_TILE + NW - 1) / NW;
+    const uint64_t kv_addr = reinterpret_cast<uint64_t>(a.kv);
+    uint64_t zero_addr = reinterpret_cast<uint64_t>(kZeroLatentRow);
+    asm volatile("" : "+s"(zero_addr));  // keep the address in registers, out of the copy code
+    auto tile_row = [&](int tn) -> uint32_t {
+        const uint32_t v = rows[max(0, min(tn, kAttnMaxSplitTokens / 32 - 1)) * 32 + (lane & 31)];
+        return tn >= 0 && tn < nt_eff ? v : kNoRow;
+    };
+    auto copy = [&](uint32_t myrow, int n, int buf) {
+        const int ii = min(wave + NW * n, S::DMA_PER_TILE - 1);  // wave-uniform
+        const bool is_main = ii < S::DMA_MAIN;
+        const int j = ii - S::DMA_MAIN;
+        const uint32_t row = is_main ? lane_read(myrow, min(ii, 31)) : myrow;
+        const uint64_t base = row != kNoRow ? kv_addr + (uint64_t)row * (QK * 2) : zero_addr;
+        const uint32_t off = is_main ? lane * 16 : (S::MAIN + 2 * j + (lane >> 5)) * 16;
+        const int dst = buf * S::TILE_BYTES + (is_main ? ii * S::MAIN_STRIDE : S::TAIL_BASE + j * 1024);
+        // The LDS address goes through an opaque register: the copy then carries
+        // no alias scope of `tile`, and the compiler adds no wait for it before
+        // later tile reads (which read other buffers; the ring waits above order
+        // the rest).
+        uint32_t la = (uint32_t)(uintptr_t)((SA_LDS uint8_t *)&tile[0][0] + dst);
+        asm volatile("" : "+s"(la));
+        dma16_to_lds(reinterpret_cast<const void *>(base + off), (SA_LDS void *)(uintptr_t)la);
+    };
+    auto issue_tile = [&](int tn, int buf) {
+        const uint32_t myrow = tile_row(tn);
+#pragma unroll 9
+        for (int n = 0; n < DMA_W; ++n) copy(myrow, n, buf);
     };
 
-    auto compute = [&](int t, int buf) {
+    // LDS byte offset of this lane's K operand of step ks (S row c holds token
+    // row_token(c); the lane supplies its pieces 2ks + half).
+    auto k_offset = [&](int c, int hf, int ks) {
+        const int tok = row_token(c);
+        return 2 * ks < S::MAIN ? tok * S::MAIN_STRIDE + 16 * hf + 32 * ks
+                                : S::TAIL_BASE + (2 * ks - S::MAIN + hf) * 512 + 16 * tok;
+    };
+
+    // One tile: S^T = K Q^T, softmax weights, O^T += V^T P^T, with the copies
+    // of tile tn into buffer nbuf issued between the q.k steps.  The schedule is
+    // pinned so that LDS operand reads run ahead of the MFMAs that use them:
+    // K operands KPF steps ahead, the first V operands during the softmax.
+    constexpr int KPF = 3;
+    auto compute = [&](int t, int buf, int tn, int nbuf) {
         // The lane id is made opaque per tile so that the lane-dependent values
         // below are recomputed (a few ALU ops) instead of being hoisted out of
         // the tile loop, where they would compete with the accumulators for
@@ -212,51 +285,64 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         int ln = lane;
         asm volatile("" : "+v"(ln));
         const int c = ln & 31, hf = ln >> 5;
-        // Per-lane LDS byte offsets of the operand reads.  With the swizzle only the
-        // low 3 bits of a piece index move, so every read is one of these bases
-        // plus a compile-time offset:
-        //   K operand of step ks (token c, piece 2ks+hf):   koff[ks&3] + 128*(ks>>2)
-        //   V dword of token 16k2+tj0(j), pair VW/2*vh + 32vp + c:
-        //                                 voff[j] + 256*PIECES*k2 + 128*vp  (vh folded into voff)
-        int koff[4], voff[8];
-        {
-            const int xk = (c >> 1) & 7;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) koff[j] = (c * PIECES + ((2 * j + hf) ^ xk)) * 16;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const int tj0 = 8 * (j >> 2) + 4 * hf + (j & 3);
-                voff[j] = (tj0 * PIECES + ((c >> 2) ^ ((tj0 >> 1) & 7))) * 16 + (c & 3) * 4 + vh * VW * 2;
-            }
-        }
         const uint8_t *tb = tile[buf];
-        // two accumulators (even / odd steps) halve the dependent MFMA chain
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
+        const uint32_t myrow = tile_row(tn);
+        const uint32_t vw = vbits[t];
+        bf16x8 kr[KS];
 #pragma unroll
-        for (int g = 0; g < KS; g += 4) {
-            bf16x8 ka[4];
+        for (int u = 0; u < KPF && u < KS; ++u)
+            kr[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, u)));
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 + (KPF < KS ? KPF : KS), 0);
+        f32x16 s = f32x16{};
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (g + u < KS)
-                    ka[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff[(g + u) & 3] + 128 * ((g + u) >> 2)));
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int ks = g + u;
-                if (ks >= KS) break;
-                if (ks & 1) s1 = mfma_32x32x16(ka[u], qb[ks], s1);
-                else s0 = mfma_32x32x16(ka[u], qb[ks], s0);
+        for (int ks = 0; ks < KS; ++ks) {
+            if (ks + KPF < KS) {
+                kr[ks + KPF] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, ks + KPF)));
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
-        }
-        f32x16 s = s0 + s1;
-        const uint32_t vb = vbits[t] >> (4 * hf);  // bit acc_row(i, hf) - 4hf = 8(i/4) + i%4
-        float tmax = -INFINITY;
+            // copies n with n * KS / DMA_W == ks
+            const int n_lo = (ks * DMA_W + KS - 1) / KS, n_hi = ((ks + 1) * DMA_W + KS - 1) / KS;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const bool ok = (vb >> (8 * (i >> 2) + (i & 3))) & 1u;
-            s[i] = ok ? s[i] * a.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, s[i]);
+            for (int n = n_lo; n < n_hi; ++n) {
+                copy(myrow, n, nbuf);
+                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+            }
+            s = mfma_32x32x16(kr[ks], qb[ks], s);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        // V^T operand element e of this lane for step q = (k2, vp): v pair
+        // vh*VW/2 + 32vp + c of token 16k2 + 8hf + e.
+        int vbase;
+        if constexpr (S::MAIN > 0)
+            vbase = 8 * hf * S::MAIN_STRIDE + 2 * vh * VW + 4 * c;
+        else
+            vbase = S::TAIL_BASE + (c >> 2) * 512 + (c & 3) * 4 + 128 * hf + vh * VW * 64;
+        auto vread = [&](int q, uint32_t *d) {
+            const int k2 = q / VP, vp = q % VP;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int off = S::MAIN > 0 ? (16 * k2 + e) * S::MAIN_STRIDE + 128 * vp
+                                            : (16 * k2 + e) * 16 + 4096 * vp;
+                d[e] = *reinterpret_cast<const uint32_t *>(tb + vbase + off);
+            }
+        };
+        constexpr int VPF = 2;  // V operand steps read ahead
+        uint32_t vd[2 * VP][8];
+#pragma unroll
+        for (int q = 0; q < VPF && q < 2 * VP; ++q) vread(q, vd[q]);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (VPF < 2 * VP ? VPF : 2 * VP), 0);
+
+        // register i of half hf holds token 16(i/8) + 8hf + i%8
+        if (vw != 0xFFFFFFFFu) {  // a tile with padding (block-uniform)
+            const uint32_t vb = vw >> (8 * hf);
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+                if (!((vb >> (16 * (i >> 3) + (i & 7))) & 1u)) s[i] = -INFINITY;
+        }
+        float tmax = s[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;
         // The reference max is fixed by the first tile with a valid token for this
         // head (until then O and l are 0, so nothing needs rescaling) and never
         // moves afterwards: the output accumulators are only ever touched by the
@@ -265,63 +351,63 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         // split is then recomputed exactly with its true max (below).
         if (m == -INFINITY) m = tmax;
         ovf |= tmax > m + 64.0f;
+        const float mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every s is -inf
         bf16x8 pb[2];
 #pragma unroll
         for (int k2 = 0; k2 < 2; ++k2) {
             u32x4 w;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float x0 = s[8 * k2 + 2 * jj], x1 = s[8 * k2 + 2 * jj + 1];
-                const float p0 = x0 == -INFINITY ? 0.0f : exp2f(fminf(x0 - m, 64.0f));
-                const float p1 = x1 == -INFINITY ? 0.0f : exp2f(fminf(x1 - m, 64.0f));
+                const float p0 = exp2_hw(fminf(fmaf(s[8 * k2 + 2 * jj], a.scale_log2, -mref), 64.0f));
+                const float p1 = exp2_hw(fminf(fmaf(s[8 * k2 + 2 * jj + 1], a.scale_log2, -mref), 64.0f));
                 w[jj] = pack_bf16x2(p0, p1);
                 // the normaliser sums the same bf16-rounded weights the MFMA
                 // multiplies V by, so the output is an exact weighted mean of
                 // the kept rows up to fp32 accumulation
-                l += __uint_as_float(w[jj] << 16) + __uint_as_float(w[jj] & 0xFFFF0000u);
+                l = add_bf16_pair(w[jj], l);
                 le += p0 + p1;
             }
             pb[k2] = as_bf16x8(w);
         }
+        // O^T += V^T P^T, step q = (k2, vp); the operands of step q + VPF are
+        // read while step q multiplies
 #pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-#pragma unroll
-            for (int vp = 0; vp < VP; ++vp) {
-                uint32_t d[8];
-#pragma unroll
-                for (int j = 0; j < 8; ++j)
-                    d[j] = *reinterpret_cast<const uint32_t *>(tb + voff[j] + 256 * PIECES * k2 + 128 * vp);
-                u32x4 ev, od;
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    ev[jj] = __builtin_amdgcn_perm(d[2 * jj + 1], d[2 * jj], 0x05040100u);
-                    od[jj] = __builtin_amdgcn_perm(d[2 * jj + 1], d[2 * jj], 0x07060302u);
-                }
-                oe[vp] = mfma_32x32x16(as_bf16x8(ev), pb[k2], oe[vp]);
-                oo[vp] = mfma_32x32x16(as_bf16x8(od), pb[k2], oo[vp]);
+        for (int q = 0; q < 2 * VP; ++q) {
+            if (q + VPF < 2 * VP) {
+                vread(q + VPF, vd[q + VPF]);
+                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
             }
+            const int k2 = q / VP, vp = q % VP;
+            u32x4 ev, od;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                ev[jj] = __builtin_amdgcn_perm(vd[q][2 * jj + 1], vd[q][2 * jj], 0x05040100u);
+                od[jj] = __builtin_amdgcn_perm(vd[q][2 * jj + 1], vd[q][2 * jj], 0x07060302u);
+            }
+            oe[vp] = mfma_32x32x16(as_bf16x8(ev), pb[k2], oe[vp]);
+            oo[vp] = mfma_32x32x16(as_bf16x8(od), pb[k2], oo[vp]);
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
         }
     };
 
-    // Ring of kAttnBuffers tiles.  Iteration t: wait until this wave's copies of
-    // tile t have landed (at most the kAttnBuffers-2 younger tiles' copies still in
-    // flight), barrier (every wave's share of tile t is in LDS, and every wave is
-    // done reading tile t-1's buffer), refill that buffer with tile
-    // t+kAttnBuffers-1, then compute tile t.  Tiles of padding only are neither
-    // copied nor computed (block-uniform).  Each wave issues the same number of
-    // copies per tile only when NW divides DMA_PER_TILE; otherwise the wait count
-    // below is still an upper bound of the younger copies, so it only over-waits.
+    // Ring of kAttnBuffers tiles.  The prologue issues tiles 0..2; computing
+    // tile t issues tile t+3 into the buffer of tile t-1 (zeros past nt_eff), so
+    // exactly two younger tiles' copies are in flight when tile t is waited
+    // for.  Copies complete in order: "tile t landed" is "at most 2 DMA_W copies
+    // in flight".  The barrier then also certifies that every wave is done with
+    // tile t-1's buffer before it is refilled.  Tiles of padding only are not
+    // computed (block-uniform).
+    static_assert(kAttnBuffers == 4, "wait count below assumes two younger tiles");
+    constexpr int W2 = 2 * DMA_W < 63 ? 2 * DMA_W : 63;  // clamped: waiting for more is safe
 #pragma unroll
-    for (int j = 0; j < kAttnBuffers - 1; ++j)
-        if (j < nt_eff) issue_tile(j, j);
+    for (int j = 0; j < kAttnBuffers - 1; ++j) issue_tile(j, j);
     for (int t = 0; t < nt_eff; ++t) {
-        // (clamped to the counter's range: waiting for more copies is always safe)
-        attn_wait_vmcnt<(DMA_W * (kAttnBuffers - 2) < 63 ? DMA_W * (kAttnBuffers - 2) : 63)>();
+        attn_wait_vmcnt<W2>();
         barrier_no_fence();
         const int tn = t + kAttnBuffers - 1;
-        if (tn < nt_eff) issue_tile(tn, tn % kAttnBuffers);
-        compute(t, t % kAttnBuffers);
+        compute(t, t % kAttnBuffers, tn, tn % kAttnBuffers);
     }
+    attn_wait_vmcnt<0>();  // the last (zero) copies have landed
 
     // Exact recompute of the split when some head's logits outgrew its reference
     // max by more than 64 (never for logits within a few dozen of each other):
@@ -332,20 +418,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         float mt = -INFINITY;
         for (int t = 0; t < nt_eff; ++t) {
             issue_tile(t, 0);
+            attn_wait_vmcnt<0>();
             __syncthreads();
             const uint8_t *tb = tile[0];
             f32x16 s0 = f32x16{};
-            const int xk = (col >> 1) & 7;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int slot = 8 * (ks >> 2) + ((2 * (ks & 3) + half) ^ xk);
-                s0 = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + (col * PIECES + slot) * 16)),
+            for (int ks = 0; ks < KS; ++ks)
+                s0 = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(col, half, ks))),
                                    qb[ks], s0);
-            }
-            const uint32_t vb = vbits[t] >> (4 * half);
+            const uint32_t vb = vbits[t] >> (8 * half);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-                if ((vb >> (8 * (i >> 2) + (i & 3))) & 1u) mt = fmaxf(mt, s0[i] * a.scale_log2);
+                if ((vb >> (16 * (i >> 3) + (i & 7))) & 1u) mt = fmaxf(mt, s0[i] * a.scale_log2);
             __syncthreads();
         }
         mt = fmaxf(mt, __shfl_xor(mt, 32));
@@ -359,8 +443,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         }
         for (int t = 0; t < nt_eff; ++t) {
             issue_tile(t, 0);
+            attn_wait_vmcnt<0>();
             __syncthreads();
-            compute(t, 0);  // s <= m now, so no weight is clamped
+            compute(t, 0, -1, 1);  // s <= m now, so no weight is clamped; no copies ahead (zeros into buffer 1)
+            attn_wait_vmcnt<0>();
             __syncthreads();
         }
     }

@@ -260,21 +260,23 @@ void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *id
 
 void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st, StageMarks *mk)
 {
-    const int nw = (p->num_heads + 31) / 32;
-    dim3 grid(a.splits * (p->v_dim > 256 ? 2 : 1), rows), block(64 * nw);
-#define SA_ATTEND(QK_, V_)                                                                             \
-    switch (nw) {                                                                                      \
-    case 1: hipLaunchKernelGGL((attend_kernel<QK_, V_, 1>), grid, block, 0, st, a); break;            \
-    case 2: hipLaunchKernelGGL((attend_kernel<QK_, V_, 2>), grid, block, 0, st, a); break;            \
-    case 3: hipLaunchKernelGGL((attend_kernel<QK_, V_, 3>), grid, block, 0, st, a); break;            \
-    default: hipLaunchKernelGGL((attend_kernel<QK_, V_, 4>), grid, block, 0, st, a); break;           \
-    }
+    // waves of 32 heads; the 576-wide family runs 2 or 4 waves (a 1- or 3-wave
+    // build would need more registers than the pipelined tile loop can spare),
+    // waves past num_heads mask their heads
+    int nw = (p->num_heads + 31) / 32;
+    if (p->qk_dim == 576) nw = nw <= 2 ? 2 : 4;
+    dim3 grid(a.splits * (p->v_dim > 256 ? 2 : 1) * rows), block(64 * nw);
     if (p->qk_dim == 576) {
-        SA_ATTEND(576, 512)
+        if (nw == 2) hipLaunchKernelGGL((attend_kernel<576, 512, 2>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attend_kernel<576, 512, 4>), grid, block, 0, st, a);
     } else {
-        SA_ATTEND(64, 64)
+        switch (nw) {
+        case 1: hipLaunchKernelGGL((attend_kernel<64, 64, 1>), grid, block, 0, st, a); break;
+        case 2: hipLaunchKernelGGL((attend_kernel<64, 64, 2>), grid, block, 0, st, a); break;
+        case 3: hipLaunchKernelGGL((attend_kernel<64, 64, 3>), grid, block, 0, st, a); break;
+        default: hipLaunchKernelGGL((attend_kernel<64, 64, 4>), grid, block, 0, st, a); break;
+        }
     }
-#undef SA_ATTEND
     if (mk) mk->mark();
     if (a.splits > 1) {
         dim3 cg(p->num_heads, rows);
