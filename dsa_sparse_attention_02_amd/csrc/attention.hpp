@@ -67,6 +67,10 @@ struct AttnArgs {
     float scale_log2;            // softmax_scale * log2(e)
 };
 
+#ifndef SA_ATTN_GATHER_NT
+#define SA_ATTN_GATHER_NT 0
+#endif
+
 constexpr int kAttnBuffers = 4;  // tile ring: kAttnBuffers - 1 tiles in flight while one is computed
 
 // s_barrier without the memory fence __syncthreads adds (which would wait for
@@ -256,7 +260,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         // the rest).
         uint32_t la = (uint32_t)(uintptr_t)((SA_LDS uint8_t *)&tile[0][0] + dst);
         asm volatile("" : "+s"(la));
+#if SA_ATTN_GATHER_NT
+        dma16_to_lds_stream(reinterpret_cast<const void *>(base + off), (SA_LDS void *)(uintptr_t)la);
+#else
         dma16_to_lds(reinterpret_cast<const void *>(base + off), (SA_LDS void *)(uintptr_t)la);
+#endif
     };
     auto issue_tile = [&](int tn, int buf) {
         const uint32_t myrow = tile_row(tn);

@@ -55,6 +55,14 @@ __device__ __forceinline__ void dma16_to_lds(const void *src, SA_LDS void *lds_w
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 0);
 }
 
+// The same copy with the non-temporal cache policy, for data read once: a
+// streamed 1.2 GB read of random 16 KiB pages runs at ~6.7 TB/s with it
+// against ~4.6 TB/s with the default policy on MI355X.
+__device__ __forceinline__ void dma16_to_lds_stream(const void *src, SA_LDS void *lds_wave_base)
+{
+    __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 2 /* nt */);
+}
+
 // Min and max of v over the 32 lanes of each wave half (every lane gets them);
 // lanes with valid == false are ignored.
 __device__ __forceinline__ f32x2 minmax32(float v, bool valid)

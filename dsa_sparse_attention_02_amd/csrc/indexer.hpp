@@ -48,6 +48,23 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+constexpr int kScanStores = 2;  // store instructions per scored tile: scores, tile range
+
+// Wait until the copies of the j-th tile of a segment have landed (see the ring
+// comment in the kernel): younger are (stages - 1) tiles of copies and the
+// stores of min(j, stages - 1) scored tiles.
+template <int DMA>
+__device__ __forceinline__ void scan_wait(int j)
+{
+    constexpr int S1 = kScanStages - 1;
+    static_assert(S1 * (DMA + kScanStores) < 64, "vmcnt range");
+    if (j >= S1) wait_vmcnt<S1 * (DMA + kScanStores)>();
+    else if (j == 0) wait_vmcnt<S1 * DMA>();
+    else if (j == 1) wait_vmcnt<S1 * DMA + kScanStores>();
+    else if (j == 2) wait_vmcnt<S1 * DMA + 2 * kScanStores>();
+    else wait_vmcnt<S1 * DMA>();  // (deeper rings) waiting for more is safe
+}
+
 // BLOCK_TILE: every cache block holds a whole number of 32-key tiles (block_size
 // >= 32), so a tile's 32 rows are contiguous and its block id is one scalar load.
 template <int IDX_DIM, int IDX_TILES, bool BLOCK_TILE>
@@ -107,20 +124,16 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
     // per-segment state, read by the helpers below
     int ctx = 0, nt = 0;
     const int32_t *tbl = block_table;
-    // Physical row of a tile's first key (BLOCK_TILE).  A window of 64 block-table
-    // entries sits in one register (lane i holds entry lo + i) and is read with
-    // v_readlane, so the steady state issues no memory request for the table;
-    // the window is refilled once per 64 blocks.
-    int win_lo = -(1 << 30), win = 0;
+    // Physical row of a tile's first key (BLOCK_TILE).  The block-table entry is a
+    // scalar load (constant address space, wave-uniform index): scalar loads are
+    // counted by lgkmcnt, so waiting for one never drains the copies in flight,
+    // and it is issued a tile before its copies need it.
+    typedef const __attribute__((address_space(4))) int32_t *ctbl_t;
     auto tile_base = [&](int t) -> int64_t {
         if constexpr (BLOCK_TILE) {
             const int s0 = (t < nt - 1 ? t : nt - 1) * 32;
-            const int bi = s0 >> bs_log2;
-            if (bi < win_lo || bi >= win_lo + 64) {
-                win_lo = bi;
-                win = bi + lane < max_blocks ? tbl[bi + lane] : 0;
-            }
-            const int blk = __builtin_amdgcn_readlane(win, bi - win_lo);
+            const int bi = __builtin_amdgcn_readfirstlane(s0 >> bs_log2);
+            const int blk = ((ctbl_t)(uintptr_t)tbl)[bi];
             return ((int64_t)blk << bs_log2) | (s0 & bmask);
         } else {
             return 0;
@@ -135,7 +148,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
             int64_t row;
             if constexpr (BLOCK_TILE) row = base + (s - s0);
             else row = ((int64_t)tbl[s >> bs_log2] << bs_log2) | (s & bmask);
-            dma16_to_lds(idx_k + row * IDX_DIM + dma_piece[i] * 8, (SA_LDS void *)(my + stage * TILE + i * 1024));
+            dma16_to_lds_stream(idx_k + row * IDX_DIM + dma_piece[i] * 8, (SA_LDS void *)(my + stage * TILE + i * 1024));
         }
     };
 
@@ -147,7 +160,6 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
         const int64_t rem = t_end - row_first;
         const int t1 = rem < nt ? (int)rem : nt;
         tbl = block_table + (int64_t)b * max_blocks;
-        win_lo = -(1 << 30);
         float *out = scores + (int64_t)b * score_stride;
 
         // queries and head weights of row b (waits for everything in flight: once per segment)
@@ -165,6 +177,11 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
             }
         }
 
+        // Ring waits.  Every tile issues DMA copies and then kScanStores stores (its
+        // scores and its range), all counted by vmcnt, which completes in issue
+        // order; at the wait for tile j the younger operations are the copies of
+        // the kScanStages - 1 tiles ahead and the stores of the (up to)
+        // kScanStages - 1 tiles scored since tile j's copies went out.
         const int n = t1 - t0;
 #pragma unroll
         for (int j = 0; j < kScanStages - 1; ++j)
@@ -175,7 +192,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
             if (j + kScanStages - 1 < n) {
                 issue(t0 + j + kScanStages - 1, (j + kScanStages - 1) % kScanStages, base_next);
                 base_next = tile_base(t0 + j + kScanStages);
-                wait_vmcnt<DMA * (kScanStages - 1)>();
+                scan_wait<DMA>(j);
             } else {
                 wait_vmcnt<0>();
             }
@@ -204,8 +221,12 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
                 }
             const float p = (part[0] + part[1]) + (part[2] + part[3]);
             const float tot = p + __shfl_xor(p, 32);
+            // Every slot of the tile lies inside the row's score stride (rounded up
+            // from the largest context), so all lanes store: slots at or past ctx
+            // get values nothing reads, and the store instruction is issued on
+            // every tile, as the ring waits count.
             const int s = (t0 + j) * 32 + col;
-            if (half == 0 && s < ctx) out[s] = tot + 0.0f;
+            out[s] = tot + 0.0f;
             // the tile's score range, for the range-binned top-k histogram
             const f32x2 mm = minmax32(tot + 0.0f, s < ctx);
             if (lane == 0) tile_mm[(int64_t)b * mm_stride + t0 + j] = mm;

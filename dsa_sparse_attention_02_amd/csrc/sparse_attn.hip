@@ -27,6 +27,10 @@ using namespace sa;
 constexpr int kMaxTopk = 16384;
 constexpr int kTargetAttnBlocks = 256;        // one attention workgroup per CU of an MI355X
 constexpr int kCUs = 256;                     // compute units of an MI355X
+#ifndef SA_SCAN_BLOCKS_PER_CU
+#define SA_SCAN_BLOCKS_PER_CU 1
+#endif
+constexpr int kScanBlocksPerCU = SA_SCAN_BLOCKS_PER_CU;  // persistent scan blocks per CU
 constexpr size_t kPrefillScoreBudget = size_t(256) << 20;  // bytes of scores per prefill chunk
 constexpr size_t kPrefillPartialBudget = size_t(256) << 20;
 constexpr size_t kAlign = 256;
@@ -90,7 +94,7 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
     d.tokens_per_split = tps;
     // persistent scan: one block of 4 waves per CU, fewer when there are few tiles
     const int64_t tiles = (int64_t)batch * ((std::max(max_ctx, 1) + 31) / 32);
-    d.scan_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(kCUs, (tiles + 31) / 32));
+    d.scan_blocks = (int)std::max<int64_t>(1, std::min<int64_t>(kScanBlocksPerCU * kCUs, (tiles + 31) / 32));
     size_t off = 0;
     d.off_scores = off;
     off = align_up(off + (size_t)batch * d.score_stride * 4, kAlign);
