@@ -182,22 +182,81 @@ def sa_chunk_rows(sa, p, L):
 
 
 def cpu_baseline(args, w):
+    """The oracle as it stands, on the host's cores, over a bounded sample of the
+    same batch: rows longest first, passes repeated until the time budget is spent."""
     import oracle
     import numpy as np
     ctx = w["context_lens"]
     order = np.argsort(ctx)[::-1]  # start with the longest rows: the costliest per token
-    rows, t0 = [], time.perf_counter()
+    done, distinct, t0 = 0, set(), time.perf_counter()
     stage = np.zeros(3)
-    for r in order:
-        oracle.run(w, rows=[int(r)], stage_seconds=stage)
-        rows.append(int(r))
-        if time.perf_counter() - t0 >= args.cpu_seconds:
-            break
+    while time.perf_counter() - t0 < args.cpu_seconds:
+        for r in order:
+            oracle.run(w, rows=[int(r)], stage_seconds=stage)
+            done += 1
+            distinct.add(int(r))
+            if time.perf_counter() - t0 >= args.cpu_seconds:
+                break
     el = time.perf_counter() - t0
-    return {"value": round(len(rows) / el, 3), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
-            "sample": f"{len(rows)} of {len(ctx)} decode rows of {args.workload} (longest first, ctx "
-                      f"{int(ctx[rows].min())}-{int(ctx[rows].max())}); {el:.1f}s: indexer {stage[0]:.1f}s, "
-                      f"sort {stage[1]:.1f}s, attention {stage[2]:.1f}s"}
+    rows = sorted(distinct)
+    return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "sample": f"{done} decode-row evaluations over {len(rows)} of {len(ctx)} rows of {args.workload} "
+                      f"(longest first, ctx {int(ctx[rows].min())}-{int(ctx[rows].max())}, repeated to fill the "
+                      f"budget); {el:.1f}s: indexer {stage[0]:.1f}s, sort {stage[1]:.1f}s, attention {stage[2]:.1f}s"}
+
+
+TRAFFIC_KERNEL = "idx_score_decode_kernel<128, 2>"
+TRAFFIC_SOURCES = ["indexer.hpp", "device_common.hpp"]
+
+
+def _counter_rows(path):
+    """(kernel name, counter name, value) of every row of a rocprofv3 counter CSV
+    (a file, or a directory searched for *counter_collection.csv)."""
+    import csv
+    import glob
+    files = [path] if os.path.isfile(path) else \
+        glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit(f"no counter_collection.csv under {path}")
+    out = []
+    for f in files:
+        with open(f, newline="") as fh:
+            for row in csv.DictReader(fh):
+                out.append((row["Kernel_Name"], row["Counter_Name"], float(row["Counter_Value"])))
+    return out
+
+
+def traffic_summary(fetch_path, write_path, workload):
+    """HBM bytes per launch of the decode scan from two rocprofv3 --pmc runs
+    (FETCH_SIZE, then WRITE_SIZE, KiB per dispatch), each scaled by what the
+    same counter reads for a plain 1 GiB device copy (bench.py --copy-calibration)."""
+    def per_kernel(rows, counter):
+        vals = {}
+        for k, c, v in rows:
+            if c == counter:
+                vals.setdefault(k, []).append(v)
+        return vals
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_path), ("WRITE_SIZE", write_path)):
+        vals = per_kernel(_counter_rows(path), counter)
+        kib = 1 << 20  # a 1 GiB copy reads and writes 1 GiB
+        copies = [v for k, vs in vals.items() if "copy" in k.lower() or "elementwise" in k.lower()
+                  for v in vs if 0.5 * kib < v < 4 * kib]
+        if not copies:
+            raise SystemExit(f"no 1 GiB copy dispatch found for {counter}")
+        factor = kib / statistics.median(copies)
+        scan = [v for k, vs in vals.items() if k.startswith("void sa::idx_score_decode_kernel<128, 2, true>")
+                or k.startswith("sa::idx_score_decode_kernel<128, 2, true>") for v in vs]
+        if not scan:
+            raise SystemExit(f"no decode-scan dispatch found for {counter}")
+        res[counter] = dict(kib_raw=statistics.median(scan), copy_kib_raw=statistics.median(copies),
+                            factor=factor, bytes=statistics.median(scan) * factor * 1024, dispatches=len(scan))
+    return {"kernel": TRAFFIC_KERNEL, "workload": workload, "sources": TRAFFIC_SOURCES,
+            "source_hash": source_hash(*TRAFFIC_SOURCES),
+            "fetch_bytes_per_launch": round(res["FETCH_SIZE"]["bytes"]),
+            "write_bytes_per_launch": round(res["WRITE_SIZE"]["bytes"]),
+            "bytes_per_launch": round(res["FETCH_SIZE"]["bytes"] + res["WRITE_SIZE"]["bytes"]),
+            "counters": res}
 
 
 def main():
@@ -213,7 +272,23 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU run: turn two rocprofv3 --pmc outputs (FETCH_SIZE, WRITE_SIZE) of this "
+                         "benchmark into profiles/traffic.json")
     args = ap.parse_args()
+    if args.traffic_from:
+        t = traffic_summary(args.traffic_from[0], args.traffic_from[1], args.workload)
+        path = os.path.join(ROOT, "profiles", "traffic.json")
+        try:
+            with open(path) as f:
+                allt = json.load(f)
+        except (OSError, ValueError):
+            allt = {}
+        allt[TRAFFIC_KERNEL + "/" + args.workload] = t
+        with open(path, "w") as f:
+            json.dump(allt, f, indent=1)
+        print(json.dumps(t, indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the sparse-attention path here is single-GPU "
@@ -233,9 +308,9 @@ def main():
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)
         for _ in range(3):
-            dst.copy_(src)
+            torch.mul(src, 1.0, out=dst)  # an elementwise kernel: reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
-        log("copy calibration: 3 copies of 1 GiB")
+        log("copy calibration: 3 elementwise copies of 1 GiB")
         del src, dst
 
     w, dec = run_decode(args, torch, sa, synth)
@@ -247,8 +322,8 @@ def main():
     roof = None
     if t_idx:
         achieved = alg["indexer_bytes"] / (t_idx / 1e3) / 1e9
-        traffic = traffic_from_profiles("idx_score_decode_kernel<128, 2>/" + args.workload, 1)
-        roof = {"bound": "hbm", "kernel": "idx_score_decode_kernel<128, 2>", "achieved": round(achieved, 1),
+        traffic = traffic_from_profiles(TRAFFIC_KERNEL + "/" + args.workload, 1)
+        roof = {"bound": "hbm", "kernel": TRAFFIC_KERNEL, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                 "traffic": traffic, "avg_ms": round(t_idx, 5)}
     line = {

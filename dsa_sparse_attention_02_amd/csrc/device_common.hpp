@@ -76,6 +76,43 @@ __device__ __forceinline__ f32x2 minmax32(float v, bool valid)
     return f32x2{mn, mx};
 }
 
+// p[l] + p[l ^ 32] in every lane: v_permlane32_swap of p with itself hands
+// lanes 0..31 the upper half and lanes 32..63 the lower half.
+__device__ __forceinline__ float add_wave_halves(float p)
+{
+    const uint32_t u = __float_as_uint(p);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+
+// Min and max of v over lanes 0..31 (lanes with valid == false ignored), as
+// wave-uniform values: DPP butterflies within each 16-lane row (quad swaps,
+// half-row mirror, row mirror), then the two row results read by v_readlane.
+// The wave must run with every lane active.
+__device__ __forceinline__ f32x2 minmax32_uniform(float v, bool valid)
+{
+    float mn = valid ? v : INFINITY, mx = valid ? v : -INFINITY;
+    mn = fminf(mn, dpp_f32<0xB1>(mn));   // quad_perm [1,0,3,2]
+    mx = fmaxf(mx, dpp_f32<0xB1>(mx));
+    mn = fminf(mn, dpp_f32<0x4E>(mn));   // quad_perm [2,3,0,1]
+    mx = fmaxf(mx, dpp_f32<0x4E>(mx));
+    mn = fminf(mn, dpp_f32<0x141>(mn));  // row_half_mirror
+    mx = fmaxf(mx, dpp_f32<0x141>(mx));
+    mn = fminf(mn, dpp_f32<0x140>(mn));  // row_mirror
+    mx = fmaxf(mx, dpp_f32<0x140>(mx));
+    const float mn0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mn), 0));
+    const float mn1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mn), 16));
+    const float mx0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 0));
+    const float mx1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx), 16));
+    return f32x2{fminf(mn0, mn1), fmaxf(mx0, mx1)};
+}
+
 // Order-preserving map from an fp32 score to uint32: a larger key is a larger
 // score; -0 is folded into +0 first so the two compare equal.
 __device__ __forceinline__ uint32_t score_key(float f)

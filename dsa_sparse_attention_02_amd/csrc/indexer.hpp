@@ -16,6 +16,8 @@
 // sum are applied in registers and the two lane halves are added with one swap.
 #pragma once
 
+#include <type_traits>
+
 #include "device_common.hpp"
 
 namespace sa {
@@ -48,7 +50,9 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-constexpr int kScanStores = 2;  // store instructions per scored tile: scores, tile range
+// store instructions every scored tile issues (its scores); the tile ranges are
+// flushed once per 16 tiles, and such an extra store only lengthens a wait
+constexpr int kScanStores = 1;
 
 // Wait until the copies of the j-th tile of a segment have landed (see the ring
 // comment in the kernel): younger are (stages - 1) tiles of copies and the
@@ -183,6 +187,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
         // the kScanStages - 1 tiles ahead and the stores of the (up to)
         // kScanStages - 1 tiles scored since tile j's copies went out.
         const int n = t1 - t0;
+        float mm_lo = 0.0f, mm_hi = 0.0f;  // lane i: range of the segment's pending tile with index = i mod 16
 #pragma unroll
         for (int j = 0; j < kScanStages - 1; ++j)
             if (j < n) issue(t0 + j, j, tile_base(t0 + j));
@@ -211,25 +216,41 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
 #pragma unroll
                 for (int t = 0; t < IDX_TILES; ++t) acc[t][ks & 1] = mfma_32x32x16(qa[t][ks], kb[ks], acc[t][ks & 1]);
             float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            auto head_sum = [&](auto relu_on) {
 #pragma unroll
-            for (int t = 0; t < IDX_TILES; ++t)
+                for (int t = 0; t < IDX_TILES; ++t)
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float d = acc[t][0][i] + acc[t][1][i];
-                    if (relu) d = fmaxf(d, 0.0f);
-                    part[i & 3] = fmaf(wr[t][i], d, part[i & 3]);
-                }
+                    for (int i = 0; i < 16; ++i) {
+                        float d = acc[t][0][i] + acc[t][1][i];
+                        if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
+                        part[i & 3] = fmaf(wr[t][i], d, part[i & 3]);
+                    }
+            };
+            if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
+            else head_sum(std::false_type{});
             const float p = (part[0] + part[1]) + (part[2] + part[3]);
-            const float tot = p + __shfl_xor(p, 32);
+            const float tot = add_wave_halves(p);
             // Every slot of the tile lies inside the row's score stride (rounded up
-            // from the largest context), so all lanes store: slots at or past ctx
-            // get values nothing reads, and the store instruction is issued on
-            // every tile, as the ring waits count.
-            const int s = (t0 + j) * 32 + col;
-            out[s] = tot + 0.0f;
-            // the tile's score range, for the range-binned top-k histogram
-            const f32x2 mm = minmax32(tot + 0.0f, s < ctx);
-            if (lane == 0) tile_mm[(int64_t)b * mm_stride + t0 + j] = mm;
+            // from the largest context), so the 32 lanes of half 0 all store: slots
+            // at or past ctx get values nothing reads, and the store instruction is
+            // issued on every tile, as the ring waits count.
+            const int tt = t0 + j;
+            const int s = tt * 32 + col;
+            if (half == 0) out[s] = tot + 0.0f;
+            // The tile's score range, for the range-binned top-k histogram.  Lane
+            // tt % 16 keeps it, and a group of 16 tiles is written as one whole
+            // 128-byte line (partial lines only at segment ends) instead of one
+            // 8-byte store per tile.
+            const f32x2 mm = minmax32_uniform(tot + 0.0f, s < ctx);
+            if (lane == (tt & 15)) {
+                mm_lo = mm[0];
+                mm_hi = mm[1];
+            }
+            if ((tt & 15) == 15 || j == n - 1) {
+                const int g0 = tt & ~15, first = (g0 > t0 ? g0 : t0) - g0;
+                if (lane >= first && lane <= (tt & 15))
+                    tile_mm[(int64_t)b * mm_stride + g0 + lane] = f32x2{mm_lo, mm_hi};
+            }
         }
         t_cur = row_first + t1;
         row_first += nt;
