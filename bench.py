@@ -156,7 +156,10 @@ def run_prefill(args, torch, sa, synth):
         if r0 + min(plan_rows, L - r0) > p.topk:
             names.append("indexer")
         names.append("topk")
-    names += ["attention"] * (n_marks - 1 - len(names))
+    n_attn = n_marks - 1 - len(names)
+    if n_attn < 1:
+        raise SystemExit(f"prefill marks ({n_marks}) do not match the chunk plan ({len(names)} select kernels)")
+    names += ["attention"] * n_attn
     tot = {}
     for ev in evs:
         for i, k in enumerate(names):
@@ -175,9 +178,9 @@ def run_prefill(args, torch, sa, synth):
 
 def sa_chunk_rows(sa, p, L):
     """Rows per prefill indexer/top-k chunk (mirrors the library's planning: scores of
-    a chunk take at most 256 MiB, in multiples of 16 rows)."""
+    a chunk take at most 1 GiB, in multiples of 16 rows)."""
     stride = (L + 63) // 64 * 64
-    rows = max(16, ((256 << 20) // (stride * 4)) // 16 * 16)
+    rows = max(16, ((1 << 30) // (stride * 4)) // 16 * 16)
     return min(rows, (L + 15) // 16 * 16)
 
 

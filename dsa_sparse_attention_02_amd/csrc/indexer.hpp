@@ -353,19 +353,23 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
                     for (int t = 0; t < IDX_TILES; ++t) acc[t] = mfma_32x32x16(qa[rr][t][ks], kb[ks], acc[t]);
                 const int lr = 2 * wave + rr;
                 float part = 0.0f;
+                auto head_sum = [&](auto relu_on) {
 #pragma unroll
-                for (int t = 0; t < IDX_TILES; ++t)
+                    for (int t = 0; t < IDX_TILES; ++t)
 #pragma unroll
-                    for (int q4 = 0; q4 < 4; ++q4) {
-                        const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&wts[lr][32 * t + 8 * q4 + 4 * half]);
+                        for (int q4 = 0; q4 < 4; ++q4) {
+                            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&wts[lr][32 * t + 8 * q4 + 4 * half]);
 #pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float d = acc[t][4 * q4 + e];
-                            if (relu) d = fmaxf(d, 0.0f);
-                            part = fmaf(w4[e], d, part);
+                            for (int e = 0; e < 4; ++e) {
+                                float d = acc[t][4 * q4 + e];
+                                if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
+                                part = fmaf(w4[e], d, part);
+                            }
                         }
-                    }
-                const float tot = part + __shfl_xor(part, 32);
+                };
+                if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
+                else head_sum(std::false_type{});
+                const float tot = add_wave_halves(part);
                 const int s = s0 + col;
                 if (half == 0 && s <= pos[rr]) scores[(int64_t)(r0 + lr) * score_stride + s] = tot + 0.0f;
                 if (s <= pos[rr]) {  // lane-local running range of the row's scores

@@ -31,7 +31,7 @@ constexpr int kCUs = 256;                     // compute units of an MI355X
 #define SA_SCAN_BLOCKS_PER_CU 1
 #endif
 constexpr int kScanBlocksPerCU = SA_SCAN_BLOCKS_PER_CU;  // persistent scan blocks per CU
-constexpr size_t kPrefillScoreBudget = size_t(256) << 20;  // bytes of scores per prefill chunk
+constexpr size_t kPrefillScoreBudget = size_t(1) << 30;  // bytes of scores per prefill chunk (enough rows to fill every CU)
 constexpr size_t kPrefillPartialBudget = size_t(256) << 20;
 constexpr size_t kAlign = 256;
 

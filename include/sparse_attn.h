@@ -166,7 +166,9 @@ sa_status sparse_attn_decode_profiled(const sa_params *p, const sa_paged_cache *
  * position q_start + i and sees keys [0, q_start + i] (causal limit, itself
  * included).  The cache must hold at least q_start + num_rows tokens.
  * Layouts as for decode with batch replaced by num_rows.  Rows whose visible
- * key count is at most topk attend to all of their keys.
+ * key count is at most topk attend to all of their keys.  The workspace holds
+ * the fp32 scores of a chunk of rows at a time (at most 1 GiB of them, at
+ * least 16 rows), so it stays bounded however many rows the call covers.
  */
 sa_status sa_prefill_workspace_size(const sa_params *p, int32_t num_rows, int32_t q_start,
                                     size_t *bytes /* host, out */);
