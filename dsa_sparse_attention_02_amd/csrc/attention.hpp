@@ -67,16 +67,8 @@ struct AttnArgs {
     float scale_log2;            // softmax_scale * log2(e)
 };
 
-#ifndef SA_ATTN_GATHER_NT
-#define SA_ATTN_GATHER_NT 0
-#endif
-
 constexpr int kAttnBuffers = 4;  // tile ring: kAttnBuffers - 1 tiles in flight while one is computed
 
-// s_barrier without the memory fence __syncthreads adds (which would wait for
-// every LDS-DMA copy in flight); the asm memory clobber keeps the compiler from
-// moving memory operations across it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
 template <int N>
 __device__ __forceinline__ void attn_wait_vmcnt()
@@ -254,17 +246,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         const uint64_t base = row != kNoRow ? kv_addr + (uint64_t)row * (QK * 2) : zero_addr;
         const uint32_t off = is_main ? lane * 16 : (S::MAIN + 2 * j + (lane >> 5)) * 16;
         const int dst = buf * S::TILE_BYTES + (is_main ? ii * S::MAIN_STRIDE : S::TAIL_BASE + j * 1024);
-        // The LDS address goes through an opaque register: the copy then carries
-        // no alias scope of `tile`, and the compiler adds no wait for it before
-        // later tile reads (which read other buffers; the ring waits above order
-        // the rest).
-        uint32_t la = (uint32_t)(uintptr_t)((SA_LDS uint8_t *)&tile[0][0] + dst);
-        asm volatile("" : "+s"(la));
-#if SA_ATTN_GATHER_NT
-        dma16_to_lds_stream(reinterpret_cast<const void *>(base + off), (SA_LDS void *)(uintptr_t)la);
-#else
-        dma16_to_lds(reinterpret_cast<const void *>(base + off), (SA_LDS void *)(uintptr_t)la);
-#endif
+        // (opaque LDS address: the tile reads that follow use other buffers, and
+        // the ring waits order the rest)
+        SA_LDS void *la = opaque_lds((SA_LDS uint8_t *)&tile[0][0] + dst);
+        dma16_to_lds(reinterpret_cast<const void *>(base + off), la);
     };
     auto issue_tile = [&](int tn, int buf) {
         const uint32_t myrow = tile_row(tn);

@@ -63,6 +63,22 @@ __device__ __forceinline__ void dma16_to_lds_stream(const void *src, SA_LDS void
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 2 /* nt */);
 }
 
+// s_barrier without the memory fence __syncthreads adds (which would wait for
+// every LDS-DMA copy in flight); the asm memory clobber keeps the compiler from
+// moving memory operations across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
+// An LDS address the compiler cannot trace to a __shared__ array: a copy into it
+// carries no alias scope, so the compiler adds no wait for that copy before
+// later reads of other buffers of the same array (ordering is then the
+// caller's, through explicit vmcnt waits and barriers).
+__device__ __forceinline__ SA_LDS void *opaque_lds(SA_LDS void *p)
+{
+    uint32_t a = (uint32_t)(uintptr_t)p;
+    asm volatile("" : "+s"(a));
+    return (SA_LDS void *)(uintptr_t)a;
+}
+
 // Min and max of v over the 32 lanes of each wave half (every lane gets them);
 // lanes with valid == false are ignored.
 __device__ __forceinline__ f32x2 minmax32(float v, bool valid)

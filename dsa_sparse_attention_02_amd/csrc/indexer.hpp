@@ -262,13 +262,16 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
 // ----------------------------------------------------------------- prefill --
 // One workgroup of 8 waves owns 16 consecutive query rows (2 per wave) and
 // streams every key those rows can see, [0, last row's position], in tiles of
-// 32 keys staged once in LDS and read by all 8 waves.  Each wave keeps both of
-// its rows' indexer queries in registers, so every key tile feeds
-// 2 rows x IDX_TILES x (IDX_DIM/16) MFMAs per wave.  Blocks run heaviest
-// (last rows) first.
+// 32 keys read by all 8 waves.  Key tiles come HBM/L2 -> LDS through the
+// LDS-DMA path into a kPrefillRing-deep ring, in the decode scan's swizzled
+// layout (one 1 KiB copy per wave per tile for 128-dim keys).  Each wave keeps
+// both of its rows' indexer queries in registers, so every key tile feeds
+// 2 rows x IDX_TILES x (IDX_DIM/16) MFMAs per wave.  Blocks run heaviest (last
+// rows) first.
 constexpr int kPrefillRowsPerBlock = 16;
+constexpr int kPrefillRing = 4;
 
-template <int IDX_DIM, int IDX_TILES>
+template <int IDX_DIM, int IDX_TILES, bool BLOCK_TILE>
 __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
     const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int bs_log2,
     const uint16_t *__restrict__ idx_q, const float *__restrict__ idx_w, int idx_heads, int relu,
@@ -276,25 +279,53 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
     int64_t mm_stride)
 {
     constexpr int KS = IDX_DIM / 16;
-    constexpr int ROW_BYTES = IDX_DIM * 2 + 16;  // +16: consecutive keys start 4 banks apart
-    constexpr int CHUNKS = 32 * IDX_DIM * 2 / 16;  // 16-byte pieces per key tile
+    constexpr int PIECES = IDX_DIM / 8;         // 16-byte pieces per key row
+    constexpr int TILE = 32 * IDX_DIM * 2;      // bytes per 32-key tile
+    constexpr int DMA = TILE / 1024;            // copies per tile, one per wave for DMA <= 8
+    static_assert(DMA <= 8, "one copy per wave and tile");
+    constexpr int SW = PIECES - 1;
     constexpr int HP = 32 * IDX_TILES;
-    __shared__ __attribute__((aligned(16))) uint8_t ktile[2][32 * ROW_BYTES];
+    constexpr int R = kPrefillRing;
+    __shared__ __attribute__((aligned(1024))) uint8_t ring[R][TILE];
     __shared__ __attribute__((aligned(16))) float wts[kPrefillRowsPerBlock][HP];
 
     const int g = gridDim.x - 1 - blockIdx.x;
     const int r0 = g * kPrefillRowsPerBlock;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
     const int rows_here = min(kPrefillRowsPerBlock, nrows - r0);
     const int nkeys = pos0 + r0 + rows_here;  // keys visible to the block's last row
     const int bmask = (1 << bs_log2) - 1;
+    const int ntiles = (nkeys + 31) / 32;
+
+    // this wave's copy of every tile: slot 64*wave + lane = PIECES*r + q holds
+    // piece q ^ (r & SW) of the tile's key row r
+    const int dslot = 64 * wave + lane;
+    const int dr = dslot / PIECES, dpiece = (dslot % PIECES) ^ (dr & SW);
+    typedef const __attribute__((address_space(4))) int32_t *ctbl_t;
+    auto issue = [&](int kt) {
+        if (wave >= DMA) return;  // (wave-uniform)
+        const int ktc = kt < ntiles ? kt : ntiles - 1;  // past the end: copy the last tile again
+        const int s0 = ktc * 32;
+        int s = s0 + dr;
+        s = s < nkeys ? s : nkeys - 1;  // rows past the last visible key re-read it; never scored
+        int64_t row;
+        if constexpr (BLOCK_TILE) {
+            const int bi = __builtin_amdgcn_readfirstlane(s0 >> bs_log2);
+            row = (((int64_t)((ctbl_t)(uintptr_t)block_table)[bi]) << bs_log2) + (s & bmask);
+        } else {
+            row = ((int64_t)block_table[s >> bs_log2] << bs_log2) | (s & bmask);
+        }
+        dma16_to_lds(idx_k + row * IDX_DIM + dpiece * 8, opaque_lds((SA_LDS void *)&ring[kt % R][64 * wave * 16]));
+    };
+    // the ring is issued first: its copies overlap the query loads below
+#pragma unroll
+    for (int j = 0; j < R - 1; ++j) issue(j);
 
     for (int e = threadIdx.x; e < kPrefillRowsPerBlock * HP; e += blockDim.x) {
         const int rr = e / HP, hj = e % HP;
         wts[rr][hj] = (rr < rows_here && hj < idx_heads) ? idx_w[(int64_t)(r0 + rr) * idx_heads + hj] : 0.0f;
     }
-
     bf16x8 qa[2][IDX_TILES][KS];
     int pos[2];
 #pragma unroll
@@ -311,76 +342,67 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
                                                                     : as_bf16x8(u32x4{0, 0, 0, 0});
         }
     }
-
-    // one 16-byte piece of a key tile per thread (threads past CHUNKS idle)
-    const int pc = threadIdx.x;
-    const int pkey = pc / (IDX_DIM / 8), ppart = pc % (IDX_DIM / 8);
-    auto fetch = [&](int kt) -> u32x4 {
-        const int s = kt * 32 + pkey;
-        if (pc < CHUNKS && s < nkeys) {
-            const int64_t row = ((int64_t)block_table[s >> bs_log2] << bs_log2) | (s & bmask);
-            return load16(idx_k + row * IDX_DIM + ppart * 8);
-        }
-        return u32x4{0, 0, 0, 0};
-    };
-    auto stash = [&](int buf, u32x4 v) {
-        if (pc < CHUNKS) *reinterpret_cast<u32x4 *>(&ktile[buf][pkey * ROW_BYTES + ppart * 16]) = v;
-    };
-
-    const int ntiles = (nkeys + 31) / 32;
+    const int koff = col * PIECES * 16, kx = col & SW;
     float rlo[2] = {INFINITY, INFINITY}, rhi[2] = {-INFINITY, -INFINITY};
-    stash(0, fetch(0));
-    __syncthreads();
+
+    // Ring: tile kt's copies were issued R-1 iterations earlier, and every later
+    // iteration issued exactly one more copy per copying wave (tiles past the end
+    // repeat the last one), so at the wait for tile kt at least R-2 younger copies
+    // are in flight; copies complete in order, and the younger score stores only
+    // lengthen the wait.  The barrier then makes every wave's copy of tile kt
+    // visible and frees tile kt-1's buffer for tile kt+R-1.
     for (int kt = 0; kt < ntiles; ++kt) {
-        const int buf = kt & 1;
-        u32x4 nxt = u32x4{0, 0, 0, 0};
-        if (kt + 1 < ntiles) nxt = fetch(kt + 1);
+        wait_vmcnt<R - 2>();
+        barrier_no_fence();
+        issue(kt + R - 1);
         const int s0 = kt * 32;
-        if (s0 <= pos[0] || s0 <= pos[1]) {
-            bf16x8 kb[KS];
-            const uint8_t *kr = &ktile[buf][col * ROW_BYTES + half * IDX_DIM];
+        if (s0 > pos[0] && s0 > pos[1]) continue;  // (wave-uniform) both rows end before this tile
+        const uint8_t *tb = &ring[kt % R][0];
+        // all K operands of the tile first (their LDS reads overlap), then per row:
+        // its MFMAs, then its head reduction, so that one wave's reduction runs
+        // beside the other wave's MFMAs on the same SIMD
+        bf16x8 kb[KS];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) kb[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(kr + 16 * ks));
+        for (int ks = 0; ks < KS; ++ks)
+            kb[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff + (((half * KS + ks) ^ kx) * 16)));
 #pragma unroll
-            for (int rr = 0; rr < 2; ++rr) {
-                if (s0 > pos[rr]) continue;  // wave-uniform
-                f32x16 acc[IDX_TILES];
+        for (int rr = 0; rr < 2; ++rr) {
+            if (s0 > pos[rr]) continue;  // wave-uniform
+            f32x16 acc[IDX_TILES];
 #pragma unroll
-                for (int t = 0; t < IDX_TILES; ++t) acc[t] = f32x16{};
+            for (int t = 0; t < IDX_TILES; ++t) acc[t] = f32x16{};
 #pragma unroll
-                for (int ks = 0; ks < KS; ++ks)
+            for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-                    for (int t = 0; t < IDX_TILES; ++t) acc[t] = mfma_32x32x16(qa[rr][t][ks], kb[ks], acc[t]);
-                const int lr = 2 * wave + rr;
-                float part = 0.0f;
-                auto head_sum = [&](auto relu_on) {
+                for (int t = 0; t < IDX_TILES; ++t) acc[t] = mfma_32x32x16(qa[rr][t][ks], kb[ks], acc[t]);
+            const int lr = 2 * wave + rr;
+            float part = 0.0f;
+            auto head_sum = [&](auto relu_on) {
 #pragma unroll
-                    for (int t = 0; t < IDX_TILES; ++t)
+                for (int t = 0; t < IDX_TILES; ++t)
 #pragma unroll
-                        for (int q4 = 0; q4 < 4; ++q4) {
-                            const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&wts[lr][32 * t + 8 * q4 + 4 * half]);
+                    for (int q4 = 0; q4 < 4; ++q4) {
+                        const f32x4 w4 = *reinterpret_cast<const f32x4 *>(&wts[lr][32 * t + 8 * q4 + 4 * half]);
 #pragma unroll
-                            for (int e = 0; e < 4; ++e) {
-                                float d = acc[t][4 * q4 + e];
-                                if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
-                                part = fmaf(w4[e], d, part);
-                            }
+                        for (int e = 0; e < 4; ++e) {
+                            float d = acc[t][4 * q4 + e];
+                            if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
+                            part = fmaf(w4[e], d, part);
                         }
-                };
-                if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
-                else head_sum(std::false_type{});
-                const float tot = add_wave_halves(part);
-                const int s = s0 + col;
-                if (half == 0 && s <= pos[rr]) scores[(int64_t)(r0 + lr) * score_stride + s] = tot + 0.0f;
-                if (s <= pos[rr]) {  // lane-local running range of the row's scores
-                    rlo[rr] = fminf(rlo[rr], tot + 0.0f);
-                    rhi[rr] = fmaxf(rhi[rr], tot + 0.0f);
-                }
+                    }
+            };
+            if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
+            else head_sum(std::false_type{});
+            const float tot = add_wave_halves(part);
+            const int s = s0 + col;
+            if (half == 0 && s <= pos[rr]) scores[(int64_t)(r0 + lr) * score_stride + s] = tot + 0.0f;
+            if (s <= pos[rr]) {  // lane-local running range of the row's scores
+                rlo[rr] = fminf(rlo[rr], tot + 0.0f);
+                rhi[rr] = fmaxf(rhi[rr], tot + 0.0f);
             }
         }
-        if (kt + 1 < ntiles) stash(buf ^ 1, nxt);
-        __syncthreads();
     }
+    wait_vmcnt<0>();  // the last (repeated) copies have landed before the block ends
     // each row's score range, stored as the row's first tile entry (the prefill
     // top-k reads one range entry per row)
 #pragma unroll

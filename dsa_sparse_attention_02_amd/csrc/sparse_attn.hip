@@ -244,9 +244,14 @@ void launch_idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint1
                         hipStream_t st)
 {
     dim3 grid((nrows + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock);
-    hipLaunchKernelGGL((idx_score_prefill_kernel<D, T>), grid, dim3(512), 0, st, (const uint16_t *)c->idx_k,
-                       c->block_table, ilog2(p->block_size), idx_q, idx_w, p->idx_heads, p->idx_relu, pos0, nrows,
-                       scores, stride, mm, mm_stride);
+    if (p->block_size >= 32)
+        hipLaunchKernelGGL((idx_score_prefill_kernel<D, T, true>), grid, dim3(512), 0, st, (const uint16_t *)c->idx_k,
+                           c->block_table, ilog2(p->block_size), idx_q, idx_w, p->idx_heads, p->idx_relu, pos0,
+                           nrows, scores, stride, mm, mm_stride);
+    else
+        hipLaunchKernelGGL((idx_score_prefill_kernel<D, T, false>), grid, dim3(512), 0, st,
+                           (const uint16_t *)c->idx_k, c->block_table, ilog2(p->block_size), idx_q, idx_w,
+                           p->idx_heads, p->idx_relu, pos0, nrows, scores, stride, mm, mm_stride);
 }
 
 void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w, int pos0,
