@@ -103,6 +103,9 @@ CASES = {
     "prefill_qstart": lambda: synth.small_prefill("prefill_qstart", MLA, rows=700, q_start=1900, seed=107),
     "prefill_tiny_qstart": lambda: synth.small_prefill("prefill_tiny_qs", synth.TINY, rows=100, q_start=37, seed=108),
     "prefill_k4100": lambda: synth.small_prefill("prefill_k4100", MLA, rows=300, q_start=4000, seed=109, topk=4100),
+    # rows with exactly k, and more than k, 32-key tiles (the top-k's tile-maximum bound)
+    "decode_k256_bound": lambda: synth.small_decode("decode_k256_bound", MLA, [8191, 8192, 8193, 20000, 65536],
+                                                    seed=113, topk=256),
     # head counts that leave waves (or lanes of a wave) without a head
     "decode_h48": lambda: synth.small_decode("decode_h48", replace(MLA, num_heads=48), [1, 40, 2100, 5000], seed=110),
     "decode_h96": lambda: synth.small_decode("decode_h96", replace(MLA, num_heads=96), [2, 33, 2048, 6000], seed=111),
