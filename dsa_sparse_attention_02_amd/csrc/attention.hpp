@@ -67,6 +67,13 @@ struct AttnArgs {
     float scale_log2;            // softmax_scale * log2(e)
 };
 
+#ifndef SA_ATTN_KPF
+#define SA_ATTN_KPF 8  // K operand steps read ahead of their MFMA
+#endif
+#ifndef SA_ATTN_VPF
+#define SA_ATTN_VPF 4  // V operand steps read ahead of their MFMAs
+#endif
+
 constexpr int kAttnBuffers = 4;  // tile ring: kAttnBuffers - 1 tiles in flight while one is computed
 
 
@@ -151,6 +158,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     const int r = lb / per_row, split = (lb % per_row) / S::VSPLIT, vh = lb % S::VSPLIT;
     constexpr int nthreads = 64 * NW;
     const int wave = wave_uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
+    __builtin_assume(wave >= 0 && wave < NW);  // lets copy kinds resolve at compile time
     const int col = lane & 31, half = lane >> 5;
     const int seq = a.decode ? r : 0;
     const int limit = a.decode ? a.ctx_lens[r] : a.limit_base + r + 1;
@@ -238,23 +246,26 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         const uint32_t v = rows[max(0, min(tn, kAttnMaxSplitTokens / 32 - 1)) * 32 + (lane & 31)];
         return tn >= 0 && tn < nt_eff ? v : kNoRow;
     };
-    auto copy = [&](uint32_t myrow, int n, int buf) {
+    // `dstb`: the LDS base of the buffer, from opaque_lds (the tile reads that
+    // follow use other buffers, and the ring waits order the rest)
+    auto copy = [&](uint32_t myrow, int n, SA_LDS uint8_t *dstb) {
         const int ii = min(wave + NW * n, S::DMA_PER_TILE - 1);  // wave-uniform
         const bool is_main = ii < S::DMA_MAIN;
         const int j = ii - S::DMA_MAIN;
         const uint32_t row = is_main ? lane_read(myrow, min(ii, 31)) : myrow;
-        const uint64_t base = row != kNoRow ? kv_addr + (uint64_t)row * (QK * 2) : zero_addr;
+        // (a mask blend rather than a conditional, so no branch splits the q.k steps)
+        const uint64_t keep = (uint64_t)0 - (uint64_t)(row != kNoRow);
+        const uint64_t base = ((kv_addr + (uint64_t)row * (QK * 2)) & keep) | (zero_addr & ~keep);
         const uint32_t off = is_main ? lane * 16 : (S::MAIN + 2 * j + (lane >> 5)) * 16;
-        const int dst = buf * S::TILE_BYTES + (is_main ? ii * S::MAIN_STRIDE : S::TAIL_BASE + j * 1024);
-        // (opaque LDS address: the tile reads that follow use other buffers, and
-        // the ring waits order the rest)
-        SA_LDS void *la = opaque_lds((SA_LDS uint8_t *)&tile[0][0] + dst);
-        dma16_to_lds(reinterpret_cast<const void *>(base + off), la);
+        const int dst = is_main ? ii * S::MAIN_STRIDE : S::TAIL_BASE + j * 1024;
+        dma16_to_lds(reinterpret_cast<const void *>(base + off), dstb + dst);
     };
+    auto buffer_base = [&](int buf) { return (SA_LDS uint8_t *)opaque_lds((SA_LDS uint8_t *)&tile[buf][0]); };
     auto issue_tile = [&](int tn, int buf) {
         const uint32_t myrow = tile_row(tn);
+        SA_LDS uint8_t *dstb = buffer_base(buf);
 #pragma unroll 9
-        for (int n = 0; n < DMA_W; ++n) copy(myrow, n, buf);
+        for (int n = 0; n < DMA_W; ++n) copy(myrow, n, dstb);
     };
 
     // LDS byte offset of this lane's K operand of step ks (S row c holds token
@@ -265,27 +276,38 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
                                 : S::TAIL_BASE + (2 * ks - S::MAIN + hf) * 512 + 16 * tok;
     };
 
-    // One tile: S^T = K Q^T, softmax weights, O^T += V^T P^T, with the copies
-    // of tile tn into buffer nbuf issued between the q.k steps.  The schedule is
-    // pinned so that LDS operand reads run ahead of the MFMAs that use them:
-    // K operands KPF steps ahead, the first V operands during the softmax.
-    constexpr int KPF = 3;
-    auto compute = [&](int t, int buf, int tn, int nbuf) {
+    // Per tile: S^T = K Q^T (qk), the softmax weights of S^T (softmax), then
+    // O^T += V^T P^T (pv).  The loop below is software-pipelined across tiles:
+    // iteration t computes S^T of tile t+1 while the weights of tile t are
+    // formed (VALU beside the MFMAs), then multiplies tile t's values.  The
+    // schedule is pinned so that LDS operand reads run ahead of the MFMAs that
+    // use them: K operands KPF steps ahead, V operands VPF steps ahead.
+    constexpr int KPF = SA_ATTN_KPF, VPF = SA_ATTN_VPF;
+    auto lane_id = [&]() {
         // The lane id is made opaque per tile so that the lane-dependent values
-        // below are recomputed (a few ALU ops) instead of being hoisted out of
-        // the tile loop, where they would compete with the accumulators for
-        // registers.
+        // derived from it are recomputed (a few ALU ops) instead of being hoisted
+        // out of the tile loop, where they would compete with the accumulators.
         int ln = lane;
         asm volatile("" : "+v"(ln));
-        const int c = ln & 31, hf = ln >> 5;
+        return ln;
+    };
+    // S^T of the tile in buffer buf; with_copies: the copies of tile tn into
+    // buffer nbuf go out between the q.k steps, and after each MFMA a few VALU
+    // slots are left for independent work (the previous tile's softmax)
+    auto qk = [&](int buf, int tn, int nbuf, auto with_copies, auto &&fill) -> f32x16 {
+        const int ln = lane_id(), c = ln & 31, hf = ln >> 5;
         const uint8_t *tb = tile[buf];
-        const uint32_t myrow = tile_row(tn);
-        const uint32_t vw = vbits[t];
+        uint32_t myrow = kNoRow;
+        SA_LDS uint8_t *dstb = nullptr;
+        if constexpr (decltype(with_copies)::value) {
+            myrow = tile_row(tn);
+            dstb = buffer_base(nbuf);
+        }
         bf16x8 kr[KS];
 #pragma unroll
         for (int u = 0; u < KPF && u < KS; ++u)
             kr[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, u)));
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 + (KPF < KS ? KPF : KS), 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1 + (KPF < KS ? KPF : KS), 0);
         f32x16 s = f32x16{};
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
@@ -293,18 +315,97 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
                 kr[ks + KPF] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, ks + KPF)));
                 __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
             }
-            // copies n with n * KS / DMA_W == ks
-            const int n_lo = (ks * DMA_W + KS - 1) / KS, n_hi = ((ks + 1) * DMA_W + KS - 1) / KS;
+            if constexpr (decltype(with_copies)::value) {
+                // copies n with n * KS / DMA_W == ks
+                const int n_lo = (ks * DMA_W + KS - 1) / KS, n_hi = ((ks + 1) * DMA_W + KS - 1) / KS;
 #pragma unroll
-            for (int n = n_lo; n < n_hi; ++n) {
-                copy(myrow, n, nbuf);
-                __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+                for (int n = n_lo; n < n_hi; ++n) {
+                    copy(myrow, n, dstb);
+                    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
+                }
             }
             s = mfma_32x32x16(kr[ks], qb[ks], s);
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            fill(ks);
         }
-        // V^T operand element e of this lane for step q = (k2, vp): v pair
-        // vh*VW/2 + 32vp + c of token 16k2 + 8hf + e.
+        return s;
+    };
+    auto no_fill = [](int) {};
+    // Weights of tile t from its S^T (branch-free).  Register i of half hf holds
+    // token 16(i/8) + 8hf + i%8.  The reference max is fixed by the first tile
+    // with a valid token for this head (until then O and l are 0, so nothing
+    // needs rescaling) and never moves afterwards: the output accumulators are
+    // only ever touched by the MFMAs.  Weights are exp2(min(s - m, 64)), finite
+    // in fp32 and bf16; a head whose logits outgrow its reference by more than
+    // 64 raises `ovf`, and the split is then recomputed exactly with its true
+    // max (below).
+    // The weights in kSmSteps small steps, so that the steps can sit between the
+    // next tile's q.k MFMAs: steps 0-3 mask, 4-7 reduce the max, 8 crosses the
+    // half-waves and sets the reference, 9-24 exponentiate, 25-32 round to bf16
+    // and sum.  State lives in `SmState`.
+    struct SmState {
+        f32x16 s;
+        float tmax, mref;
+        float p[16];
+        u32x4 w[2];
+        uint32_t vb;
+    };
+    constexpr int kSmSteps = 33;
+    auto sm_begin = [&](SmState &st, const f32x16 &s_in, int t) {
+        st.s = s_in;
+        st.vb = vbits[t] >> (8 * half);
+    };
+    auto sm_step = [&](SmState &st, int step) {
+        if (step < 4) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int i = 4 * step + e;
+                st.s[i] = ((st.vb >> (16 * (i >> 3) + (i & 7))) & 1u) ? st.s[i] : -INFINITY;
+            }
+        } else if (step < 8) {
+            const int i0 = 4 * (step - 4);
+            const float mx = fmaxf(fmaxf(st.s[i0], st.s[i0 + 1]), fmaxf(st.s[i0 + 2], st.s[i0 + 3]));
+            st.tmax = step == 4 ? mx : fmaxf(st.tmax, mx);
+        } else if (step == 8) {
+            // max over the two half-waves (they hold the other 16 tokens)
+            const uint32_t u = __float_as_uint(st.tmax);
+            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+            const float tmax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * a.scale_log2;
+            m = m == -INFINITY ? tmax : m;
+            ovf |= tmax > m + 64.0f;
+            st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every s is -inf
+        } else if (step < 25) {
+            const int i = step - 9;
+            st.p[i] = exp2_hw(fminf(fmaf(st.s[i], a.scale_log2, -st.mref), 64.0f));
+        } else if (step < kSmSteps) {
+            const int j = step - 25, k2 = j >> 2, jj = j & 3;
+            const uint32_t w = pack_bf16x2(st.p[2 * j], st.p[2 * j + 1]);
+            st.w[k2][jj] = w;
+            // the normaliser sums the same bf16-rounded weights the MFMA
+            // multiplies V by, so the output is an exact weighted mean of the
+            // kept rows up to fp32 accumulation
+            l = add_bf16_pair(w, l);
+            le += st.p[2 * j] + st.p[2 * j + 1];
+        }
+    };
+    auto sm_finish = [&](SmState &st, bf16x8 *pb) {
+        pb[0] = as_bf16x8(st.w[0]);
+        pb[1] = as_bf16x8(st.w[1]);
+    };
+    // the whole softmax of one tile, unpipelined
+    auto softmax = [&](const f32x16 &s_in, int t, bf16x8 *pb) {
+        SmState st;
+        sm_begin(st, s_in, t);
+#pragma unroll
+        for (int step = 0; step < kSmSteps; ++step) sm_step(st, step);
+        sm_finish(st, pb);
+    };
+    // O^T += V^T P^T over the tile's two 16-token halves.  V^T operand element e
+    // of this lane for step q = (k2, vp): v pair vh*VW/2 + 32vp + c of token
+    // 16k2 + 8hf + e; the operands of step q + VPF are read while step q multiplies.
+    auto pv = [&](int buf, const bf16x8 *pb) {
+        const int ln = lane_id(), c = ln & 31, hf = ln >> 5;
+        const uint8_t *tb = tile[buf];
         int vbase;
         if constexpr (S::MAIN > 0)
             vbase = 8 * hf * S::MAIN_STRIDE + 2 * vh * VW + 4 * c;
@@ -319,51 +420,10 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
                 d[e] = *reinterpret_cast<const uint32_t *>(tb + vbase + off);
             }
         };
-        constexpr int VPF = 2;  // V operand steps read ahead
         uint32_t vd[2 * VP][8];
 #pragma unroll
         for (int q = 0; q < VPF && q < 2 * VP; ++q) vread(q, vd[q]);
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (VPF < 2 * VP ? VPF : 2 * VP), 0);
-
-        // register i of half hf holds token 16(i/8) + 8hf + i%8
-        if (vw != 0xFFFFFFFFu) {  // a tile with padding (block-uniform)
-            const uint32_t vb = vw >> (8 * hf);
-#pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if (!((vb >> (16 * (i >> 3) + (i & 7))) & 1u)) s[i] = -INFINITY;
-        }
-        float tmax = s[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, s[i]);
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32)) * a.scale_log2;
-        // The reference max is fixed by the first tile with a valid token for this
-        // head (until then O and l are 0, so nothing needs rescaling) and never
-        // moves afterwards: the output accumulators are only ever touched by the
-        // MFMAs.  Weights are exp2(min(s - m, 64)), finite in fp32 and bf16; a head
-        // whose logits outgrow its reference by more than 64 raises `ovf`, and the
-        // split is then recomputed exactly with its true max (below).
-        if (m == -INFINITY) m = tmax;
-        ovf |= tmax > m + 64.0f;
-        const float mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every s is -inf
-        bf16x8 pb[2];
-#pragma unroll
-        for (int k2 = 0; k2 < 2; ++k2) {
-            u32x4 w;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const float p0 = exp2_hw(fminf(fmaf(s[8 * k2 + 2 * jj], a.scale_log2, -mref), 64.0f));
-                const float p1 = exp2_hw(fminf(fmaf(s[8 * k2 + 2 * jj + 1], a.scale_log2, -mref), 64.0f));
-                w[jj] = pack_bf16x2(p0, p1);
-                // the normaliser sums the same bf16-rounded weights the MFMA
-                // multiplies V by, so the output is an exact weighted mean of
-                // the kept rows up to fp32 accumulation
-                l = add_bf16_pair(w[jj], l);
-                le += p0 + p1;
-            }
-            pb[k2] = as_bf16x8(w);
-        }
-        // O^T += V^T P^T, step q = (k2, vp); the operands of step q + VPF are
-        // read while step q multiplies
 #pragma unroll
         for (int q = 0; q < 2 * VP; ++q) {
             if (q + VPF < 2 * VP) {
@@ -383,22 +443,45 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         }
     };
 
-    // Ring of kAttnBuffers tiles.  The prologue issues tiles 0..2; computing
-    // tile t issues tile t+3 into the buffer of tile t-1 (zeros past nt_eff), so
-    // exactly two younger tiles' copies are in flight when tile t is waited
-    // for.  Copies complete in order: "tile t landed" is "at most 2 DMA_W copies
-    // in flight".  The barrier then also certifies that every wave is done with
-    // tile t-1's buffer before it is refilled.  Tiles of padding only are not
-    // computed (block-uniform).
-    static_assert(kAttnBuffers == 4, "wait count below assumes two younger tiles");
+    // Ring of kAttnBuffers = 4 tile buffers, two tiles resident (t for its values,
+    // t+1 for its q.k) and two in flight.  The prologue issues tiles 0..2;
+    // iteration t (which computes S^T of tile t+1) issues tile t+3 into the buffer
+    // of tile t-1 (zeros past nt_eff).  Copies complete in order and every wave
+    // issues DMA_W per tile, so waiting for tile t+1 with only tile t+2 younger is
+    // "at most DMA_W copies in flight" (before the loop: tile 0, two younger).
+    // The barrier then makes every wave's share of tile t+1 visible and certifies
+    // that every wave is done with tile t-1's buffer.  Tiles of padding only are
+    // not computed (block-uniform).
+    static_assert(kAttnBuffers == 4, "the ring below holds two resident and two in-flight tiles");
     constexpr int W2 = 2 * DMA_W < 63 ? 2 * DMA_W : 63;  // clamped: waiting for more is safe
+    constexpr int W1 = DMA_W < 63 ? DMA_W : 63;
 #pragma unroll
     for (int j = 0; j < kAttnBuffers - 1; ++j) issue_tile(j, j);
-    for (int t = 0; t < nt_eff; ++t) {
+    f32x16 s_cur = f32x16{};
+    if (nt_eff > 0) {
         attn_wait_vmcnt<W2>();
         barrier_no_fence();
-        const int tn = t + kAttnBuffers - 1;
-        compute(t, t % kAttnBuffers, tn, tn % kAttnBuffers);
+        s_cur = qk(0, -1, 0, std::false_type{}, no_fill);
+    }
+    for (int t = 0; t < nt_eff; ++t) {
+        bf16x8 pb[2];
+        f32x16 s_nxt = f32x16{};
+        if (t + 1 < nt_eff) {  // (block-uniform)
+            attn_wait_vmcnt<W1>();
+            barrier_no_fence();
+            SmState st;
+            sm_begin(st, s_cur, t);
+            // step ks of tile t's softmax after q.k step ks of tile t+1
+            s_nxt = qk((t + 1) % kAttnBuffers, t + 3, (t + 3) % kAttnBuffers, std::true_type{},
+                       [&](int ks) { sm_step(st, ks); });
+#pragma unroll
+            for (int step = KS; step < kSmSteps; ++step) sm_step(st, step);
+            sm_finish(st, pb);
+        } else {
+            softmax(s_cur, t, pb);
+        }
+        pv(t % kAttnBuffers, pb);
+        s_cur = s_nxt;
     }
     attn_wait_vmcnt<0>();  // the last (zero) copies have landed
 
@@ -413,12 +496,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
             issue_tile(t, 0);
             attn_wait_vmcnt<0>();
             __syncthreads();
-            const uint8_t *tb = tile[0];
-            f32x16 s0 = f32x16{};
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                s0 = mfma_32x32x16(as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(col, half, ks))),
-                                   qb[ks], s0);
+            const f32x16 s0 = qk(0, -1, 0, std::false_type{}, no_fill);
             const uint32_t vb = vbits[t] >> (8 * half);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
@@ -438,8 +516,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
             issue_tile(t, 0);
             attn_wait_vmcnt<0>();
             __syncthreads();
-            compute(t, 0, -1, 1);  // s <= m now, so no weight is clamped; no copies ahead (zeros into buffer 1)
-            attn_wait_vmcnt<0>();
+            bf16x8 pb[2];
+            softmax(qk(0, -1, 0, std::false_type{}, no_fill), t, pb);  // s <= m now, so no weight is clamped
+            pv(0, pb);
             __syncthreads();
         }
     }

@@ -75,7 +75,7 @@ __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::
 __device__ __forceinline__ SA_LDS void *opaque_lds(SA_LDS void *p)
 {
     uint32_t a = (uint32_t)(uintptr_t)p;
-    asm volatile("" : "+s"(a));
+    asm("" : "+s"(a));  // (not volatile: no scheduling barrier)
     return (SA_LDS void *)(uintptr_t)a;
 }
 
