@@ -19,9 +19,11 @@
 // gfx950 mapping.  One workgroup = one (row, split, value half); wave w owns heads
 // 32w..32w+31 and keeps their query rows in registers for the whole split.  Per
 // tile of 32 kept tokens:
-//   * the 32 latent rows are copied HBM -> LDS by the LDS-DMA path
-//     (global_load_lds_dwordx4), 16-byte pieces XOR-swizzled by token so that
-//     MFMA operand reads do not collide on LDS banks; a ring of 4 tile buffers
+//   * the 32 latent rows are copied HBM -> LDS by buffer-form LDS-DMA, one
+//     resource per token row: a 64-lane copy of its first 1 KiB and an 8-lane
+//     copy of its 128-byte tail; the main rows' 16-byte pieces are XOR-swizzled
+//     by token (through the copy's per-lane source offsets) so that MFMA
+//     operand reads do not collide on LDS banks; a ring of 4 tile buffers
 //     keeps 3 tiles' copies in flight while one tile is computed;
 //   * the query of 32 heads (QK = 576: 144 registers per lane) and the 32 x 512
 //     fp32 output accumulators (256 registers) of one wave do not fit in the
@@ -37,9 +39,8 @@
 //   * the S^T accumulator already has the register layout of the B operand of
 //     O^T[v][head] += V^T[v][token] . P^T[token][head]: P is only rounded to bf16.
 //     The softmax denominator sums the same rounded P.
-//     The V^T operand is gathered from LDS as dwords (two adjacent v of one
-//     token) and split with byte permutes into an "even v" and an "odd v"
-//     operand, so every LDS byte read is used.
+//     The V^T operand comes straight from the token-major tile through
+//     transposed LDS reads (ds_read_b64_tr_b16), four tokens per read.
 #pragma once
 
 #include "device_common.hpp"
@@ -68,10 +69,13 @@ struct AttnArgs {
 };
 
 #ifndef SA_ATTN_KPF
-#define SA_ATTN_KPF 8  // K operand steps read ahead of their MFMA
+#define SA_ATTN_KPF 6  // K operand steps read ahead of their MFMA
 #endif
 #ifndef SA_ATTN_VPF
 #define SA_ATTN_VPF 4  // V operand steps read ahead of their MFMAs
+#endif
+#ifndef SA_ATTN_FENCE
+#define SA_ATTN_FENCE 1  // 1: a scheduling fence closes every MFMA step
 #endif
 
 constexpr int kAttnBuffers = 4;  // tile ring: kAttnBuffers - 1 tiles in flight while one is computed
@@ -89,24 +93,31 @@ struct AttnShape {
     static constexpr int KS = QK / 16;                   // MFMA steps of q.k
     static constexpr int VSPLIT = V > 256 ? 2 : 1;       // workgroups sharing one (row, split), by v range
     static constexpr int VW = V / VSPLIT;                // v columns per workgroup
-    static constexpr int VP = VW / 64;                   // 64-wide v groups (even + odd tiles)
+    static constexpr int NVT = VW / 32;                  // 32-column output tiles per wave
     static constexpr int PIECES = QK / 8;                // 16-byte pieces per latent row
     // LDS image of a 32-token tile.  Main rows: pieces 0..63 of each token
-    // (one 1 KiB copy per token), MAIN_STRIDE bytes apart; the extra 16 bytes
-    // move each token to the next 16-byte bank group.  Tail: the remaining
-    // pieces, stored piece-major ([piece][32 tokens]), so one copy moves two
-    // pieces of all 32 tokens.  Rows shorter than 64 pieces live in the tail only.
+    // (one 1 KiB copy per token), MAIN_STRIDE bytes apart, piece p of token t
+    // stored at position p ^ main_swizzle(t).  Tail: the remaining 8 pieces
+    // (128 bytes) of each token, TAIL_STRIDE bytes apart (the extra 16 bytes
+    // move consecutive tokens to different 16-byte bank groups).  Rows shorter
+    // than 64 pieces live in the tail only.
     static constexpr int MAIN = PIECES >= 64 ? 64 : 0;
     static constexpr int TAIL = PIECES - MAIN;
-    static constexpr int MAIN_STRIDE = MAIN * 16 + 16;
-    static constexpr int TAIL_BASE = MAIN ? 32 * MAIN_STRIDE : 0;
-    static constexpr int TILE_BYTES = TAIL_BASE + TAIL * 32 * 16;
-    static constexpr int DMA_MAIN = MAIN ? 32 : 0;       // main-row copies per tile
-    static constexpr int DMA_TAIL = TAIL / 2;            // tail copies per tile
-    static constexpr int DMA_PER_TILE = DMA_MAIN + DMA_TAIL;
-    static_assert(QK % 16 == 0 && VW % 64 == 0 && V <= QK, "shape family");
-    static_assert(TAIL % 2 == 0 && (MAIN == 0 || V <= 8 * MAIN), "value columns must lie in the main rows");
+    static constexpr int MAIN_STRIDE = MAIN * 16;
+    static constexpr int TAIL_STRIDE = TAIL * 16 + 16;
+    static constexpr int TAIL_BASE = 32 * MAIN_STRIDE;
+    static constexpr int TILE_BYTES = TAIL_BASE + 32 * TAIL_STRIDE;
+    static constexpr int COPIES_PER_TOKEN = (MAIN ? 1 : 0) + 1;  // main row, tail
+    static_assert(QK % 16 == 0 && VW % 32 == 0 && V <= QK, "shape family");
+    static_assert(TAIL == 8, "the tail is one 8-lane copy of 128 bytes");
+    static_assert(V <= 8 * (MAIN ? MAIN : TAIL), "value columns must lie in one row region");
 };
+
+// Position swizzle of the main rows: piece p of tile token t sits at position
+// p ^ main_swizzle(t) (the low two bit pairs of t, exchanged).  Then a K
+// operand read (16 tokens, one piece each) and a transposed V read (4 tokens x
+// 4 consecutive pieces per 32 lanes) both touch 16 distinct 16-byte bank groups.
+__device__ __forceinline__ constexpr int main_swizzle(int t) { return 4 * (t & 3) + ((t >> 2) & 3); }
 
 // Row rho of a tile's S^T accumulator holds tile token row_token(rho) (bits 2
 // and 3 swapped).  Then the two half-waves of a V^T operand read tokens 8
@@ -128,8 +139,6 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float l)
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2, w), __builtin_bit_cast(b2, 0x3F803F80u), l, false);
 }
 
-// Scheduling-group masks of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008, kSchedVmemRead = 0x020, kSchedDsRead = 0x100, kSchedValu = 0x002;
 
 // Workgroup id -> logical block.  Workgroups are dealt to the 8 XCDs in turn
 // (id mod 8); this map gives each XCD a contiguous range of logical blocks, so
@@ -147,7 +156,7 @@ template <int QK, int V, int NW>
 __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
 {
     using S = AttnShape<QK, V>;
-    constexpr int KS = S::KS, VP = S::VP, VW = S::VW;
+    constexpr int KS = S::KS, VW = S::VW;
     __shared__ __attribute__((aligned(1024))) uint8_t tile[kAttnBuffers][S::TILE_BYTES];
     __shared__ uint32_t rows[kAttnMaxSplitTokens];
     __shared__ uint32_t vbits[kAttnMaxSplitTokens / 32];
@@ -214,12 +223,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         last_tile = -1;
         overflow_flag = 0;
     }
-    f32x16 oe[VP], oo[VP];
+    f32x16 oacc[S::NVT];  // O^T tile vt: columns 32vt.. of this block's value range
 #pragma unroll
-    for (int vp = 0; vp < VP; ++vp) {
-        oe[vp] = f32x16{};
-        oo[vp] = f32x16{};
-    }
+    for (int vt = 0; vt < S::NVT; ++vt) oacc[vt] = f32x16{};
     // m: reference max (log2 units); l: sum of the bf16-rounded weights (output
     // normaliser); le: sum of the unrounded weights (log-sum-exp)
     float m = -INFINITY, l = 0.0f, le = 0.0f;
@@ -230,15 +236,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     __syncthreads();
     const int nt_eff = last_tile + 1;  // tiles after the last valid token are skipped
 
-    // Copies.  A tile is DMA_PER_TILE wave-wide 16-byte-per-lane copies: copy
-    // i < DMA_MAIN moves token i's main row (lane l: piece l, the row from
-    // v_readlane), tail copy j moves pieces MAIN + 2j and MAIN + 2j + 1 of all 32
-    // tokens (lane l: token l % 32, its own row).  Padding tokens, and tiles at
-    // or past nt_eff, copy zeros.  Wave w issues copies w, w + NW, ... and
-    // exactly DMA_W of them per tile (a surplus repeats the last copy, which
-    // writes the same bytes again), so the copy counter of every wave advances
-    // by DMA_W per tile.  `myrow` is the row of token lane % 32 of the tile.
-    constexpr int DMA_W = (S::DMA_PER_TILE + NW - 1) / NW;
+    // Copies.  Wave w copies tokens w, w + NW, ... of a tile, TOK_W of them (a
+    // surplus repeats token 31, which writes the same bytes again).  Per token:
+    // a buffer resource over its latent row (a zero row for padding tokens and
+    // for tiles at or past nt_eff), then the main-row copy (64 lanes x 16 bytes)
+    // and the tail copy (lanes 0..7 x 16 bytes), both buffer-form LDS-DMA.  The
+    // memory counter of every wave thus advances by DMA_W per tile.  `myrow` is
+    // the row of token lane % 32 of the tile.
+    constexpr int TOK_W = (32 + NW - 1) / NW;
+    constexpr int DMA_W = TOK_W * S::COPIES_PER_TOKEN;
     const uint64_t kv_addr = reinterpret_cast<uint64_t>(a.kv);
     uint64_t zero_addr = reinterpret_cast<uint64_t>(kZeroLatentRow);
     asm volatile("" : "+s"(zero_addr));  // keep the address in registers, out of the copy code
@@ -248,32 +254,34 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     };
     // `dstb`: the LDS base of the buffer, from opaque_lds (the tile reads that
     // follow use other buffers, and the ring waits order the rest)
-    auto copy = [&](uint32_t myrow, int n, SA_LDS uint8_t *dstb) {
-        const int ii = min(wave + NW * n, S::DMA_PER_TILE - 1);  // wave-uniform
-        const bool is_main = ii < S::DMA_MAIN;
-        const int j = ii - S::DMA_MAIN;
-        const uint32_t row = is_main ? lane_read(myrow, min(ii, 31)) : myrow;
+    auto copy_token = [&](uint32_t myrow, int n, SA_LDS uint8_t *dstb) {
+        const int ii = min(wave + NW * n, 31);  // wave-uniform
+        const uint32_t row = lane_read(myrow, ii);
         // (a mask blend rather than a conditional, so no branch splits the q.k steps)
         const uint64_t keep = (uint64_t)0 - (uint64_t)(row != kNoRow);
         const uint64_t base = ((kv_addr + (uint64_t)row * (QK * 2)) & keep) | (zero_addr & ~keep);
-        const uint32_t off = is_main ? lane * 16 : (S::MAIN + 2 * j + (lane >> 5)) * 16;
-        const int dst = is_main ? ii * S::MAIN_STRIDE : S::TAIL_BASE + j * 1024;
-        dma16_to_lds(reinterpret_cast<const void *>(base + off), dstb + dst);
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const void *>(base), QK * 2);
+        if constexpr (S::MAIN > 0)  // lane i fetches the piece stored at position i
+            buf_dma16_to_lds(rs, (lane * 16) ^ (16 * main_swizzle(ii)), dstb + ii * S::MAIN_STRIDE);
+        if (lane < 8) buf_dma16_to_lds(rs, S::MAIN * 16 + lane * 16, dstb + S::TAIL_BASE + ii * S::TAIL_STRIDE);
     };
     auto buffer_base = [&](int buf) { return (SA_LDS uint8_t *)opaque_lds((SA_LDS uint8_t *)&tile[buf][0]); };
     auto issue_tile = [&](int tn, int buf) {
         const uint32_t myrow = tile_row(tn);
         SA_LDS uint8_t *dstb = buffer_base(buf);
-#pragma unroll 9
-        for (int n = 0; n < DMA_W; ++n) copy(myrow, n, dstb);
+#pragma unroll
+        for (int n = 0; n < TOK_W; ++n) copy_token(myrow, n, dstb);
     };
 
     // LDS byte offset of this lane's K operand of step ks (S row c holds token
     // row_token(c); the lane supplies its pieces 2ks + half).
+    // (main pieces 2ks + hf at position (2ks + hf) ^ swizzle: the swizzle only
+    // flips bits 0..3 of the piece index)
     auto k_offset = [&](int c, int hf, int ks) {
         const int tok = row_token(c);
-        return 2 * ks < S::MAIN ? tok * S::MAIN_STRIDE + 16 * hf + 32 * ks
-                                : S::TAIL_BASE + (2 * ks - S::MAIN + hf) * 512 + 16 * tok;
+        return 2 * ks < S::MAIN
+                   ? tok * S::MAIN_STRIDE + ((32 * (ks & 7) + 16 * hf) ^ (16 * main_swizzle(tok))) + 256 * (ks >> 3)
+                   : S::TAIL_BASE + tok * S::TAIL_STRIDE + 16 * (2 * ks - S::MAIN + hf);
     };
 
     // Per tile: S^T = K Q^T (qk), the softmax weights of S^T (softmax), then
@@ -291,42 +299,37 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         asm volatile("" : "+v"(ln));
         return ln;
     };
-    // S^T of the tile in buffer buf; with_copies: the copies of tile tn into
-    // buffer nbuf go out between the q.k steps, and after each MFMA a few VALU
-    // slots are left for independent work (the previous tile's softmax)
-    auto qk = [&](int buf, int tn, int nbuf, auto with_copies, auto &&fill) -> f32x16 {
+    // S^T of the tile in buffer buf; with_copies: the main copies of the tile
+    // whose lane rows are `myrow` go into buffer nbuf between the q.k steps, and
+    // after each MFMA a few VALU slots are left for independent work (the
+    // previous tile's softmax)
+    auto qk = [&](int buf, uint32_t myrow, int nbuf, auto with_copies, auto &&fill) -> f32x16 {
         const int ln = lane_id(), c = ln & 31, hf = ln >> 5;
         const uint8_t *tb = tile[buf];
-        uint32_t myrow = kNoRow;
         SA_LDS uint8_t *dstb = nullptr;
-        if constexpr (decltype(with_copies)::value) {
-            myrow = tile_row(tn);
-            dstb = buffer_base(nbuf);
-        }
+        if constexpr (decltype(with_copies)::value) dstb = buffer_base(nbuf);
         bf16x8 kr[KS];
 #pragma unroll
         for (int u = 0; u < KPF && u < KS; ++u)
             kr[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, u)));
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1 + (KPF < KS ? KPF : KS), 0);
         f32x16 s = f32x16{};
+        // Step ks: read the operand of step ks + KPF, multiply, issue this
+        // step's copies, then the caller's VALU work.
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
-            if (ks + KPF < KS) {
+            if (ks + KPF < KS)
                 kr[ks + KPF] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, ks + KPF)));
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-            }
-            if constexpr (decltype(with_copies)::value) {
-                // copies n with n * KS / DMA_W == ks
-                const int n_lo = (ks * DMA_W + KS - 1) / KS, n_hi = ((ks + 1) * DMA_W + KS - 1) / KS;
-#pragma unroll
-                for (int n = n_lo; n < n_hi; ++n) {
-                    copy(myrow, n, dstb);
-                    __builtin_amdgcn_sched_group_barrier(kSchedVmemRead, 1, 0);
-                }
-            }
             s = mfma_32x32x16(kr[ks], qb[ks], s);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if constexpr (decltype(with_copies)::value) {
+                // tokens n with n * KS / TOK_W == ks
+                const int n_lo = (ks * TOK_W + KS - 1) / KS, n_hi = ((ks + 1) * TOK_W + KS - 1) / KS;
+#pragma unroll
+                for (int n = n_lo; n < n_hi; ++n) copy_token(myrow, n, dstb);
+            }
             fill(ks);
+#if SA_ATTN_FENCE
+            __builtin_amdgcn_sched_barrier(0);
+#endif
         }
         return s;
     };
@@ -400,46 +403,51 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         for (int step = 0; step < kSmSteps; ++step) sm_step(st, step);
         sm_finish(st, pb);
     };
-    // O^T += V^T P^T over the tile's two 16-token halves.  V^T operand element e
-    // of this lane for step q = (k2, vp): v pair vh*VW/2 + 32vp + c of token
-    // 16k2 + 8hf + e; the operands of step q + VPF are read while step q multiplies.
+    // O^T += V^T P^T over the tile's two 16-token halves: step q = (k2, vt)
+    // multiplies output tile vt (value columns 32vt..32vt+31 of this block's
+    // range) by token half k2.  The V^T operand of lane (c, hf) is column c of
+    // tokens 16k2 + 8hf + 0..7, read as two transposed 4-token reads
+    // (ds_read_b64_tr_b16: within each 16 lanes, lane 4a + b receives element b
+    // of the 8-byte chunks addressed by lanes a, a + 4, a + 8, a + 12).  So lane
+    // L addresses token 16k2 + 8hf + 4s + ((L >> 2) & 3), columns 32vt + 16((L >> 4)
+    // & 1) + 4(L & 3)..+3.  The operands of step q + VPF are read while step q
+    // multiplies.
     auto pv = [&](int buf, const bf16x8 *pb) {
-        const int ln = lane_id(), c = ln & 31, hf = ln >> 5;
-        const uint8_t *tb = tile[buf];
-        int vbase;
+        const int ln = lane_id();
+        const int j = (ln >> 2) & 3, a4 = ln & 3, g1 = (ln >> 4) & 1, hfv = ln >> 5;
+        const int xq = 2 * g1 + (a4 >> 1);  // piece within the 32-column tile
+        SA_LDS uint8_t *tb = (SA_LDS uint8_t *)&tile[buf][0];
+        // lane-constant part of the address, and the step part XORed into it
+        int lb;
         if constexpr (S::MAIN > 0)
-            vbase = 8 * hf * S::MAIN_STRIDE + 2 * vh * VW + 4 * c;
+            lb = (8 * hfv + j) * S::MAIN_STRIDE + 8 * (a4 & 1) + 64 * j + 16 * (xq ^ (2 * hfv)) + 16 * (vh * VW / 8);
         else
-            vbase = S::TAIL_BASE + (c >> 2) * 512 + (c & 3) * 4 + 128 * hf + vh * VW * 64;
-        auto vread = [&](int q, uint32_t *d) {
-            const int k2 = q / VP, vp = q % VP;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const int off = S::MAIN > 0 ? (16 * k2 + e) * S::MAIN_STRIDE + 128 * vp
-                                            : (16 * k2 + e) * 16 + 4096 * vp;
-                d[e] = *reinterpret_cast<const uint32_t *>(tb + vbase + off);
-            }
+            lb = S::TAIL_BASE + (8 * hfv + j) * S::TAIL_STRIDE + 8 * (a4 & 1) + 16 * xq + 16 * (vh * VW / 8);
+        auto vaddr = [&](int k2, int sh, int vt) -> int {
+            if constexpr (S::MAIN > 0)
+                return (lb ^ (64 * (vt & 3) + 16 * sh)) + (16 * k2 + 4 * sh) * S::MAIN_STRIDE + 256 * (vt >> 2);
+            else
+                return lb + (16 * k2 + 4 * sh) * S::TAIL_STRIDE + 64 * vt;
         };
-        uint32_t vd[2 * VP][8];
+        typedef short s16x4 __attribute__((ext_vector_type(4)));
+        auto vread = [&](int q) -> bf16x8 {
+            const int k2 = q / S::NVT, vt = q % S::NVT;
+            const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS s16x4 *)(tb + vaddr(k2, 0, vt)));
+            const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS s16x4 *)(tb + vaddr(k2, 1, vt)));
+            return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        };
+        constexpr int NQ = 2 * S::NVT;
+        bf16x8 vd[NQ];
 #pragma unroll
-        for (int q = 0; q < VPF && q < 2 * VP; ++q) vread(q, vd[q]);
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8 * (VPF < 2 * VP ? VPF : 2 * VP), 0);
+        for (int q = 0; q < VPF && q < NQ; ++q) vd[q] = vread(q);
 #pragma unroll
-        for (int q = 0; q < 2 * VP; ++q) {
-            if (q + VPF < 2 * VP) {
-                vread(q + VPF, vd[q + VPF]);
-                __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-            }
-            const int k2 = q / VP, vp = q % VP;
-            u32x4 ev, od;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                ev[jj] = __builtin_amdgcn_perm(vd[q][2 * jj + 1], vd[q][2 * jj], 0x05040100u);
-                od[jj] = __builtin_amdgcn_perm(vd[q][2 * jj + 1], vd[q][2 * jj], 0x07060302u);
-            }
-            oe[vp] = mfma_32x32x16(as_bf16x8(ev), pb[k2], oe[vp]);
-            oo[vp] = mfma_32x32x16(as_bf16x8(od), pb[k2], oo[vp]);
-            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+        for (int q = 0; q < NQ; ++q) {
+            if (q + VPF < NQ) vd[q + VPF] = vread(q + VPF);
+            const int k2 = q / S::NVT, vt = q % S::NVT;
+            oacc[vt] = mfma_32x32x16(vd[q], pb[k2], oacc[vt]);
+#if SA_ATTN_FENCE
+            __builtin_amdgcn_sched_barrier(0);
+#endif
         }
     };
 
@@ -461,18 +469,19 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     if (nt_eff > 0) {
         attn_wait_vmcnt<W2>();
         barrier_no_fence();
-        s_cur = qk(0, -1, 0, std::false_type{}, no_fill);
+        s_cur = qk(0, kNoRow, 0, std::false_type{}, no_fill);
     }
     for (int t = 0; t < nt_eff; ++t) {
         bf16x8 pb[2];
         f32x16 s_nxt = f32x16{};
         if (t + 1 < nt_eff) {  // (block-uniform)
+            const uint32_t myrow = tile_row(t + 3);
             attn_wait_vmcnt<W1>();
             barrier_no_fence();
             SmState st;
             sm_begin(st, s_cur, t);
             // step ks of tile t's softmax after q.k step ks of tile t+1
-            s_nxt = qk((t + 1) % kAttnBuffers, t + 3, (t + 3) % kAttnBuffers, std::true_type{},
+            s_nxt = qk((t + 1) % kAttnBuffers, myrow, (t + 3) % kAttnBuffers, std::true_type{},
                        [&](int ks) { sm_step(st, ks); });
 #pragma unroll
             for (int step = KS; step < kSmSteps; ++step) sm_step(st, step);
@@ -496,7 +505,7 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
             issue_tile(t, 0);
             attn_wait_vmcnt<0>();
             __syncthreads();
-            const f32x16 s0 = qk(0, -1, 0, std::false_type{}, no_fill);
+            const f32x16 s0 = qk(0, kNoRow, 0, std::false_type{}, no_fill);
             const uint32_t vb = vbits[t] >> (8 * half);
 #pragma unroll
             for (int i = 0; i < 16; ++i)
@@ -508,16 +517,13 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         l = 0.0f;
         le = 0.0f;
 #pragma unroll
-        for (int vp = 0; vp < VP; ++vp) {
-            oe[vp] = f32x16{};
-            oo[vp] = f32x16{};
-        }
+        for (int vt = 0; vt < S::NVT; ++vt) oacc[vt] = f32x16{};
         for (int t = 0; t < nt_eff; ++t) {
             issue_tile(t, 0);
             attn_wait_vmcnt<0>();
             __syncthreads();
             bf16x8 pb[2];
-            softmax(qk(0, -1, 0, std::false_type{}, no_fill), t, pb);  // s <= m now, so no weight is clamped
+            softmax(qk(0, kNoRow, 0, std::false_type{}, no_fill), t, pb);  // s <= m now, so no weight is clamped
             pv(0, pb);
             __syncthreads();
         }
@@ -530,15 +536,16 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
         const int64_t obase = ((int64_t)r * a.num_heads + head) * V + vh * VW;
 #pragma unroll
-        for (int vp = 0; vp < VP; ++vp)
+        for (int vt = 0; vt < S::NVT; ++vt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int v = 64 * vp + 2 * acc_row(i, half);
-                const float e0 = oe[vp][i] * inv, e1 = oo[vp][i] * inv;
+            for (int i = 0; i < 16; i += 4) {
+                const int v = 32 * vt + acc_row(i, half);  // registers i..i+3: columns v..v+3
+                const f32x4 o = f32x4{oacc[vt][i], oacc[vt][i + 1], oacc[vt][i + 2], oacc[vt][i + 3]} * inv;
                 if (a.out_bf16)
-                    reinterpret_cast<uint32_t *>(a.out)[(obase + v) >> 1] = pack_bf16x2(e0, e1);
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(a.out) + obase + v) =
+                        u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
                 else
-                    *reinterpret_cast<f32x2 *>(reinterpret_cast<float *>(a.out) + obase + v) = f32x2{e0, e1};
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + obase + v) = o;
             }
         if (a.lse && half == 0 && vh == 0)
             a.lse[(int64_t)r * a.num_heads + head] = lt > 0.0f ? (m + log2f(lte)) * 0.69314718055994531f : -INFINITY;
@@ -546,12 +553,11 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         const int64_t pbase = (((int64_t)r * a.splits + split) * a.num_heads + head);
         float *po = a.part_o + pbase * V + vh * VW;
 #pragma unroll
-        for (int vp = 0; vp < VP; ++vp)
+        for (int vt = 0; vt < S::NVT; ++vt)
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int v = 64 * vp + 2 * acc_row(i, half);
-                *reinterpret_cast<f32x2 *>(po + v) = f32x2{oe[vp][i], oo[vp][i]};
-            }
+            for (int i = 0; i < 16; i += 4)
+                *reinterpret_cast<f32x4 *>(po + 32 * vt + acc_row(i, half)) =
+                    f32x4{oacc[vt][i], oacc[vt][i + 1], oacc[vt][i + 2], oacc[vt][i + 3]};
         if (half == 0 && vh == 0) *reinterpret_cast<f32x4 *>(a.part_ml + pbase * 4) = f32x4{m, lt, lte, 0.0f};
     }
 }

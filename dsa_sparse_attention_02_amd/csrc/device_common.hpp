@@ -38,6 +38,13 @@ __device__ __forceinline__ u32x4 load16(const void *p)
     return *reinterpret_cast<const u32x4 *>(p);
 }
 
+// 16-byte load from a global-memory address held as an integer (the address
+// space is explicit, so the compiler emits a global, not a flat, load)
+__device__ __forceinline__ u32x4 load16_global(uint64_t addr)
+{
+    return *reinterpret_cast<const __attribute__((address_space(1))) u32x4 *>(addr);
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     typedef float f2 __attribute__((ext_vector_type(2)));
@@ -61,6 +68,27 @@ __device__ __forceinline__ void dma16_to_lds(const void *src, SA_LDS void *lds_w
 __device__ __forceinline__ void dma16_to_lds_stream(const void *src, SA_LDS void *lds_wave_base)
 {
     __builtin_amdgcn_global_load_lds(src, lds_wave_base, 16, 0, 2 /* nt */);
+}
+
+// Buffer resource word 3 for gfx9-family raw buffers (32-bit data format; the
+// dword-count loads below ignore the format).
+constexpr int kBufferWord3 = 0x00020000;
+
+// Buffer resource over `bytes` bytes at `base` (wave-uniform: the resource
+// lives in scalar registers).  Reads through it at or past `bytes` return zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, kBufferWord3);
+}
+
+// The 16-byte-per-lane LDS-DMA copy in its buffer (MUBUF) form: each active
+// lane i reads resource offset voff_i (32-bit) and writes lds_wave_base + 16*i.
+// The compiler counts LDS reads exactly around this form, whereas after the
+// global (FLAT-encoded) form it assumes the copy may still be pending on the
+// LDS counter and waits for every LDS read in flight at each later use of one.
+__device__ __forceinline__ void buf_dma16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t voff, SA_LDS void *lds_wave_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, 0, 0, 0);
 }
 
 // s_barrier without the memory fence __syncthreads adds (which would wait for
