@@ -91,6 +91,12 @@ __device__ __forceinline__ void buf_dma16_to_lds(__amdgpu_buffer_rsrc_t r, uint3
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, 0, 0, 0);
 }
 
+// The same with the non-temporal cache policy (data read once).
+__device__ __forceinline__ void buf_dma16_to_lds_stream(__amdgpu_buffer_rsrc_t r, uint32_t voff, SA_LDS void *lds_wave_base)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds_wave_base, 16, voff, 0, 0, 2 /* nt */);
+}
+
 // s_barrier without the memory fence __syncthreads adds (which would wait for
 // every LDS-DMA copy in flight); the asm memory clobber keeps the compiler from
 // moving memory operations across it.

@@ -50,6 +50,9 @@ __device__ __forceinline__ void wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // store instructions every scored tile issues (its scores); the tile ranges are
 // flushed once per 16 tiles, and such an extra store only lengthens a wait
 constexpr int kScanStores = 1;
@@ -143,16 +146,24 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
             return 0;
         }
     };
+    // The copies of a tile.  With BLOCK_TILE its 32 rows are contiguous: one
+    // buffer resource over them, buffer-form LDS-DMA (after the global form the
+    // compiler would drain every LDS read in flight at each later wait on one).
     auto issue = [&](int t, int stage, int64_t base) {
         const int s0 = t * 32;
+        [[maybe_unused]] __amdgpu_buffer_rsrc_t rs;
+        if constexpr (BLOCK_TILE) rs = buffer_rsrc(idx_k + base * IDX_DIM, TILE);
 #pragma unroll
         for (int i = 0; i < DMA; ++i) {
             int s = s0 + dma_r[i];
             s = s < ctx ? s : ctx - 1;  // rows past the context re-read the last key; never scored
-            int64_t row;
-            if constexpr (BLOCK_TILE) row = base + (s - s0);
-            else row = ((int64_t)tbl[s >> bs_log2] << bs_log2) | (s & bmask);
-            dma16_to_lds_stream(idx_k + row * IDX_DIM + dma_piece[i] * 8, (SA_LDS void *)(my + stage * TILE + i * 1024));
+            SA_LDS void *dst = (SA_LDS void *)(my + stage * TILE + i * 1024);
+            if constexpr (BLOCK_TILE) {
+                buf_dma16_to_lds_stream(rs, (s - s0) * (IDX_DIM * 2) + dma_piece[i] * 16, dst);
+            } else {
+                const int64_t row = ((int64_t)tbl[s >> bs_log2] << bs_log2) | (s & bmask);
+                dma16_to_lds_stream(idx_k + row * IDX_DIM + dma_piece[i] * 8, dst);
+            }
         }
     };
 
@@ -180,6 +191,10 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
                 wr[t][i] = hj < idx_heads ? idx_w[(int64_t)b * idx_heads + hj] : 0.0f;
             }
         }
+        // A wait the compiler sees: the tile loop below then finds the queries
+        // and weights complete and adds no memory wait of its own (which, next
+        // to the LDS-DMA copies, it could only make a full drain on every tile).
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
         // Ring waits.  Every tile issues DMA copies and then kScanStores stores (its
         // scores and its range), all counted by vmcnt, which completes in issue
@@ -309,14 +324,15 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
         const int s0 = ktc * 32;
         int s = s0 + dr;
         s = s < nkeys ? s : nkeys - 1;  // rows past the last visible key re-read it; never scored
-        int64_t row;
-        if constexpr (BLOCK_TILE) {
+        SA_LDS void *dst = opaque_lds((SA_LDS void *)&ring[kt % R][64 * wave * 16]);
+        if constexpr (BLOCK_TILE) {  // the tile's rows are contiguous: one buffer resource (see the decode scan)
             const int bi = __builtin_amdgcn_readfirstlane(s0 >> bs_log2);
-            row = (((int64_t)((ctbl_t)(uintptr_t)block_table)[bi]) << bs_log2) + (s & bmask);
+            const int64_t row0 = (((int64_t)((ctbl_t)(uintptr_t)block_table)[bi]) << bs_log2) + (s0 & bmask);
+            buf_dma16_to_lds(buffer_rsrc(idx_k + row0 * IDX_DIM, TILE), (s - s0) * (IDX_DIM * 2) + dpiece * 16, dst);
         } else {
-            row = ((int64_t)block_table[s >> bs_log2] << bs_log2) | (s & bmask);
+            const int64_t row = ((int64_t)block_table[s >> bs_log2] << bs_log2) | (s & bmask);
+            dma16_to_lds(idx_k + row * IDX_DIM + dpiece * 8, dst);
         }
-        dma16_to_lds(idx_k + row * IDX_DIM + dpiece * 8, opaque_lds((SA_LDS void *)&ring[kt % R][64 * wave * 16]));
     };
     // the ring is issued first: its copies overlap the query loads below
 #pragma unroll
