@@ -194,6 +194,27 @@ __device__ void topk_radix_row(TopkShared &sh, const float *__restrict__ sr, int
     }
 }
 
+// 5. The kept positions (set bits of the bitmap) in ascending order: contiguous
+// words per thread, a block scan of their bit counts.
+__device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int32_t *o, int tid)
+{
+    const int per = (words + kTopkThreads - 1) / kTopkThreads;
+    const int w0 = tid * per, w1 = min(words, w0 + per);
+    uint32_t cnt = 0;
+    for (int w = w0; w < w1; ++w) cnt += __popc(sh.bitmap[w]);
+    uint32_t tot;
+    uint32_t pos = block_inclusive_scan(cnt, sh.wsum, &tot) - cnt;
+    for (int w = w0; w < w1; ++w) {
+        uint32_t bits = sh.bitmap[w];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (pos < (uint32_t)k) o[pos] = w * 32 + b;
+            ++pos;
+        }
+    }
+}
+
 // Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
 // else n = n_base + r + 1 (prefill row at position n_base + r).  tile_mm holds
 // score ranges (min, max) at row stride mm_stride: one per 32-key tile
@@ -303,31 +324,50 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
             }
         }
     };
-    // wave-uniform loop: a wave covers U x 256 keys per iteration (U loads in flight)
-    for (int wb = 4 * 64 * wv; wb < n; wb += 4 * U * kTopkThreads) {
+    // Wave-uniform loops: a wave covers U x 256 keys per iteration.  The main
+    // loop's iterations lie wholly inside the row, so its U loads carry no
+    // bounds checks and are all in flight together; the rest goes key by key.
+    const int wEnd = n - 4 * (U - 1) * kTopkThreads - 4 * 64;  // last full iteration starts before this
+    int wb = 4 * 64 * wv;
+    for (; wb < wEnd; wb += 4 * U * kTopkThreads) {
         f32x4 v[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int i0 = wb + u * 4 * kTopkThreads + 4 * lane;
-            v[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-            if (i0 + 3 < n) {
-                v[u] = *reinterpret_cast<const f32x4 *>(sr + i0);
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (i0 + e < n) v[u][e] = sr[i0 + e];
-            }
-        }
+        for (int u = 0; u < U; ++u) v[u] = *reinterpret_cast<const f32x4 *>(sr + wb + u * 4 * kTopkThreads + 4 * lane);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int i0 = wb + u * 4 * kTopkThreads + 4 * lane;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) visit(v[u][e], i0 + e, i0 + e < n);
+            for (int e = 0; e < 4; ++e) visit(v[u][e], i0 + e, true);
         }
     }
+    for (; wb < n; wb += 4 * U * kTopkThreads)
+        for (int u = 0; u < U; ++u) {
+            const int i0 = wb + u * 4 * kTopkThreads + 4 * lane;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const bool ok = i0 + e < n;
+                visit(ok ? sr[i0 + e] : 0.0f, i0 + e, ok);
+            }
+        }
     __syncthreads();
 
-    // 4. the need best candidates: bitonic sort, descending by (key, -position)
+    // 4. the need best candidates, by (key, -position) descending.  Up to 64 of
+    // them: wave 0 ranks each against all (lane i holds candidate i); more: a
+    // bitonic sort over the block.
+    if (m <= 64) {  // block-uniform
+        if (wv == 0) {
+            const uint64_t mine = lane < (int)m ? sh.cand[lane] : 0;
+            int rank = 0;  // candidates ahead of mine (keys are distinct: positions differ)
+            for (int j = 0; j < (int)m; ++j) rank += __shfl(mine, j) > mine;
+            if (lane < (int)m && rank < (int)need) {
+                const int pos = (int)(0xFFFFFFFFu - (uint32_t)mine);
+                atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
+            }
+        }
+        __syncthreads();
+        topk_emit(sh, words, k, o, tid);
+        return;
+    }
     int P = 1;
     while (P < (int)m) P <<= 1;
     for (int i = (int)m + tid; i < P; i += kTopkThreads) sh.cand[i] = 0;
@@ -351,22 +391,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
     }
     __syncthreads();
 
-    // 5. positions in ascending order: contiguous words per thread, scan of bit counts
-    const int per = (words + kTopkThreads - 1) / kTopkThreads;
-    const int w0 = tid * per, w1 = min(words, w0 + per);
-    uint32_t cnt = 0;
-    for (int w = w0; w < w1; ++w) cnt += __popc(sh.bitmap[w]);
-    uint32_t tot;
-    uint32_t pos = block_inclusive_scan(cnt, sh.wsum, &tot) - cnt;
-    for (int w = w0; w < w1; ++w) {
-        uint32_t bits = sh.bitmap[w];
-        while (bits) {
-            const int b = __builtin_ctz(bits);
-            bits &= bits - 1;
-            if (pos < (uint32_t)k) o[pos] = w * 32 + b;
-            ++pos;
-        }
-    }
+    topk_emit(sh, words, k, o, tid);
 }
 
 }  // namespace sa
