@@ -75,7 +75,8 @@ sa_status check_cache(const sa_params *p, const sa_paged_cache *c, bool need_kv,
 struct DecodePlan {
     int64_t score_stride, mm_stride;  // floats per score row; tiles per min/max row
     int splits, tokens_per_split, scan_blocks;
-    size_t off_scores, off_mm, off_part_o, off_part_ml, total;
+    size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
+    int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
 };
 
 DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
@@ -109,6 +110,12 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
     } else {
         d.off_part_ml = off;
     }
+    // many-workgroup top-k state: per row a MbRowState, 3 digit histograms and
+    // two counts per chunk
+    d.off_mb = off;
+    d.mb_chunks = max_ctx > kBitmapKeys ? (max_ctx + kMbChunk - 1) / kMbChunk : 0;
+    if (d.mb_chunks > 0)
+        off = align_up(off + (size_t)batch * (sizeof(MbRowState) + 3 * kMbBins * 4 + (size_t)d.mb_chunks * 8), kAlign);
     d.total = std::max(off, kAlign);
     return d;
 }
@@ -118,7 +125,8 @@ struct PrefillPlan {
     int chunk_rows;          // rows per indexer/top-k chunk
     int splits, tokens_per_split;
     int attn_chunk_rows;     // rows per attention launch when splits > 1
-    size_t off_scores, off_mm, off_part_o, off_part_ml, total;
+    size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
+    int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
 };
 
 PrefillPlan plan_prefill(const sa_params *p, int num_rows, int q_start)
@@ -330,8 +338,27 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
         idx_decode(p, c, batch, idx_q, idx_w, scores, d.score_stride, mm, d.mm_stride, d.scan_blocks, st);
         if (mk) mk->mark();
     }
-    hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                       d.mm_stride, 0, c->context_lens, 0, p->topk, topk_idx);
+    if (d.mb_chunks > 0) {
+        MbRowState *mst = (MbRowState *)((char *)ws + d.off_mb);
+        uint32_t *hist = (uint32_t *)(mst + batch);
+        uint32_t *counts = hist + (size_t)batch * 3 * kMbBins;
+        const dim3 grid(d.mb_chunks, batch);
+        const int32_t *cl = c->context_lens;
+        hipLaunchKernelGGL(topk_mb_init_kernel, dim3(batch), dim3(256), 0, st, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_hist_kernel<0>, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_pick_kernel<0>, dim3(batch), dim3(kTopkThreads), 0, st, cl, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_hist_kernel<1>, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_pick_kernel<1>, dim3(batch), dim3(kTopkThreads), 0, st, cl, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_hist_kernel<2>, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_pick_kernel<2>, dim3(batch), dim3(kTopkThreads), 0, st, cl, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_count_kernel, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk,
+                           mst, counts, d.mb_chunks);
+        hipLaunchKernelGGL(topk_mb_emit_kernel, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk,
+                           mst, counts, d.mb_chunks, topk_idx);
+    } else {
+        hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
+                           d.mm_stride, 0, c->context_lens, 0, p->topk, topk_idx);
+    }
     if (mk) mk->mark();
 }
 

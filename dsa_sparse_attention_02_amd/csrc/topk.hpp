@@ -394,4 +394,209 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
     topk_emit(sh, words, k, o, tid);
 }
 
+// ------------------------------------------------- many workgroups per row --
+// Exact top-k of long rows (a few rows of up to millions of keys) on many
+// workgroups per row.  The k-th largest order-preserving score key T is found
+// by radix select in three digit passes (key bits 31..21, 20..10, 9..0): each
+// pass histograms, over chunks of kMbChunk keys, the next digit of the keys
+// that match the digits fixed so far (LDS, then global atomics), and one
+// workgroup per row picks the digit where the running count from the top
+// reaches the remaining rank.  Afterwards the row keeps every key above T and
+// the first `krem` keys equal to T in position order (lowest index first).  A
+// count pass gives each chunk its numbers of both; the emit pass writes each
+// chunk's kept positions, in ascending order, at the offset the counts of the
+// chunks before it give.
+constexpr int kMbChunk = 16384;  // keys per workgroup
+constexpr int kMbBins = 2048;
+
+struct MbRowState {
+    uint32_t prefix, pmask, krem, pad;  // digits fixed so far, their mask, rank left within them
+};
+
+__global__ __launch_bounds__(256) void topk_mb_init_kernel(int k, MbRowState *__restrict__ st,
+                                                           uint32_t *__restrict__ hist)
+{
+    const int r = blockIdx.x;
+    for (int i = threadIdx.x; i < 3 * kMbBins; i += 256) hist[(int64_t)r * 3 * kMbBins + i] = 0u;
+    if (threadIdx.x == 0) st[r] = MbRowState{0u, 0u, (uint32_t)k, 0u};
+}
+
+// the four keys of positions i..i+3 of the chunk ending at c1 (zero keys past c1, never counted)
+__device__ __forceinline__ void mb_keys4(const float *__restrict__ sr, int i, int c1, uint32_t *key)
+{
+    if (i + 3 < c1) {
+        const f32x4 v = *reinterpret_cast<const f32x4 *>(sr + i);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[e] = score_key(v[e]);
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[e] = i + e < c1 ? score_key(sr[i + e]) : 0u;
+    }
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kTopkThreads) void topk_mb_hist_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens, int k,
+    const MbRowState *__restrict__ st, uint32_t *__restrict__ hist)
+{
+    constexpr int SHIFT = PASS == 0 ? 21 : PASS == 1 ? 10 : 0;
+    constexpr int NB = PASS == 2 ? 1024 : 2048;
+    __shared__ uint32_t h[NB];
+    const int r = blockIdx.y, n = ctx_lens[r], tid = threadIdx.x;
+    const int c0 = blockIdx.x * kMbChunk;
+    if (n <= k || c0 >= n) return;  // block-uniform
+    const int c1 = min(n, c0 + kMbChunk);
+    const MbRowState s = st[r];
+    for (int i = tid; i < NB; i += kTopkThreads) h[i] = 0u;
+    __syncthreads();
+    const float *sr = scores + (int64_t)r * score_stride;
+    for (int i = c0 + 4 * tid; i < c1; i += 4 * kTopkThreads) {
+        uint32_t key[4];
+        mb_keys4(sr, i, c1, key);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (i + e < c1 && (key[e] & s.pmask) == s.prefix) atomicAdd(&h[(key[e] >> SHIFT) & (NB - 1)], 1u);
+    }
+    __syncthreads();
+    uint32_t *g = hist + ((int64_t)r * 3 + PASS) * kMbBins;
+    for (int i = tid; i < NB; i += kTopkThreads)
+        if (h[i]) atomicAdd(&g[i], h[i]);
+}
+
+template <int PASS>
+__global__ __launch_bounds__(kTopkThreads) void topk_mb_pick_kernel(const int32_t *__restrict__ ctx_lens, int k,
+                                                                      MbRowState *__restrict__ st,
+                                                                      const uint32_t *__restrict__ hist)
+{
+    constexpr int SHIFT = PASS == 0 ? 21 : PASS == 1 ? 10 : 0;
+    constexpr int NB = PASS == 2 ? 1024 : 2048;
+    constexpr int PER = NB / kTopkThreads;
+    __shared__ uint32_t wsum[kTopkWaves];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    if (ctx_lens[r] <= k) return;
+    const MbRowState s = st[r];
+    const uint32_t *g = hist + ((int64_t)r * 3 + PASS) * kMbBins;
+    // thread t owns bins NB-1-PER*t .. NB-PER*(t+1), visited from the top
+    uint32_t cnt[PER], mine = 0u;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) mine += cnt[e] = g[NB - 1 - (PER * tid + e)];
+    uint32_t tot;
+    uint32_t above = block_inclusive_scan(mine, wsum, &tot) - mine;  // keys in the bins above mine
+    if (above < s.krem && s.krem <= above + mine) {  // exactly one thread
+#pragma unroll
+        for (int e = 0; e < PER; ++e) {
+            if (s.krem <= above + cnt[e]) {
+                const uint32_t b = (uint32_t)(NB - 1 - (PER * tid + e));
+                st[r] = MbRowState{s.prefix | (b << SHIFT), s.pmask | ((uint32_t)(NB - 1) << SHIFT), s.krem - above, 0u};
+                break;
+            }
+            above += cnt[e];
+        }
+    }
+}
+
+// per chunk: keys above T, keys equal to T
+__global__ __launch_bounds__(kTopkThreads) void topk_mb_count_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens, int k,
+    const MbRowState *__restrict__ st, uint32_t *__restrict__ counts, int chunks)
+{
+    __shared__ uint32_t wsum[kTopkWaves];
+    const int r = blockIdx.y, n = ctx_lens[r], tid = threadIdx.x;
+    const int c0 = blockIdx.x * kMbChunk;
+    if (n <= k) return;
+    uint32_t *cc = counts + ((int64_t)r * chunks + blockIdx.x) * 2;
+    if (c0 >= n) {
+        if (tid == 0) cc[0] = cc[1] = 0u;
+        return;
+    }
+    const int c1 = min(n, c0 + kMbChunk);
+    const uint32_t T = st[r].prefix;
+    const float *sr = scores + (int64_t)r * score_stride;
+    uint32_t a = 0u, e_ = 0u;
+    for (int i = c0 + 4 * tid; i < c1; i += 4 * kTopkThreads) {
+        uint32_t key[4];
+        mb_keys4(sr, i, c1, key);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = i + e < c1;
+            a += ok && key[e] > T;
+            e_ += ok && key[e] == T;
+        }
+    }
+    uint32_t ta, te;
+    block_inclusive_scan(a, wsum, &ta);
+    block_inclusive_scan(e_, wsum, &te);
+    if (tid == 0) {
+        cc[0] = ta;
+        cc[1] = te;
+    }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_mb_emit_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens, int k,
+    const MbRowState *__restrict__ st, const uint32_t *__restrict__ counts, int chunks, int32_t *__restrict__ out)
+{
+    __shared__ uint32_t wsum[kTopkWaves];
+    __shared__ uint32_t base[2];  // this chunk's output offset, ties it keeps
+    const int r = blockIdx.y, n = ctx_lens[r], tid = threadIdx.x;
+    int32_t *o = out + (int64_t)r * k;
+    if (n <= k) {  // the whole row, then padding; the row's workgroups share the k slots
+        for (int i = blockIdx.x * kTopkThreads + tid; i < k; i += gridDim.x * kTopkThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const int c0 = blockIdx.x * kMbChunk;
+    if (c0 >= n) return;
+    const int c1 = min(n, c0 + kMbChunk);
+    const uint32_t T = st[r].prefix, krem = st[r].krem;
+    if (tid == 0) {
+        // ties go to the chunks in position order, krem of them in all
+        const uint32_t *cc = counts + (int64_t)r * chunks * 2;
+        uint32_t off = 0u, ties = 0u;
+        for (int c = 0; c < (int)blockIdx.x; ++c) {
+            const uint32_t t = min(cc[2 * c + 1], krem > ties ? krem - ties : 0u);
+            off += cc[2 * c] + t;
+            ties += cc[2 * c + 1];
+        }
+        base[0] = off;
+        base[1] = min(cc[2 * blockIdx.x + 1], krem > ties ? krem - ties : 0u);
+    }
+    __syncthreads();
+    const uint32_t off0 = base[0], my_ties = base[1];
+    const float *sr = scores + (int64_t)r * score_stride;
+    uint32_t done = 0u, ties_seen = 0u;  // kept and tied keys of the chunk before this round
+    for (int i0 = c0; i0 < c1; i0 += 4 * kTopkThreads) {  // block-uniform rounds of 4096 keys
+        const int i = i0 + 4 * tid;
+        uint32_t key[4] = {0u, 0u, 0u, 0u};
+        if (i < c1) mb_keys4(sr, i, c1, key);
+        uint32_t nt = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) nt += i + e < c1 && key[e] == T;
+        uint32_t tt;
+        uint32_t tie_rank = ties_seen + block_inclusive_scan(nt, wsum, &tt) - nt;
+        bool keep[4];
+        uint32_t nk = 0u;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool ok = i + e < c1;
+            bool kp = ok && key[e] > T;
+            if (ok && key[e] == T) {
+                kp = tie_rank < my_ties;
+                ++tie_rank;
+            }
+            keep[e] = kp;
+            nk += kp;
+        }
+        uint32_t tk;
+        uint32_t rank = done + block_inclusive_scan(nk, wsum, &tk) - nk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (keep[e]) {
+                if (off0 + rank < (uint32_t)k) o[off0 + rank] = i + e;  // (always, by the counts)
+                ++rank;
+            }
+        done += tk;
+        ties_seen += tt;
+    }
+}
+
 }  // namespace sa
