@@ -564,38 +564,96 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
 
 // Merge the split partials of one (row, head): with M the largest partial max,
 // o = sum_i 2^(m_i - M) o_i / sum_i 2^(m_i - M) l_i and
-// lse = (M + log2 sum_i 2^(m_i - M) le_i) ln 2.
+// lse = (M + log2 sum_i 2^(m_i - M) le_i) ln 2.  The max and the sums run over
+// the splits with one split per thread; the weights 2^(m_i - M) are kept in LDS,
+// and the weighted sum loads four splits' partials at a time.  A split without a
+// valid token has l_i = 0, weight 0 and a zero (finite) partial.
+constexpr int kCombineWeights = 256;  // splits whose weights are kept in LDS
+
+__device__ __forceinline__ float combine_block_reduce(float v, bool is_max, float *red)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float o = __shfl_xor(v, d);
+        v = is_max ? fmaxf(v, o) : v + o;
+    }
+    const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+    if ((threadIdx.x & 63) == 0) red[wave] = v;
+    __syncthreads();
+    float t = red[0];
+    for (int w = 1; w < nw; ++w) t = is_max ? fmaxf(t, red[w]) : t + red[w];
+    __syncthreads();  // red is reused by the next call
+    return t;
+}
+
 template <int V>
 __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_ml, int splits,
                                                       int num_heads, void *__restrict__ out, int out_bf16,
                                                       float *__restrict__ lse)
 {
-    const int h = blockIdx.x, r = blockIdx.y;
+    __shared__ float wgt[kCombineWeights];
+    __shared__ float red[2];
+    const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, nt = blockDim.x;
     const int64_t base = (int64_t)r * splits * num_heads + h;  // partial (r, split 0, h)
-    float M = -INFINITY;
-    for (int s = 0; s < splits; ++s) {
-        const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + (base + (int64_t)s * num_heads) * 4);
-        if (ml[1] > 0.0f) M = fmaxf(M, ml[0]);
-    }
-    float L = 0.0f, Le = 0.0f;
-    for (int s = 0; s < splits; ++s) {
-        const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + (base + (int64_t)s * num_heads) * 4);
-        if (ml[1] > 0.0f) {
-            const float f = exp2f(ml[0] - M);
-            L += ml[1] * f;
-            Le += ml[2] * f;
+    auto ml_of = [&](int s) { return *reinterpret_cast<const f32x4 *>(part_ml + (base + (int64_t)s * num_heads) * 4); };
+    const bool wave_path = splits <= 64;  // (block-uniform) every wave on its own, one split per lane
+    float M, L, Le, wl = 0.0f;
+    if (wave_path) {
+        const int ln = tid & 63;
+        const f32x4 ml = ln < splits ? ml_of(ln) : f32x4{-INFINITY, 0.0f, 0.0f, 0.0f};
+        float mx = ml[1] > 0.0f ? ml[0] : -INFINITY;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) mx = fmaxf(mx, __shfl_xor(mx, d));
+        M = mx;
+        wl = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
+        float ls = ml[1] * wl, les = ml[2] * wl;
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) {
+            ls += __shfl_xor(ls, d);
+            les += __shfl_xor(les, d);
         }
+        L = ls;
+        Le = les;
+    } else {
+        float mx = -INFINITY;
+        for (int s = tid; s < splits; s += nt) {
+            const f32x4 ml = ml_of(s);
+            if (ml[1] > 0.0f) mx = fmaxf(mx, ml[0]);
+        }
+        M = combine_block_reduce(mx, true, red);
+        float ls = 0.0f, les = 0.0f;
+        for (int s = tid; s < splits; s += nt) {
+            const f32x4 ml = ml_of(s);
+            const float f = ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
+            if (s < kCombineWeights) wgt[s] = f;
+            ls += ml[1] * f;
+            les += ml[2] * f;
+        }
+        L = combine_block_reduce(ls, false, red);
+        Le = combine_block_reduce(les, false, red);  // (its barriers also publish wgt)
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    auto w_of = [&](int s) -> float {
+        if (wave_path) return __shfl(wl, s);
+        if (s < kCombineWeights) return wgt[s];
+        const f32x4 ml = ml_of(s);
+        return ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;
+    };
     const int64_t obase = ((int64_t)r * num_heads + h) * V;
-    for (int v = 4 * threadIdx.x; v < V; v += 4 * blockDim.x) {
+    for (int v = 4 * tid; v < V; v += 4 * nt) {
         f32x4 acc = {0.0f, 0.0f, 0.0f, 0.0f};
-        for (int s = 0; s < splits; ++s) {
-            const int64_t ps = base + (int64_t)s * num_heads;
-            const f32x4 ml = *reinterpret_cast<const f32x4 *>(part_ml + ps * 4);
-            if (ml[1] > 0.0f) acc += exp2f(ml[0] - M) * *reinterpret_cast<const f32x4 *>(part_o + ps * V + v);
+        const float *po = part_o + base * V + v;
+        const int64_t sstep = (int64_t)num_heads * V;
+        int s = 0;
+        for (; s + 4 <= splits; s += 4) {
+            f32x4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = *reinterpret_cast<const f32x4 *>(po + (s + u) * sstep);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) acc += w_of(s + u) * x[u];
         }
+        for (; s < splits; ++s) acc += w_of(s) * *reinterpret_cast<const f32x4 *>(po + s * sstep);
         acc *= inv;
         if (out_bf16) {
             uint32_t *ob = reinterpret_cast<uint32_t *>(out) + ((obase + v) >> 1);
@@ -605,8 +663,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
             *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(out) + obase + v) = acc;
         }
     }
-    if (lse && threadIdx.x == 0)
-        lse[(int64_t)r * num_heads + h] = L > 0.0f ? (M + log2f(Le)) * 0.69314718055994531f : -INFINITY;
+    if (lse && tid == 0) lse[(int64_t)r * num_heads + h] = L > 0.0f ? (M + log2f(Le)) * 0.69314718055994531f : -INFINITY;
 }
 
 }  // namespace sa
