@@ -128,6 +128,24 @@ def run_decode(args, torch, sa, synth):
                    per_kernel=per_kernel)
 
 
+def run_other_decodes(args, torch, sa, synth, names):
+    """The other decode configurations, timed like the main one (fewer steps, no flush)."""
+    res = {}
+    for name in names:
+        sub = argparse.Namespace(**vars(args))
+        sub.workload, sub.steps, sub.warmup, sub.flush_steps = name, 10, 3, 0
+        w, dec = run_decode(sub, torch, sa, synth)
+        B = len(w["context_lens"])
+        res[name] = {"ms_per_step": round(dec["ms"], 4), "tokens_per_s": round(B / (dec["ms"] / 1e3), 1),
+                     "hbm_gbps": round(dec["alg"]["bytes"] / (dec["ms"] / 1e3) / 1e9, 1),
+                     "hbm_frac": round(dec["alg"]["bytes"] / (dec["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+                     "algorithmic_bytes_per_step": dec["alg"]["bytes"],
+                     "stages_us": {k: round(v * 1e3, 2) for k, v in dec["stages"].items()}}
+        del w, dec
+        torch.cuda.empty_cache()
+    return res
+
+
 def run_prefill(args, torch, sa, synth):
     spec = synth.WORKLOADS["prefill_L32k"]
     log(f"generating {spec.name}")
@@ -272,6 +290,10 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=2)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--other-workloads", default="none",
+                    help="comma-separated decode workloads also timed, e.g. decode_b32_ctx8k,decode_b4_ctx1m "
+                         "(supplementary, not the metric; off by default so that kernel traces of the default "
+                         "command hold the headline workload only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -347,6 +369,9 @@ def main():
     }
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, torch, sa, synth)
+    others = [x for x in args.other_workloads.split(",") if x and x != "none" and x != args.workload]
+    if others:
+        line["other_workloads"] = run_other_decodes(args, torch, sa, synth, others)
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on up to {args.cpu_seconds:.0f}s of rows")
         line["cpu_baseline"] = cpu_baseline(args, w)
