@@ -634,8 +634,11 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
         Le = combine_block_reduce(les, false, red);  // (its barriers also publish wgt)
     }
     const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    // (wave path: split s's weight sits in lane s.  v_readlane reads it whatever
+    // the exec mask, which matters below: for V < 4 * 64 only the first V / 4
+    // lanes run the column loop, and a shuffle from an inactive lane reads 0.)
     auto w_of = [&](int s) -> float {
-        if (wave_path) return __shfl(wl, s);
+        if (wave_path) return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(wl), s));
         if (s < kCombineWeights) return wgt[s];
         const f32x4 ml = ml_of(s);
         return ml[1] > 0.0f ? exp2f(ml[0] - M) : 0.0f;

@@ -27,11 +27,19 @@ namespace sa {
 // tiles (row-major, each row's tiles in key order); wave g of G takes the
 // contiguous tiles [g*T/G, (g+1)*T/G), so every wave moves the same number of
 // bytes whatever the context lengths.  Key tiles stream HBM -> LDS through the
-// LDS-DMA path (global_load_lds_dwordx4) in a kStages-deep per-wave ring: one DMA
-// instruction fetches four whole 256-byte key rows (1 KB contiguous per row
-// group), and the 16-byte pieces are XOR-swizzled so that the MFMA operand reads
-// (32 rows x one piece per half-wave) hit 16 distinct bank groups.  Waves never
-// share LDS, so the only synchronisation is each wave's own vmcnt wait.
+// LDS-DMA path in a kStages-deep per-wave ring: one DMA instruction fetches four
+// whole 256-byte key rows (1 KB contiguous per row group), and the 16-byte
+// pieces are XOR-swizzled so that the MFMA operand reads (32 rows x one piece
+// per half-wave) hit 16 distinct bank groups.  Waves never share LDS, so the
+// only synchronisation is each wave's own vmcnt wait.
+//
+// Scores are not stored tile by tile: a wave keeps the scores of up to
+// 2 * kScanScoreRegs tiles in registers (two tiles per register, one per lane
+// half) and writes them when its row segment ends or the buffer is full.  For
+// the usual share of a wave (under 80 tiles) that is one burst after its last
+// key read.  Score writes mixed into the key stream slow it far more than their
+// bytes (about 1.3 us per MB on MI355X, in 128-byte lines or 8 KiB bursts alike),
+// while the same bytes written once reading is over cost a fraction of that.
 #ifndef SA_SCAN_STAGES
 #define SA_SCAN_STAGES 2
 #endif
@@ -40,6 +48,7 @@ namespace sa {
 #endif
 constexpr int kScanStages = SA_SCAN_STAGES;       // tiles per wave ring (stages-1 in flight while one is scored)
 constexpr int kScanWavesPerBlock = SA_SCAN_WAVES;
+constexpr int kScanScoreRegs = 40;                // score buffer registers per lane (80 tiles)
 
 // s_waitcnt vmcnt(n) that also fences the compiler: LDS written by the DMA path
 // is not tracked by the compiler's own wait insertion.
@@ -53,23 +62,15 @@ __device__ __forceinline__ void wait_vmcnt()
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// store instructions every scored tile issues (its scores); the tile ranges are
-// flushed once per 16 tiles, and such an extra store only lengthens a wait
-constexpr int kScanStores = 1;
-
 // Wait until the copies of the j-th tile of a segment have landed (see the ring
-// comment in the kernel): younger are (stages - 1) tiles of copies and the
-// stores of min(j, stages - 1) scored tiles.
+// comment in the kernel): the copies of the kScanStages - 1 tiles ahead are
+// younger.  Stores (score bursts, tile ranges) issued since only lengthen it.
 template <int DMA>
-__device__ __forceinline__ void scan_wait(int j)
+__device__ __forceinline__ void scan_wait()
 {
     constexpr int S1 = kScanStages - 1;
-    static_assert(S1 * (DMA + kScanStores) < 64, "vmcnt range");
-    if (j >= S1) wait_vmcnt<S1 * (DMA + kScanStores)>();
-    else if (j == 0) wait_vmcnt<S1 * DMA>();
-    else if (j == 1) wait_vmcnt<S1 * DMA + kScanStores>();
-    else if (j == 2) wait_vmcnt<S1 * DMA + 2 * kScanStores>();
-    else wait_vmcnt<S1 * DMA>();  // (deeper rings) waiting for more is safe
+    static_assert(S1 * DMA < 64, "vmcnt range");
+    wait_vmcnt<S1 * DMA>();
 }
 
 // BLOCK_TILE: every cache block holds a whole number of 32-key tiles (block_size
@@ -88,6 +89,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
     static_assert(PIECES == 16 || PIECES == 4, "key row of 256 or 64 bytes");
     constexpr int SW = PIECES - 1;              // swizzle mask
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kScanWavesPerBlock][kScanStages][TILE];
+    __shared__ __attribute__((aligned(16))) float wlds[kScanWavesPerBlock][32 * IDX_TILES];
 
     // wave index made visibly wave-uniform so cursors live in scalar registers and
     // context lengths / block-table entries are scalar loads
@@ -114,19 +116,20 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
 
     // the DMA lane map: instruction i, lane l writes slot 64i + l = PIECES*r + q, which
     // holds piece q ^ (r & SW) of the tile's key row r
-    int dma_r[DMA], dma_piece[DMA];
-#pragma unroll
-    for (int i = 0; i < DMA; ++i) {
-        const int slot = 64 * i + lane;
-        dma_r[i] = slot / PIECES;
-        dma_piece[i] = (slot % PIECES) ^ (dma_r[i] & SW);
-    }
+    // (recomputed from an opaque lane id at every tile: a few ALU operations
+    // instead of 2 * DMA registers held across the loop)
+    auto dma_map = [&](int i, int &r, int &piece) {
+        int ln = lane;
+        asm volatile("" : "+v"(ln));
+        const int slot = 64 * i + ln;
+        r = slot / PIECES;
+        piece = (slot % PIECES) ^ (r & SW);
+    };
     // lane (key col, half) reads piece half*KS + ks of its row at step ks
     const int koff = col * PIECES * 16;
     const int kx = col & SW;
 
     bf16x8 qa[IDX_TILES][KS];
-    float wr[IDX_TILES][16];
 
     // per-segment state, read by the helpers below
     int ctx = 0, nt = 0;
@@ -155,14 +158,16 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
         if constexpr (BLOCK_TILE) rs = buffer_rsrc(idx_k + base * IDX_DIM, TILE);
 #pragma unroll
         for (int i = 0; i < DMA; ++i) {
-            int s = s0 + dma_r[i];
+            int dr, dp;
+            dma_map(i, dr, dp);
+            int s = s0 + dr;
             s = s < ctx ? s : ctx - 1;  // rows past the context re-read the last key; never scored
             SA_LDS void *dst = (SA_LDS void *)(my + stage * TILE + i * 1024);
             if constexpr (BLOCK_TILE) {
-                buf_dma16_to_lds_stream(rs, (s - s0) * (IDX_DIM * 2) + dma_piece[i] * 16, dst);
+                buf_dma16_to_lds_stream(rs, (s - s0) * (IDX_DIM * 2) + dp * 16, dst);
             } else {
                 const int64_t row = ((int64_t)tbl[s >> bs_log2] << bs_log2) | (s & bmask);
-                dma16_to_lds_stream(idx_k + row * IDX_DIM + dma_piece[i] * 8, dst);
+                dma16_to_lds_stream(idx_k + row * IDX_DIM + dp * 8, dst);
             }
         }
     };
@@ -185,24 +190,49 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 qa[t][ks] = head < idx_heads ? as_bf16x8(load16(qp + 8 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                const int hj = 32 * t + acc_row(i, half);
-                wr[t][i] = hj < idx_heads ? idx_w[(int64_t)b * idx_heads + hj] : 0.0f;
-            }
         }
+        // head weights of row b into this wave's LDS slot (read back per tile:
+        // held in registers they would cost 16 per head tile)
+        for (int h = lane; h < 32 * IDX_TILES; h += 64) wlds[wave][h] = h < idx_heads ? idx_w[(int64_t)b * idx_heads + h] : 0.0f;
         // A wait the compiler sees: the tile loop below then finds the queries
         // and weights complete and adds no memory wait of its own (which, next
         // to the LDS-DMA copies, it could only make a full drain on every tile).
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
-        // Ring waits.  Every tile issues DMA copies and then kScanStores stores (its
-        // scores and its range), all counted by vmcnt, which completes in issue
-        // order; at the wait for tile j the younger operations are the copies of
-        // the kScanStages - 1 tiles ahead and the stores of the (up to)
-        // kScanStages - 1 tiles scored since tile j's copies went out.
+        // Ring waits.  Every tile issues DMA copies, counted by vmcnt, which
+        // completes in issue order; at the wait for tile j the younger copies are
+        // those of the kScanStages - 1 tiles ahead.
         const int n = t1 - t0;
         float mm_lo = 0.0f, mm_hi = 0.0f;  // lane i: range of the segment's pending tile with index = i mod 16
+        // Score buffer: the m tiles scored since the last burst, segment tiles
+        // jb .. jb + m - 1.  `cur` collects a pair (tile jb + 2p in lane half 0,
+        // jb + 2p + 1 in half 1); a complete pair is pushed onto sbuf, newest at
+        // the end (a shift by register moves: the indices stay compile-time).
+        constexpr int NB = kScanScoreRegs;
+        float sbuf[NB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i) sbuf[i] = 0.0f;
+        float cur = 0.0f;
+        int m = 0, jb = 0;
+        auto push = [&]() {
+#pragma unroll
+            for (int i = 0; i + 1 < NB; ++i) sbuf[i] = sbuf[i + 1];
+            sbuf[NB - 1] = cur;
+        };
+        // One burst: pair p goes to tiles jb + 2p (+1), i.e. 256 contiguous
+        // bytes per store; the upper half of an incomplete last pair is masked.
+        auto flush = [&]() {
+            if (m & 1) push();
+            const int npairs = (m + 1) >> 1;
+            float *o = out + (int64_t)(t0 + jb + half) * 32 + col;
+#pragma unroll
+            for (int k = 0; k < NB; ++k) {  // k-th newest pair
+                const int pr = npairs - 1 - k;
+                if (k < npairs && (half == 0 || 2 * pr + 1 < m)) o[64 * pr] = sbuf[NB - 1 - k];
+            }
+            jb += m;
+            m = 0;
+        };
 #pragma unroll
         for (int j = 0; j < kScanStages - 1; ++j)
             if (j < n) issue(t0 + j, j, tile_base(t0 + j));
@@ -212,7 +242,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
             if (j + kScanStages - 1 < n) {
                 issue(t0 + j + kScanStages - 1, (j + kScanStages - 1) % kScanStages, base_next);
                 base_next = tile_base(t0 + j + kScanStages);
-                scan_wait<DMA>(j);
+                scan_wait<DMA>();
             } else {
                 wait_vmcnt<0>();
             }
@@ -231,27 +261,38 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
 #pragma unroll
                 for (int t = 0; t < IDX_TILES; ++t) acc[t][ks & 1] = mfma_32x32x16(qa[t][ks], kb[ks], acc[t][ks & 1]);
             float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            // head weights from LDS (an opaque lane id keeps these reads inside
+            // the loop instead of 16 registers per head tile)
+            int wl = lane;
+            asm volatile("" : "+v"(wl));
+            const float *wrow = &wlds[wave][4 * (wl >> 5)];
             auto head_sum = [&](auto relu_on) {
 #pragma unroll
                 for (int t = 0; t < IDX_TILES; ++t)
 #pragma unroll
-                    for (int i = 0; i < 16; ++i) {
-                        float d = acc[t][0][i] + acc[t][1][i];
-                        if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
-                        part[i & 3] = fmaf(wr[t][i], d, part[i & 3]);
+                    for (int g = 0; g < 4; ++g) {
+                        const f32x4 w4 = *reinterpret_cast<const f32x4 *>(wrow + 32 * t + 8 * g);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float d = acc[t][0][4 * g + e] + acc[t][1][4 * g + e];
+                            if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
+                            part[e] = fmaf(w4[e], d, part[e]);
+                        }
                     }
             };
             if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
             else head_sum(std::false_type{});
             const float p = (part[0] + part[1]) + (part[2] + part[3]);
             const float tot = add_wave_halves(p);
-            // Every slot of the tile lies inside the row's score stride (rounded up
-            // from the largest context), so the 32 lanes of half 0 all store: slots
-            // at or past ctx get values nothing reads, and the store instruction is
-            // issued on every tile, as the ring waits count.
             const int tt = t0 + j;
             const int s = tt * 32 + col;
-            if (half == 0) out[s] = tot + 0.0f;
+            // This tile's scores into the buffer (slots at or past ctx get values
+            // nothing reads; every slot lies inside the row's score stride, which
+            // is rounded up from the largest context).
+            cur = half == (m & 1) ? tot + 0.0f : cur;
+            ++m;
+            if (!(m & 1)) push();
+            if (m == 2 * NB) flush();
             // The tile's score range, for the range-binned top-k histogram.  Lane
             // tt % 16 keeps it, and a group of 16 tiles is written as one whole
             // 128-byte line (partial lines only at segment ends) instead of one
@@ -267,6 +308,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
                     tile_mm[(int64_t)b * mm_stride + g0 + lane] = f32x2{mm_lo, mm_hi};
             }
         }
+        if (m) flush();
         t_cur = row_first + t1;
         row_first += nt;
         ++b;

@@ -87,6 +87,7 @@ def compare(w, res, rows=None, tag=""):
 
 
 MLA = synth.MLA
+V64 = replace(MLA, num_heads=8, qk_dim=64, v_dim=64, softmax_scale=1.0 / 8.0)  # MLA indexer, small attention
 
 
 CASES = {
@@ -111,6 +112,10 @@ CASES = {
     "decode_h96": lambda: synth.small_decode("decode_h96", replace(MLA, num_heads=96), [2, 33, 2048, 6000], seed=111),
     "decode_tiny_h40": lambda: synth.small_decode("decode_tiny_h40", replace(synth.TINY, num_heads=40), [5, 64, 900],
                                                   seed=112),
+    # value width 64 with 32 splits per row: the merge's column loop then runs on
+    # 16 lanes of a wave while the split weights sit in lanes 0..31
+    "decode_v64_splits": lambda: synth.small_decode("decode_v64_splits", V64, [3000, 2500, 4000, 2049, 5000, 2100],
+                                                    seed=115),
 }
 
 
@@ -177,3 +182,17 @@ def test_parity_full_size(dev, name):
         ctx = w["context_lens"]
         rows = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 63})
     compare(w, run_gpu(dev, w), rows=rows, tag=name)
+
+
+def test_parity_scan_score_bursts(dev):
+    """About 6M visible keys: each of the scan's 2048 waves scores about 92
+    32-key tiles, more than its 80-tile score buffer, so every wave writes a
+    full burst mid-segment and a partial one at its end, and a few ranges cross
+    a row boundary.  The attention part is kept small (8 heads of dim 64) so the
+    cache stays near 2.3 GB; the indexer has the MLA shape."""
+    shape = V64
+    ctx = [1_000_003, 999_999, 1_000_000, 1_048_576, 1_000_037, 1_000_001]
+    spec = synth.small_decode("decode_scan_bursts", shape, ctx, seed=114)
+    say("[gpu] scan score bursts, 6 rows of ~1M keys")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w), rows=[0, 3, 5], tag="decode_scan_bursts")
