@@ -24,9 +24,10 @@ namespace sa {
 
 // ------------------------------------------------------------------ decode --
 // Persistent key scan.  The visible keys of all rows form one list of 32-key
-// tiles (row-major, each row's tiles in key order); wave g of G takes the
-// contiguous tiles [g*T/G, (g+1)*T/G), so every wave moves the same number of
-// bytes whatever the context lengths.  Key tiles stream HBM -> LDS through the
+// tiles (row-major, each row's tiles in key order), grouped in pairs; block b
+// of B takes the contiguous pairs [b*P/B, (b+1)*P/B), so every block moves the
+// same number of bytes whatever the context lengths, and its waves claim those
+// pairs one at a time (below).  Key tiles stream HBM -> LDS through the
 // LDS-DMA path in a kStages-deep per-wave ring: one DMA instruction fetches four
 // whole 256-byte key rows (1 KB contiguous per row group), and the 16-byte
 // pieces are XOR-swizzled so that the MFMA operand reads (32 rows x one piece
@@ -35,9 +36,9 @@ namespace sa {
 //
 // Scores are not stored tile by tile: a wave keeps the scores of up to
 // 2 * kScanScoreRegs tiles in registers (two tiles per register, one per lane
-// half) and writes them when its row segment ends or the buffer is full.  For
-// the usual share of a wave (under 80 tiles) that is one burst after its last
-// key read.  Score writes mixed into the key stream slow it far more than their
+// half) and writes them when the buffer is full or its work is done.  For the
+// usual share of a wave (under 80 tiles) that is one burst after its last key
+// read.  Score writes mixed into the key stream slow it far more than their
 // bytes (about 1.3 us per MB on MI355X, in 128-byte lines or 8 KiB bursts alike),
 // while the same bytes written once reading is over cost a fraction of that.
 #ifndef SA_SCAN_STAGES
@@ -62,16 +63,20 @@ __device__ __forceinline__ void wait_vmcnt()
 // s_waitcnt immediate for vmcnt(0) alone (expcnt and lgkmcnt at their maxima)
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Wait until the copies of the j-th tile of a segment have landed (see the ring
-// comment in the kernel): the copies of the kScanStages - 1 tiles ahead are
-// younger.  Stores (score bursts, tile ranges) issued since only lengthen it.
-template <int DMA>
-__device__ __forceinline__ void scan_wait()
-{
-    constexpr int S1 = kScanStages - 1;
-    static_assert(S1 * DMA < 64, "vmcnt range");
-    wait_vmcnt<S1 * DMA>();
-}
+// vmcnt(n) as an immediate for the compiler-visible s_waitcnt builtin
+// (expcnt and lgkmcnt at their maxima)
+__device__ __forceinline__ constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
+
+// Work of the scan.  Each row's tiles are grouped in pairs (the last pair of a
+// row with an odd tile count holds one tile); the pairs of all rows form one
+// list, split evenly into one contiguous range per block, and the block's 8
+// waves claim its pairs one at a time from a counter in LDS.  Waves do not
+// move bytes at one rate: on MI355X waves of one XCD finished equal static
+// shares about 10% apart (and whole XCDs up to 20% apart), so a static split
+// per wave leaves the kernel waiting on its slowest waves.  Global atomics
+// would balance across blocks too, but their returns join the memory counter
+// that the ring waits on, and each claim then stalled the tile it followed
+// (the scan ran 30% slower that way); LDS atomics stay off that counter.
 
 // BLOCK_TILE: every cache block holds a whole number of 32-key tiles (block_size
 // >= 32), so a tile's 32 rows are contiguous and its block id is one scalar load.
@@ -86,10 +91,16 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
     constexpr int PIECES = IDX_DIM / 8;         // 16-byte pieces per key row
     constexpr int TILE = 32 * IDX_DIM * 2;      // bytes per 32-key tile
     constexpr int DMA = TILE / 1024;            // DMA instructions per tile
+    constexpr int NB = kScanScoreRegs;          // score buffer: pairs of tiles
     static_assert(PIECES == 16 || PIECES == 4, "key row of 256 or 64 bytes");
+    static_assert(kScanStages == 2, "the tile stream below keeps one tile in flight while one is scored");
     constexpr int SW = PIECES - 1;              // swizzle mask
     __shared__ __attribute__((aligned(1024))) uint8_t ring[kScanWavesPerBlock][kScanStages][TILE];
     __shared__ __attribute__((aligned(16))) float wlds[kScanWavesPerBlock][32 * IDX_TILES];
+    // per buffered pair: its row, first tile (+ 1 << 30 when it holds one tile)
+    // and the two tiles' score ranges
+    __shared__ int2 pair_dst[kScanWavesPerBlock][NB];
+    __shared__ f32x4 pair_mm[kScanWavesPerBlock][NB];
 
     // wave index made visibly wave-uniform so cursors live in scalar registers and
     // context lengths / block-table entries are scalar loads
@@ -98,21 +109,62 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
     const int bmask = (1 << bs_log2) - 1;
     uint8_t *my = &ring[wave][0][0];
 
-    // this wave's share [t_begin, t_end) of all tiles of all rows
-    int64_t total = 0;
-    for (int b = 0; b < batch; ++b) total += (ctx_lens[b] + 31) >> 5;
-    const int64_t G = (int64_t)gridDim.x * kScanWavesPerBlock;
-    const int64_t g = (int64_t)blockIdx.x * kScanWavesPerBlock + wave;
-    int64_t t_cur = total * g / G;
-    const int64_t t_end = total * (g + 1) / G;
-    if (t_cur >= t_end) return;
-    int b = 0;
-    int64_t row_first = 0;  // global index of row b's first tile
-    for (;; ++b) {
-        const int nt = (ctx_lens[b] + 31) >> 5;
-        if (t_cur < row_first + nt) break;
-        row_first += nt;
-    }
+    // ---- the pair list and this block's claims ----
+    auto row_pairs = [&](int b) { return (((ctx_lens[b] + 31) >> 5) + 1) >> 1; };
+    int64_t total_pairs = 0;
+    for (int b = 0; b < batch; ++b) total_pairs += row_pairs(b);
+    const int nblk = gridDim.x;
+    auto range_lo = [&](int blk) { return total_pairs * blk / nblk; };
+    int rb = 0;              // row cursor: row rb's first pair is list index rfirst
+    int64_t rfirst = 0;
+    auto locate = [&](int64_t p) {
+        if (p < rfirst) {
+            rb = 0;
+            rfirst = 0;
+        }
+        for (;;) {  // (rows without keys are stepped over)
+            const int np = row_pairs(rb);
+            if (p < rfirst + np) break;
+            rfirst += np;
+            ++rb;
+        }
+    };
+    __shared__ int blk_claims;
+    if (threadIdx.x == 0) blk_claims = 0;
+    __syncthreads();
+    const int64_t my_lo = range_lo(blockIdx.x), my_hi = range_lo(blockIdx.x + 1);
+    int claim = 0;  // lane 0: this wave's pending claim
+    if (lane == 0) claim = atomicAdd(&blk_claims, 1);
+    // The next pair of this wave: (row, first tile, tiles 1 or 2); false when
+    // the block's range is used up.  Using a claim sets need_claim: the main
+    // loop requests the next one after its ring wait, well before its use.
+    bool need_claim = false;
+    auto next_pair = [&](int &pb, int &pt, int &pn) -> bool {
+        if (need_claim) {  // (a one-tile pair right after the last claim: request it now)
+            if (lane == 0) claim = atomicAdd(&blk_claims, 1);
+            need_claim = false;
+        }
+        const int64_t p = my_lo + __builtin_amdgcn_readfirstlane(claim);
+        if (p >= my_hi) return false;
+        need_claim = true;
+        locate(p);
+        const int nt = (ctx_lens[rb] + 31) >> 5;
+        pb = rb;
+        pt = 2 * (int)(p - rfirst);
+        pn = pt + 1 < nt ? 2 : 1;
+        return true;
+    };
+    int pr_b = 0, pr_t = 0, pr_n = 0, pr_i = 0;  // current pair and the next tile index within it
+    auto next_tile = [&](int &b_out, int &t_out) -> bool {
+        if (pr_i >= pr_n) {
+            if (!next_pair(pr_b, pr_t, pr_n)) return false;
+            pr_i = 0;
+        }
+        b_out = pr_b;
+        t_out = pr_t + pr_i;
+        ++pr_i;
+        return true;
+    };
 
     // the DMA lane map: instruction i, lane l writes slot 64i + l = PIECES*r + q, which
     // holds piece q ^ (r & SW) of the tile's key row r
@@ -129,30 +181,27 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
     const int koff = col * PIECES * 16;
     const int kx = col & SW;
 
-    bf16x8 qa[IDX_TILES][KS];
-
-    // per-segment state, read by the helpers below
-    int ctx = 0, nt = 0;
-    const int32_t *tbl = block_table;
     // Physical row of a tile's first key (BLOCK_TILE).  The block-table entry is a
     // scalar load (constant address space, wave-uniform index): scalar loads are
     // counted by lgkmcnt, so waiting for one never drains the copies in flight,
     // and it is issued a tile before its copies need it.
     typedef const __attribute__((address_space(4))) int32_t *ctbl_t;
-    auto tile_base = [&](int t) -> int64_t {
+    auto tile_base = [&](int b, int t) -> int64_t {
         if constexpr (BLOCK_TILE) {
-            const int s0 = (t < nt - 1 ? t : nt - 1) * 32;
+            const int s0 = t * 32;
             const int bi = __builtin_amdgcn_readfirstlane(s0 >> bs_log2);
-            const int blk = ((ctbl_t)(uintptr_t)tbl)[bi];
+            const int blk = ((ctbl_t)(uintptr_t)(block_table + (int64_t)b * max_blocks))[bi];
             return ((int64_t)blk << bs_log2) | (s0 & bmask);
         } else {
             return 0;
         }
     };
-    // The copies of a tile.  With BLOCK_TILE its 32 rows are contiguous: one
-    // buffer resource over them, buffer-form LDS-DMA (after the global form the
-    // compiler would drain every LDS read in flight at each later wait on one).
-    auto issue = [&](int t, int stage, int64_t base) {
+    // The copies of tile t of row b.  With BLOCK_TILE its 32 rows are contiguous:
+    // one buffer resource over them, buffer-form LDS-DMA (after the global form
+    // the compiler would drain every LDS read in flight at each later wait on one).
+    auto issue = [&](int b, int t, int stage, int64_t base) {
+        const int ctx = ctx_lens[b];
+        const int32_t *tbl = block_table + (int64_t)b * max_blocks;
         const int s0 = t * 32;
         [[maybe_unused]] __amdgpu_buffer_rsrc_t rs;
         if constexpr (BLOCK_TILE) rs = buffer_rsrc(idx_k + base * IDX_DIM, TILE);
@@ -172,148 +221,168 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
         }
     };
 
-    // one row segment at a time: [t0, t1) tiles of row b
-    while (t_cur < t_end) {
-        ctx = ctx_lens[b];
-        nt = (ctx + 31) >> 5;
-        const int t0 = (int)(t_cur - row_first);
-        const int64_t rem = t_end - row_first;
-        const int t1 = rem < nt ? (int)rem : nt;
-        tbl = block_table + (int64_t)b * max_blocks;
-        float *out = scores + (int64_t)b * score_stride;
+    bf16x8 qa[IDX_TILES][KS];
+    int loaded_b = -1;  // row whose queries and weights are in qa / wlds
 
-        // queries and head weights of row b (waits for everything in flight: once per segment)
+    // Score buffer: one register per pair of tiles (first tile in lane half 0,
+    // second in half 1), the newest at the end (a shift by register moves: the
+    // indices stay compile-time); the m-th pair pushed since the last burst has
+    // its destination and score ranges in pair_dst / pair_mm[wave][m].
+    float sbuf[NB];
 #pragma unroll
-        for (int t = 0; t < IDX_TILES; ++t) {
-            const int head = 32 * t + col;
-            const uint16_t *qp = idx_q + ((int64_t)b * idx_heads + head) * IDX_DIM + half * (IDX_DIM / 2);
+    for (int i = 0; i < NB; ++i) sbuf[i] = 0.0f;
+    float cur = 0.0f;
+    f32x4 cur_mm = f32x4{};
+    int m = 0;
+    auto push = [&](int b, int t0, int n) {
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                qa[t][ks] = head < idx_heads ? as_bf16x8(load16(qp + 8 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
+        for (int i = 0; i + 1 < NB; ++i) sbuf[i] = sbuf[i + 1];
+        sbuf[NB - 1] = cur;
+        if (lane == 0) {
+            pair_dst[wave][m] = int2{b, t0 | (n == 1 ? (1 << 30) : 0)};
+            pair_mm[wave][m] = cur_mm;
         }
-        // head weights of row b into this wave's LDS slot (read back per tile:
-        // held in registers they would cost 16 per head tile)
-        for (int h = lane; h < 32 * IDX_TILES; h += 64) wlds[wave][h] = h < idx_heads ? idx_w[(int64_t)b * idx_heads + h] : 0.0f;
-        // A wait the compiler sees: the tile loop below then finds the queries
-        // and weights complete and adds no memory wait of its own (which, next
-        // to the LDS-DMA copies, it could only make a full drain on every tile).
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        ++m;
+    };
+    // One burst: each pair's scores as one 256-byte store (half 1 masked for a
+    // one-tile pair) and its score ranges as one 16-byte store.
+    auto flush = [&]() {
+#pragma unroll
+        for (int k = 0; k < NB; ++k) {  // k-th newest pair
+            if (k < m) {
+                const int2 dst = pair_dst[wave][m - 1 - k];
+                const bool one = (dst.y >> 30) & 1;
+                const int t0 = dst.y & ((1 << 30) - 1);
+                if (half == 0 || !one) scores[(int64_t)dst.x * score_stride + (int64_t)(t0 + half) * 32 + col] = sbuf[NB - 1 - k];
+                if (lane == 0) {
+                    const f32x4 mmv = pair_mm[wave][m - 1 - k];
+                    f32x2 *mo = tile_mm + (int64_t)dst.x * mm_stride + t0;
+                    mo[0] = f32x2{mmv[0], mmv[1]};
+                    if (!one) mo[1] = f32x2{mmv[2], mmv[3]};
+                }
+            }
+        }
+        m = 0;
+    };
 
-        // Ring waits.  Every tile issues DMA copies, counted by vmcnt, which
-        // completes in issue order; at the wait for tile j the younger copies are
-        // those of the kScanStages - 1 tiles ahead.
-        const int n = t1 - t0;
-        float mm_lo = 0.0f, mm_hi = 0.0f;  // lane i: range of the segment's pending tile with index = i mod 16
-        // Score buffer: the m tiles scored since the last burst, segment tiles
-        // jb .. jb + m - 1.  `cur` collects a pair (tile jb + 2p in lane half 0,
-        // jb + 2p + 1 in half 1); a complete pair is pushed onto sbuf, newest at
-        // the end (a shift by register moves: the indices stay compile-time).
-        constexpr int NB = kScanScoreRegs;
-        float sbuf[NB];
+    // Ring.  Per iteration: the next tile's copies are issued into the other
+    // stage, the tile after it is found (its block-table entry loads
+    // meanwhile), the wave waits for the current tile (younger: the next
+    // tile's copies; stores issued since only lengthen the wait) and scores it.
+    int a_b, a_t;
+    if (!next_tile(a_b, a_t)) return;
+    int a_n = pr_n, a_first = pr_t;  // the pair of tile a
+    issue(a_b, a_t, 0, tile_base(a_b, a_t));
+    int c_b = 0, c_t = 0;
+    bool have_c = next_tile(c_b, c_t);
+    int c_n = pr_n, c_first = pr_t;
+    int64_t c_base = have_c ? tile_base(c_b, c_t) : 0;
+    int stage = 0;
+    for (;;) {
+        const bool have_n = have_c;
+        const int n_b = c_b, n_t = c_t, n_n = c_n, n_first = c_first;
+        if (have_n) {
+            issue(n_b, n_t, stage ^ 1, c_base);
+            have_c = next_tile(c_b, c_t);
+            c_n = pr_n;
+            c_first = pr_t;
+            if (have_c) c_base = tile_base(c_b, c_t);
+        }
+        // Row change: this row's queries and weights (a wait the compiler
+        // sees: the loop then finds them complete and adds no memory wait of
+        // its own, which next to the LDS-DMA copies it could only make a full
+        // drain on every tile).
+        if (a_b != loaded_b) {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) sbuf[i] = 0.0f;
-        float cur = 0.0f;
-        int m = 0, jb = 0;
-        auto push = [&]() {
+            for (int t = 0; t < IDX_TILES; ++t) {
+                const int head = 32 * t + col;
+                const uint16_t *qp = idx_q + ((int64_t)a_b * idx_heads + head) * IDX_DIM + half * (IDX_DIM / 2);
 #pragma unroll
-            for (int i = 0; i + 1 < NB; ++i) sbuf[i] = sbuf[i + 1];
-            sbuf[NB - 1] = cur;
-        };
-        // One burst: pair p goes to tiles jb + 2p (+1), i.e. 256 contiguous
-        // bytes per store; the upper half of an incomplete last pair is masked.
-        auto flush = [&]() {
-            if (m & 1) push();
-            const int npairs = (m + 1) >> 1;
-            float *o = out + (int64_t)(t0 + jb + half) * 32 + col;
-#pragma unroll
-            for (int k = 0; k < NB; ++k) {  // k-th newest pair
-                const int pr = npairs - 1 - k;
-                if (k < npairs && (half == 0 || 2 * pr + 1 < m)) o[64 * pr] = sbuf[NB - 1 - k];
+                for (int ks = 0; ks < KS; ++ks)
+                    qa[t][ks] = head < idx_heads ? as_bf16x8(load16(qp + 8 * ks)) : as_bf16x8(u32x4{0, 0, 0, 0});
             }
-            jb += m;
-            m = 0;
-        };
+            // head weights into this wave's LDS slot (read back per tile: held in
+            // registers they would cost 16 per head tile)
+            for (int h = lane; h < 32 * IDX_TILES; h += 64)
+                wlds[wave][h] = h < idx_heads ? idx_w[(int64_t)a_b * idx_heads + h] : 0.0f;
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            loaded_b = a_b;
+        }
+        // (visible to the compiler, so that it knows the claims requested
+        // before these copies have arrived; the fence keeps the tile reads below)
+        if (have_n) __builtin_amdgcn_s_waitcnt(waitcnt_vm(DMA));
+        else __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        asm volatile("" ::: "memory");
+        if (need_claim) {
+            if (lane == 0) claim = atomicAdd(&blk_claims, 1);
+            need_claim = false;
+        }
+
+        const int ctx = ctx_lens[a_b];
+        const uint8_t *tb = my + stage * TILE;
+        // all B operands of the tile first, so the LDS reads overlap each other
+        bf16x8 kb[KS];
 #pragma unroll
-        for (int j = 0; j < kScanStages - 1; ++j)
-            if (j < n) issue(t0 + j, j, tile_base(t0 + j));
-        int64_t base_next = tile_base(t0 + kScanStages - 1);
-        for (int j = 0; j < n; ++j) {
-            const int stage = j % kScanStages;
-            if (j + kScanStages - 1 < n) {
-                issue(t0 + j + kScanStages - 1, (j + kScanStages - 1) % kScanStages, base_next);
-                base_next = tile_base(t0 + j + kScanStages);
-                scan_wait<DMA>();
-            } else {
-                wait_vmcnt<0>();
-            }
-            const uint8_t *tb = my + stage * TILE;
-            // all B operands of the tile first, so the LDS reads overlap each other
-            bf16x8 kb[KS];
+        for (int ks = 0; ks < KS; ++ks)
+            kb[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff + (((half * KS + ks) ^ kx) * 16)));
+        // two accumulators per head tile (even / odd steps) halve the dependent MFMA chain
+        f32x16 acc[IDX_TILES][2];
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
-                kb[ks] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + koff + (((half * KS + ks) ^ kx) * 16)));
-            // two accumulators per head tile (even / odd steps) halve the dependent MFMA chain
-            f32x16 acc[IDX_TILES][2];
+        for (int t = 0; t < IDX_TILES; ++t) acc[t][0] = acc[t][1] = f32x16{};
 #pragma unroll
-            for (int t = 0; t < IDX_TILES; ++t) acc[t][0] = acc[t][1] = f32x16{};
+        for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks)
+            for (int t = 0; t < IDX_TILES; ++t) acc[t][ks & 1] = mfma_32x32x16(qa[t][ks], kb[ks], acc[t][ks & 1]);
+        float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+        // head weights from LDS (an opaque lane id keeps these reads inside
+        // the loop instead of 16 registers per head tile)
+        int wl = lane;
+        asm volatile("" : "+v"(wl));
+        const float *wrow = &wlds[wave][4 * (wl >> 5)];
+        auto head_sum = [&](auto relu_on) {
 #pragma unroll
-                for (int t = 0; t < IDX_TILES; ++t) acc[t][ks & 1] = mfma_32x32x16(qa[t][ks], kb[ks], acc[t][ks & 1]);
-            float part[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-            // head weights from LDS (an opaque lane id keeps these reads inside
-            // the loop instead of 16 registers per head tile)
-            int wl = lane;
-            asm volatile("" : "+v"(wl));
-            const float *wrow = &wlds[wave][4 * (wl >> 5)];
-            auto head_sum = [&](auto relu_on) {
+            for (int t = 0; t < IDX_TILES; ++t)
 #pragma unroll
-                for (int t = 0; t < IDX_TILES; ++t)
+                for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 w4 = *reinterpret_cast<const f32x4 *>(wrow + 32 * t + 8 * gq);
 #pragma unroll
-                    for (int g = 0; g < 4; ++g) {
-                        const f32x4 w4 = *reinterpret_cast<const f32x4 *>(wrow + 32 * t + 8 * g);
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float d = acc[t][0][4 * g + e] + acc[t][1][4 * g + e];
-                            if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
-                            part[e] = fmaf(w4[e], d, part[e]);
-                        }
+                    for (int e = 0; e < 4; ++e) {
+                        float d = acc[t][0][4 * gq + e] + acc[t][1][4 * gq + e];
+                        if constexpr (decltype(relu_on)::value) d = fmaxf(d, 0.0f);
+                        part[e] = fmaf(w4[e], d, part[e]);
                     }
-            };
-            if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
-            else head_sum(std::false_type{});
-            const float p = (part[0] + part[1]) + (part[2] + part[3]);
-            const float tot = add_wave_halves(p);
-            const int tt = t0 + j;
-            const int s = tt * 32 + col;
-            // This tile's scores into the buffer (slots at or past ctx get values
-            // nothing reads; every slot lies inside the row's score stride, which
-            // is rounded up from the largest context).
-            cur = half == (m & 1) ? tot + 0.0f : cur;
-            ++m;
-            if (!(m & 1)) push();
-            if (m == 2 * NB) flush();
-            // The tile's score range, for the range-binned top-k histogram.  Lane
-            // tt % 16 keeps it, and a group of 16 tiles is written as one whole
-            // 128-byte line (partial lines only at segment ends) instead of one
-            // 8-byte store per tile.
-            const f32x2 mm = minmax32_uniform(tot + 0.0f, s < ctx);
-            if (lane == (tt & 15)) {
-                mm_lo = mm[0];
-                mm_hi = mm[1];
-            }
-            if ((tt & 15) == 15 || j == n - 1) {
-                const int g0 = tt & ~15, first = (g0 > t0 ? g0 : t0) - g0;
-                if (lane >= first && lane <= (tt & 15))
-                    tile_mm[(int64_t)b * mm_stride + g0 + lane] = f32x2{mm_lo, mm_hi};
-            }
+                }
+        };
+        if (relu) head_sum(std::true_type{});  // (uniform branch, outside the element loop)
+        else head_sum(std::false_type{});
+        const float p = (part[0] + part[1]) + (part[2] + part[3]);
+        const float tot = add_wave_halves(p);
+        // The tile's scores and its score range (for the range-binned top-k
+        // histogram) into the buffer.  Slots at or past ctx get values nothing
+        // reads; every slot lies inside the row's score stride, which is
+        // rounded up from the largest context.
+        const int second = a_t - a_first;  // 0 or 1 within its pair
+        const f32x2 mmt = minmax32_uniform(tot + 0.0f, a_t * 32 + col < ctx);
+        cur = half == second ? tot + 0.0f : cur;
+        if (second == 0) {
+            cur_mm[0] = mmt[0];
+            cur_mm[1] = mmt[1];
+        } else {
+            cur_mm[2] = mmt[0];
+            cur_mm[3] = mmt[1];
         }
-        if (m) flush();
-        t_cur = row_first + t1;
-        row_first += nt;
-        ++b;
-        while (t_cur < t_end && ((ctx_lens[b] + 31) >> 5) == 0) ++b;  // skip empty rows
+        if (second + 1 == a_n) {  // the pair is complete
+            push(a_b, a_first, a_n);
+            if (m == NB) flush();
+        }
+        if (!have_n) break;
+        a_b = n_b;
+        a_t = n_t;
+        a_n = n_n;
+        a_first = n_first;
+        stage ^= 1;
     }
+    if (m) flush();
 }
 
 // ----------------------------------------------------------------- prefill --
