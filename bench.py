@@ -92,18 +92,52 @@ def run_decode(args, torch, sa, synth):
     n_marks = call([])[3]
     kernels = ["indexer", "topk", "attention", "merge"][:n_marks - 1] if max_ctx > p.topk else \
         ["topk", "attention", "merge"][:n_marks - 1]
+    plain = lambda: sa.sparse_attn_decode(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], workspace=ws,
+                                          outputs=outs)
     log(f"warmup {args.warmup} steps ({n_marks - 1} kernels per step: {', '.join(kernels)})")
     for _ in range(args.warmup):
-        call([])
+        plain()
     torch.cuda.synchronize()
-    events = [[sa.HipEvent() for _ in range(n_marks)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
+    # The timed steps are plain calls: an event recorded between two kernels
+    # holds the next one back, so per-stage times come from separate steps.
     t0 = time.perf_counter()
-    for s in range(args.steps):
-        call(events[s])
+    for _ in range(args.steps):
+        plain()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
+    # The same step with each sequence's current token appended to the cache
+    # first (sparse_attn_decode_append; the same token every step, so the cache
+    # holds the same values throughout), timed like the plain step right after it.
+    append_ms = None
+    if args.append_steps > 0:
+        nk_np, ni_np = synth.new_tokens(w)
+        nk = torch.from_numpy(nk_np).view(torch.bfloat16).cuda()
+        ni = torch.from_numpy(ni_np).view(torch.bfloat16).cuda()
+        app = lambda: sa.sparse_attn_decode_append(p, d["cache"], max_ctx, nk, ni, d["q"], d["idx_q"], d["idx_w"],
+                                                   workspace=ws, outputs=outs)
+        for _ in range(args.warmup):
+            app()
+        torch.cuda.synchronize()
+        ta = time.perf_counter()
+        for _ in range(args.append_steps):
+            app()
+        torch.cuda.synchronize()
+        append_ms = (time.perf_counter() - ta) * 1e3 / args.append_steps
+        tb = time.perf_counter()
+        for _ in range(args.steps):
+            plain()
+        torch.cuda.synchronize()
+        again = (time.perf_counter() - tb) * 1e3 / args.steps
+        log(f"decode with append: {append_ms:.3f} ms/step (plain step again after it: {again:.3f} ms)")
+    events = [[sa.HipEvent() for _ in range(n_marks)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for s in range(args.steps):
+        call(events[s])
+    torch.cuda.synchronize()
+    ms_marked = (time.perf_counter() - t2) * 1e3 / args.steps
+    log(f"steps with an event after every kernel: {ms_marked:.3f} ms/step")
     per_kernel = {k: [] for k in kernels}
     for ev in events:
         for i, k in enumerate(kernels):
@@ -125,7 +159,7 @@ def run_decode(args, torch, sa, synth):
         del flush
     alg = decode_algorithmic(w)
     return w, dict(ms=ms, stages=stages, cold_ms=statistics.median(cold) if cold else None, alg=alg,
-                   per_kernel=per_kernel)
+                   per_kernel=per_kernel, append_ms=append_ms, ms_marked=ms_marked)
 
 
 def run_other_decodes(args, torch, sa, synth, names):
@@ -133,7 +167,7 @@ def run_other_decodes(args, torch, sa, synth, names):
     res = {}
     for name in names:
         sub = argparse.Namespace(**vars(args))
-        sub.workload, sub.steps, sub.warmup, sub.flush_steps = name, 10, 3, 0
+        sub.workload, sub.steps, sub.warmup, sub.flush_steps, sub.append_steps = name, 20, 20, 0, 0
         w, dec = run_decode(sub, torch, sa, synth)
         B = len(w["context_lens"])
         res[name] = {"ms_per_step": round(dec["ms"], 4), "tokens_per_s": round(B / (dec["ms"] / 1e3), 1),
@@ -284,10 +318,15 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; a few milliseconds of work leave the clocks below their "
+                         "loaded level, so the default warms up for about 30 ms")
     ap.add_argument("--workload", default="decode_b64_ctx16k_128k")
     ap.add_argument("--flush-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush")
     ap.add_argument("--prefill-steps", type=int, default=2)
+    ap.add_argument("--append-steps", type=int, default=20,
+                    help="steps of the decode call that also appends each sequence's current token to the "
+                         "cache (sparse_attn_decode_append), timed like the plain steps right after them")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--other-workloads", default="none",
@@ -364,9 +403,15 @@ def main():
         "hbm_frac": round(alg["bytes"] / (dec["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg["bytes"],
         "stages_us": {k: round(v * 1e3, 2) for k, v in dec["stages"].items()},
+        "ms_per_step_with_stage_events": round(dec["ms_marked"], 4),
         "cold_cache_ms_per_step": round(dec["cold_ms"], 4) if dec["cold_ms"] else None,
         "roofline": roof,
     }
+    if dec.get("append_ms"):
+        # supplementary: the same step appending each sequence's current token first
+        line["decode_append"] = {"ms_per_step": round(dec["append_ms"], 4),
+                                 "tokens_per_s": round(B / (dec["append_ms"] / 1e3), 1),
+                                 "added_us": round((dec["append_ms"] - dec["ms"]) * 1e3, 2)}
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, torch, sa, synth)
     others = [x for x in args.other_workloads.split(",") if x and x != "none" and x != args.workload]

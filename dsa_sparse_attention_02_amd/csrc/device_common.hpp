@@ -172,4 +172,52 @@ __device__ __forceinline__ uint32_t score_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The current token of each decode sequence written into the paged cache
+// ("Engineering Practices for Day-0 Adaptation of Million-Token Context Models
+// on Domestic AI Chips", Four Key Layers items 2 and 3: block-level
+// incremental cache updates during decode, merged into the attention kernels'
+// launches).  Sequence b's token sits at position context_lens[b] - 1; its
+// latent row new_kv[b] and indexer key new_idx_k[b] go to that position's
+// physical slot.  new_kv == nullptr: nothing to append.
+struct AppendArgs {
+    const uint16_t *new_kv;      // [batch][qk_dim]
+    const uint16_t *new_idx_k;   // [batch][idx_dim]
+    uint16_t *kv;                // the cache pools, written at one slot per sequence
+    uint16_t *idx_k;
+    const int32_t *block_table;  // [seqs][max_blocks]
+    const int32_t *ctx_lens;
+    int64_t num_blocks;
+    int max_blocks, bs_log2, qk_dim, idx_dim;
+};
+
+// Physical row of sequence b's current token, or -1 (no token, or an unmapped
+// block).
+__device__ __forceinline__ int64_t append_slot(const AppendArgs &ap, int b)
+{
+    const int ctx = ap.ctx_lens[b];
+    if (ctx <= 0) return -1;
+    const int s = ctx - 1;
+    const int blk = ap.block_table[(int64_t)b * ap.max_blocks + (s >> ap.bs_log2)];
+    if (blk < 0 || blk >= ap.num_blocks) return -1;
+    return ((int64_t)blk << ap.bs_log2) | (s & ((1 << ap.bs_log2) - 1));
+}
+
+// Sequence b's two new rows into the cache, 16 bytes per thread (threads
+// tid = 0 .. nthreads-1 of the calling group; row widths are multiples of 8).
+__device__ __forceinline__ void append_rows(const AppendArgs &ap, int b, int tid, int nthreads)
+{
+    if (!ap.new_kv) return;
+    const int64_t slot = append_slot(ap, b);
+    if (slot < 0) return;
+    const int nkv = ap.qk_dim / 8, nik = ap.idx_dim / 8;
+    for (int i = tid; i < nkv + nik; i += nthreads) {
+        if (i < nkv)
+            *reinterpret_cast<u32x4 *>(ap.kv + slot * ap.qk_dim + 8 * i) =
+                load16(ap.new_kv + (int64_t)b * ap.qk_dim + 8 * i);
+        else
+            *reinterpret_cast<u32x4 *>(ap.idx_k + slot * ap.idx_dim + 8 * (i - nkv)) =
+                load16(ap.new_idx_k + (int64_t)b * ap.idx_dim + 8 * (i - nkv));
+    }
+}
+
 }  // namespace sa

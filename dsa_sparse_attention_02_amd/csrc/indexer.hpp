@@ -85,7 +85,7 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
     const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int max_blocks,
     int bs_log2, const int32_t *__restrict__ ctx_lens, int batch, const uint16_t *__restrict__ idx_q,
     const float *__restrict__ idx_w, int idx_heads, int relu, float *__restrict__ scores,
-    int64_t score_stride, f32x2 *__restrict__ tile_mm, int64_t mm_stride)
+    int64_t score_stride, f32x2 *__restrict__ tile_mm, int64_t mm_stride, const AppendArgs ap)
 {
     constexpr int KS = IDX_DIM / 16;            // MFMA steps per key row
     constexpr int PIECES = IDX_DIM / 8;         // 16-byte pieces per key row
@@ -319,6 +319,15 @@ __global__ __launch_bounds__(64 * kScanWavesPerBlock) void idx_score_decode_kern
         }
 
         const int ctx = ctx_lens[a_b];
+        // Appending: the row's current token is scored with its new key (the
+        // top-k kernel that follows writes it into the cache), so the landed
+        // tile holding position ctx - 1 gets that key in its LDS image.
+        if (ap.new_kv && ((ctx - 1) >> 5) == a_t) {  // (wave-uniform)
+            const int rr = (ctx - 1) & 31;
+            if (lane < PIECES)
+                *reinterpret_cast<u32x4 *>(my + stage * TILE + 16 * (PIECES * rr + (lane ^ (rr & SW)))) =
+                    load16(ap.new_idx_k + (int64_t)a_b * IDX_DIM + 8 * lane);
+        }
         const uint8_t *tb = my + stage * TILE;
         // all B operands of the tile first, so the LDS reads overlap each other
         bf16x8 kb[KS];

@@ -220,29 +220,32 @@ struct StageMarks {
 template <int D, int T>
 void launch_idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *idx_q,
                        const float *idx_w, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, int blocks,
-                       hipStream_t st)
+                       const AppendArgs &ap, hipStream_t st)
 {
     const dim3 grid(blocks), block(64 * kScanWavesPerBlock);
     if (p->block_size >= 32)
         hipLaunchKernelGGL((idx_score_decode_kernel<D, T, true>), grid, block, 0, st, (const uint16_t *)c->idx_k,
                            c->block_table, c->max_blocks_per_seq, ilog2(p->block_size), c->context_lens, batch,
-                           (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, mm, mm_stride);
+                           (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, mm, mm_stride,
+                           ap);
     else
         hipLaunchKernelGGL((idx_score_decode_kernel<D, T, false>), grid, block, 0, st, (const uint16_t *)c->idx_k,
                            c->block_table, c->max_blocks_per_seq, ilog2(p->block_size), c->context_lens, batch,
-                           (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, mm, mm_stride);
+                           (const uint16_t *)idx_q, idx_w, p->idx_heads, p->idx_relu, scores, stride, mm, mm_stride,
+                           ap);
 }
 
 void idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *idx_q, const float *idx_w,
-                float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, int blocks, hipStream_t st)
+                float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, int blocks, const AppendArgs &ap,
+                hipStream_t st)
 {
     const bool two = p->idx_heads > 32;
     if (p->idx_dim == 128) {
-        if (two) launch_idx_decode<128, 2>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
-        else launch_idx_decode<128, 1>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
+        if (two) launch_idx_decode<128, 2>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, ap, st);
+        else launch_idx_decode<128, 1>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, ap, st);
     } else {
-        if (two) launch_idx_decode<32, 2>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
-        else launch_idx_decode<32, 1>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, st);
+        if (two) launch_idx_decode<32, 2>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, ap, st);
+        else launch_idx_decode<32, 1>(p, c, batch, idx_q, idx_w, scores, stride, mm, mm_stride, blocks, ap, st);
     }
 }
 
@@ -328,14 +331,38 @@ AttnArgs attn_args(const sa_params *p, const sa_paged_cache *c, const void *q, c
     return a;
 }
 
+// No append (new_kv == nullptr).
+AppendArgs no_append() { return AppendArgs{}; }
+
+// Append of the current tokens new_kv / new_idx_k into the cache of c.
+AppendArgs append_args(const sa_params *p, const sa_paged_cache *c, const void *new_kv, const void *new_idx_k)
+{
+    AppendArgs ap{};
+    ap.new_kv = (const uint16_t *)new_kv;
+    ap.new_idx_k = (const uint16_t *)new_idx_k;
+    ap.kv = (uint16_t *)const_cast<void *>(c->kv);      // (the one call that writes the cache)
+    ap.idx_k = (uint16_t *)const_cast<void *>(c->idx_k);
+    ap.block_table = c->block_table;
+    ap.ctx_lens = c->context_lens;
+    ap.num_blocks = c->num_blocks;
+    ap.max_blocks = c->max_blocks_per_seq;
+    ap.bs_log2 = ilog2(p->block_size);
+    ap.qk_dim = p->qk_dim;
+    ap.idx_dim = p->idx_dim;
+    return ap;
+}
+
+// Scan (when some row has more than topk keys), then top-k.  With an append,
+// the scan scores each row's current token with its new indexer key and the
+// top-k launch writes both new rows into the cache (before the attention).
 void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *idx_q,
                    const float *idx_w, int32_t *topk_idx, void *ws, const DecodePlan &d, hipStream_t st,
-                   StageMarks *mk)
+                   StageMarks *mk, const AppendArgs &ap = no_append())
 {
     float *scores = (float *)((char *)ws + d.off_scores);
     f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
     if (max_ctx > p->topk) {
-        idx_decode(p, c, batch, idx_q, idx_w, scores, d.score_stride, mm, d.mm_stride, d.scan_blocks, st);
+        idx_decode(p, c, batch, idx_q, idx_w, scores, d.score_stride, mm, d.mm_stride, d.scan_blocks, ap, st);
         if (mk) mk->mark();
     }
     if (d.mb_chunks > 0) {
@@ -344,7 +371,7 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
         uint32_t *counts = hist + (size_t)batch * 3 * kMbBins;
         const dim3 grid(d.mb_chunks, batch);
         const int32_t *cl = c->context_lens;
-        hipLaunchKernelGGL(topk_mb_init_kernel, dim3(batch), dim3(256), 0, st, p->topk, mst, hist);
+        hipLaunchKernelGGL(topk_mb_init_kernel, dim3(batch), dim3(256), 0, st, p->topk, mst, hist, ap);
         hipLaunchKernelGGL(topk_mb_hist_kernel<0>, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk, mst, hist);
         hipLaunchKernelGGL(topk_mb_pick_kernel<0>, dim3(batch), dim3(kTopkThreads), 0, st, cl, p->topk, mst, hist);
         hipLaunchKernelGGL(topk_mb_hist_kernel<1>, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk, mst, hist);
@@ -357,7 +384,7 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
                            mst, counts, d.mb_chunks, topk_idx);
     } else {
         hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, 0, c->context_lens, 0, p->topk, topk_idx);
+                           d.mm_stride, 0, c->context_lens, 0, p->topk, topk_idx, ap);
     }
     if (mk) mk->mark();
 }
@@ -390,7 +417,8 @@ void select_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, i
             if (mk) mk->mark();
         }
         hipLaunchKernelGGL(topk_rows_kernel, dim3(nr), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, 1, (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk);
+                           d.mm_stride, 1, (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk,
+                           no_append());
         if (mk) mk->mark();
     }
 }
@@ -485,7 +513,8 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *c,
 
 static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
-                             float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk)
+                             float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk,
+                             const void *new_kv = nullptr, const void *new_idx_k = nullptr)
 {
     sa_status s = check_decode(p, c, batch, max_ctx, true, true);
     if (s != SA_OK) return s;
@@ -498,7 +527,8 @@ static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_
         mk->stream = st;
         mk->mark();
     }
-    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, st, mk);
+    const AppendArgs ap = new_kv ? append_args(p, c, new_kv, new_idx_k) : no_append();
+    select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, st, mk, ap);
     attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, st, mk);
     return launched();
 }
@@ -509,6 +539,16 @@ sa_status sparse_attn_decode(const sa_params *p, const sa_paged_cache *c, int32_
 {
     return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
                        nullptr);
+}
+
+sa_status sparse_attn_decode_append(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                    const void *new_kv, const void *new_idx_k, const void *q, const void *idx_q,
+                                    const float *idx_w, int32_t *topk_idx, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream)
+{
+    if (!new_kv || !new_idx_k) return SA_ERR_NULL;
+    return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
+                       nullptr, new_kv, new_idx_k);
 }
 
 sa_status sparse_attn_decode_profiled(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,

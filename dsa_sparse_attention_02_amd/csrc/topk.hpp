@@ -221,10 +221,12 @@ __device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int3
 // (mm_per_row == 0) or mm_per_row entries covering the whole row.
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
     const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
-    int mm_per_row, const int32_t *__restrict__ ctx_lens, int n_base, int k, int32_t *__restrict__ out)
+    int mm_per_row, const int32_t *__restrict__ ctx_lens, int n_base, int k, int32_t *__restrict__ out,
+    const AppendArgs ap)
 {
     __shared__ TopkShared sh;
     const int r = blockIdx.x;
+    append_rows(ap, r, threadIdx.x, kTopkThreads);  // (decode row r = sequence r; before the attention reads it)
     const int n = ctx_lens ? ctx_lens[r] : n_base + r + 1;
     int32_t *o = out + (int64_t)r * k;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
@@ -414,9 +416,10 @@ struct MbRowState {
 };
 
 __global__ __launch_bounds__(256) void topk_mb_init_kernel(int k, MbRowState *__restrict__ st,
-                                                           uint32_t *__restrict__ hist)
+                                                           uint32_t *__restrict__ hist, const AppendArgs ap)
 {
     const int r = blockIdx.x;
+    append_rows(ap, r, threadIdx.x, 256);
     for (int i = threadIdx.x; i < 3 * kMbBins; i += 256) hist[(int64_t)r * 3 * kMbBins + i] = 0u;
     if (threadIdx.x == 0) st[r] = MbRowState{0u, 0u, (uint32_t)k, 0u};
 }

@@ -22,7 +22,7 @@ EXPORTS = (
     "sa_abi_version", "sa_status_string",
     "sa_decode_workspace_size", "sparse_attn_decode", "sparse_attn_select_decode", "sparse_attn_attend_decode",
     "sa_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_select_prefill", "sparse_attn_attend_prefill",
-    "sparse_attn_decode_profiled", "sparse_attn_prefill_profiled",
+    "sparse_attn_decode_profiled", "sparse_attn_prefill_profiled", "sparse_attn_decode_append",
 )
 
 
@@ -73,6 +73,7 @@ def lib():
                                                            ctypes.POINTER(i32)]),
             "sparse_attn_prefill_profiled": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P, P, i32,
                                                             ctypes.POINTER(i32)]),
+            "sparse_attn_decode_append": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -211,6 +212,28 @@ def sparse_attn_decode(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx
     _check(lib().sparse_attn_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
                                     idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
                                     _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode")
+    return topk_idx, out, lse
+
+
+def sparse_attn_decode_append(p: Params, cache: PagedCache, max_ctx: int, new_kv, new_idx_k, q, idx_q, idx_w, *,
+                              want_lse=True, workspace=None, outputs=None, stream=None):
+    """sparse_attn_decode after writing each sequence's current token (position
+    context_lens[b] - 1) into the cache: new_kv [B][qk_dim] and new_idx_k
+    [B][idx_dim] (bf16) overwrite that position's slot in cache.kv / cache.idx_k.
+    Returns (topk_idx, out, lse) as sparse_attn_decode."""
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    _dev(new_kv, "new_kv", _bf16_types(), (B, p.qk_dim))
+    _dev(new_idx_k, "new_idx_k", _bf16_types(), (B, p.idx_dim))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    _check(lib().sparse_attn_decode_append(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
+                                           new_kv.data_ptr(), new_idx_k.data_ptr(), q.data_ptr(), idx_q.data_ptr(),
+                                           idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
+                                           ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode_append")
     return topk_idx, out, lse
 
 

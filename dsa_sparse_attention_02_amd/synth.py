@@ -41,7 +41,7 @@ BF16_NAN = np.uint16(0x7FC0)
 BF16_POISON_IDX = np.uint16(0x4280)  # 64.0 in bf16
 SPARE_BLOCKS = 8
 
-T_Q, T_KV, T_IDX_Q, T_IDX_K, T_IDX_W, T_PERM, T_CTX = range(7)
+T_Q, T_KV, T_IDX_Q, T_IDX_K, T_IDX_W, T_PERM, T_CTX, T_NEW_KV, T_NEW_IDX_K = range(9)
 
 
 @dataclass(frozen=True)
@@ -229,6 +229,18 @@ def make(spec: Spec, keep_logical: bool = False, workers: Optional[int] = None) 
         out["kv_logical"] = kv_log
         out["idx_k_logical"] = ik_log
     return out
+
+
+def new_tokens(w: dict):
+    """The current token of each decode sequence, to be appended: its latent
+    row (bf16 N(0,1), [B][qk_dim]) and indexer key (integers in
+    [-idx_int_max, idx_int_max] as bf16, [B][idx_dim]), drawn like the cache
+    rows from their own streams."""
+    spec, sh = w["spec"], w["shape"]
+    B = spec.batch
+    new_kv = _normal_bf16(spec.seed, (T_NEW_KV,), B * sh.qk_dim).reshape(B, sh.qk_dim)
+    new_idx_k = _ints_bf16(spec.seed, (T_NEW_IDX_K,), B * sh.idx_dim, sh.idx_int_max).reshape(B, sh.idx_dim)
+    return new_kv, new_idx_k
 
 
 def small_decode(name: str, shape: Shape, ctx: Sequence[int], seed: int = 7, **kw) -> Spec:

@@ -145,6 +145,30 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *ca
                                     const int32_t *topk_idx, void *out, float *lse,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
+/* sparse_attn_decode with the current token of every sequence appended to the
+ * cache first: the cache update merged into the decode launches and the
+ * block-level incremental update of the paged cache during decode
+ * ("Engineering Practices for Day-0 Adaptation of Million-Token Context
+ * Models on Domestic AI Chips", Four Key Layers items 2 and 3).
+ *   new_kv     (device) bf16 [batch][qk_dim]:  latent row of each current token
+ *   new_idx_k  (device) bf16 [batch][idx_dim]: its indexer key
+ * Sequence b's current token is position context_lens[b] - 1 (context_lens
+ * already counts it); its physical slot, block_table[b][pos / bs] * bs +
+ * pos % bs, is overwritten in cache->kv and cache->idx_k (the one call that
+ * writes through the cache pointers, declared const for the read-only calls).
+ * Sequences with context_lens[b] == 0, or whose block-table entry for the
+ * position is outside [0, num_blocks), append nothing.  The scores, indices,
+ * output and lse are those of sparse_attn_decode on the updated cache; no
+ * kernel is added: the indexer scan scores each current token with its new
+ * key, and the top-k launch, which precedes the attention, writes both rows.
+ * Other arguments and errors as for sparse_attn_decode; null new_kv or
+ * new_idx_k -> SA_ERR_NULL.  Calls that overlap on one cache race. */
+sa_status sparse_attn_decode_append(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
+                                    int32_t max_ctx, const void *new_kv, const void *new_idx_k,
+                                    const void *q, const void *idx_q, const float *idx_w,
+                                    int32_t *topk_idx, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+
 /* Profiling variant of sparse_attn_decode: identical work, and additionally
  * records caller-created HIP events (hipEvent_t handles in events[0 ..
  * num_events)) on `stream`: events[0] before the first kernel and events[i]

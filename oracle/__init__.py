@@ -43,6 +43,8 @@ def lib():
                                   P, i64, P]
         L.oracle_topk.restype = i64
         L.oracle_topk.argtypes = [P, i64, i64, P]
+        L.oracle_append.restype = i64
+        L.oracle_append.argtypes = [i64, i64, i64, i64, i64, P, P, P, i64, P, P, P]
         L.oracle_max_threads.restype = ctypes.c_int
         L.oracle_set_threads.argtypes = [ctypes.c_int]
         _lib = L
@@ -93,6 +95,28 @@ def run(w: dict, rows=None, want_scores: bool = False, stage_seconds=None):
     if sc is not None:
         res["scores"] = sc
     return res
+
+
+def append(w: dict, new_kv: np.ndarray, new_idx_k: np.ndarray) -> dict:
+    """Decode workload `w` with each sequence's current token (position
+    context_lens[b] - 1) replaced by new_kv[b] / new_idx_k[b] in copies of its
+    cache pools.  Returns the new workload dict (the input is left as it was)."""
+    sh = w["shape"]
+    assert w["mode"] == "decode"
+    out = dict(w)
+    out["kv"] = np.array(w["kv"], dtype=np.uint16, copy=True, order="C")
+    out["idx_k"] = np.array(w["idx_k"], dtype=np.uint16, copy=True, order="C")
+    nk = np.ascontiguousarray(new_kv, dtype=np.uint16)
+    ni = np.ascontiguousarray(new_idx_k, dtype=np.uint16)
+    bt = np.ascontiguousarray(w["block_table"], dtype=np.int32)
+    ctx = np.ascontiguousarray(w["context_lens"], dtype=np.int32)
+    B = len(ctx)
+    assert nk.shape == (B, sh.qk_dim) and ni.shape == (B, sh.idx_dim)
+    lib().oracle_append(B, sh.qk_dim, sh.idx_dim, sh.block_size, out["kv"].shape[0], _p(out["kv"]),
+                        _p(out["idx_k"]), _p(bt), bt.shape[1], _p(ctx), _p(nk), _p(ni))
+    out.pop("kv_logical", None)
+    out.pop("idx_k_logical", None)
+    return out
 
 
 def max_threads() -> int:

@@ -43,6 +43,14 @@
  *     order is not a softmax and is read as standard softmax attention) and the
  *     decode pseudocode.
  *
+ * Appending (decode): before step 1 the current token of sequence b, position
+ * ctx_b - 1, is written into the cache at its physical slot (step 2's
+ * addressing): its latent row and its indexer key replace the slot's contents.
+ * "Engineering Practices for Day-0 Adaptation of Million-Token Context Models
+ * on Domestic AI Chips", Four Key Layers item 2 (block-level incremental cache
+ * updates during decode) and item 3 (the update merged with the decode
+ * attention).
+ *
  * Precision: bf16 inputs are widened exactly; the indexer sums in fp32 with no
  * fused multiply-add (built with -ffp-contract=off); attention runs in double.
  */
@@ -242,6 +250,29 @@ int oracle_rows(int mode, int64_t num_heads, int64_t qk_dim, int64_t v_dim, int6
         if (!scores_out) free(scores);
     }
     return 0;
+}
+
+/* Appends the current token of every decode sequence: for b with ctx[b] > 0,
+ * position s = ctx[b] - 1 lives at physical slot block_table[b][s / bs] * bs +
+ * s % bs; its kv row (qk_dim entries) and idx_k row (idx_dim entries) are
+ * copied from new_kv[b] and new_idx_k[b].  A block-table entry outside
+ * [0, num_blocks) appends nothing.  Returns the number of rows appended. */
+int64_t oracle_append(int64_t batch, int64_t qk_dim, int64_t idx_dim, int64_t bs, int64_t num_blocks,
+                      uint16_t *kv, uint16_t *idx_k, const int32_t *block_table, int64_t max_blocks,
+                      const int32_t *ctx, const uint16_t *new_kv, const uint16_t *new_idx_k)
+{
+    int64_t appended = 0;
+    for (int64_t b = 0; b < batch; ++b) {
+        if (ctx[b] <= 0) continue;
+        const int64_t s = ctx[b] - 1;
+        const int64_t blk = block_table[b * max_blocks + s / bs];
+        if (blk < 0 || blk >= num_blocks) continue;
+        const int64_t slot = blk * bs + s % bs;
+        for (int64_t c = 0; c < qk_dim; ++c) kv[slot * qk_dim + c] = new_kv[b * qk_dim + c];
+        for (int64_t c = 0; c < idx_dim; ++c) idx_k[slot * idx_dim + c] = new_idx_k[b * idx_dim + c];
+        ++appended;
+    }
+    return appended;
 }
 
 int oracle_max_threads(void)

@@ -131,3 +131,27 @@ def test_workspace_sizes(L):
         sa.decode_workspace_size(p, 0, 10)
     with pytest.raises(sa.SparseAttnError):
         sa.prefill_workspace_size(p, 10, -1)
+
+
+def _decode_append(L, p, c, batch=2, max_ctx=256, ws_bytes=1 << 40, **ptrs):
+    args = dict(new_kv=FAKE, new_idx_k=FAKE, q=FAKE, idx_q=FAKE, idx_w=FAKE, topk=FAKE, out=FAKE, lse=None, ws=FAKE)
+    args.update(ptrs)
+    return L.sparse_attn_decode_append(ctypes.byref(p) if p is not None else None,
+                                       ctypes.byref(c) if c is not None else None, batch, max_ctx, args["new_kv"],
+                                       args["new_idx_k"], args["q"], args["idx_q"], args["idx_w"], args["topk"],
+                                       args["out"], args["lse"], args["ws"], ws_bytes, None)
+
+
+def test_decode_append_validation(L):
+    """The append call checks its two new-token pointers, then everything the
+    decode call checks, before any HIP call."""
+    p, c = _params(), _cache()
+    assert _decode_append(L, p, c, new_kv=None) == sa.SA_ERR_NULL
+    assert _decode_append(L, p, c, new_idx_k=None) == sa.SA_ERR_NULL
+    assert _decode_append(L, None, c) == sa.SA_ERR_NULL
+    assert _decode_append(L, p, c, q=None) == sa.SA_ERR_NULL
+    assert _decode_append(L, p, _cache(kv=None)) == sa.SA_ERR_NULL
+    assert _decode_append(L, p, c, batch=0) == sa.SA_ERR_SHAPE
+    assert _decode_append(L, p, c, max_ctx=257) == sa.SA_ERR_SHAPE
+    assert _decode_append(L, _params(idx_dim=64), c) == sa.SA_ERR_UNSUPPORTED
+    assert _decode_append(L, p, c, ws_bytes=16) == sa.SA_ERR_WORKSPACE

@@ -196,3 +196,39 @@ def test_parity_scan_score_bursts(dev):
     say("[gpu] scan score bursts, 6 rows of ~1M keys")
     w = synth.make(spec)
     compare(w, run_gpu(dev, w), rows=[0, 3, 5], tag="decode_scan_bursts")
+
+
+APPEND_CASES = {
+    "append_ragged": lambda: synth.small_decode("append_ragged", MLA,
+                                                [0, 1, 31, 32, 33, 64, 2047, 2048, 2049, 5000], seed=121),
+    "append_k64_ties": lambda: synth.small_decode("append_k64", MLA, [63, 64, 65, 4000], seed=122, topk=64,
+                                                  idx_int_max=1),
+    "append_tiny": lambda: synth.small_decode("append_tiny", synth.TINY, [0, 3, 16, 64, 65, 300], seed=123),
+    "append_decode_b32_ctx8k": lambda: synth.WORKLOADS["decode_b32_ctx8k"],
+}
+
+
+@pytest.mark.parametrize("name", list(APPEND_CASES))
+def test_decode_append_parity(dev, name):
+    """sparse_attn_decode_append against the oracle: the cache pools after the
+    call equal the oracle-appended pools bit for bit, and indices, output and
+    lse are those of the oracle on the appended cache."""
+    torch, sa = dev
+    spec = APPEND_CASES[name]()
+    say(f"[gpu] decode append {name}")
+    w = synth.make(spec)
+    new_kv, new_idx_k = synth.new_tokens(w)
+    w2 = oracle.append(w, new_kv, new_idx_k)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    nk = torch.from_numpy(new_kv).view(torch.bfloat16).cuda()
+    ni = torch.from_numpy(new_idx_k).view(torch.bfloat16).cuda()
+    res = sa.sparse_attn_decode_append(p, d["cache"], int(w["context_lens"].max()), nk, ni, d["q"], d["idx_q"],
+                                       d["idx_w"])
+    torch.cuda.synchronize()
+    kv_after = d["cache"].kv.view(torch.int16).cpu().numpy().view(np.uint16)
+    ik_after = d["cache"].idx_k.view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(kv_after, w2["kv"]), f"{name}: kv pool differs after the append"
+    assert np.array_equal(ik_after, w2["idx_k"]), f"{name}: idx_k pool differs after the append"
+    rows = None if w["rows"] <= 64 else [0, 1, 15, 31]
+    compare(w2, res, rows=rows, tag=f"{name} (appended)")

@@ -289,3 +289,50 @@ def test_generator_is_thread_count_independent():
     b = synth.make(spec, workers=4)
     for key in ("kv", "idx_k", "q", "idx_q", "idx_w", "block_table", "context_lens"):
         assert np.array_equal(a[key], b[key]), key
+
+
+@pytest.mark.parametrize("which", ["mla_decode_short", "tiny_decode"])
+def test_append_writes_the_current_token(which):
+    """The oracle's decode append, pinned to the logical view of the cache the
+    generator keeps (never paged): after appending, dense brute-force attention
+    and the exact integer indexer over the logical rows with row ctx - 1
+    replaced by the new token equal the oracle's results on the appended
+    (paged) workload; exactly one pool row per non-empty sequence changed."""
+    if which == "mla_decode_short":
+        spec = synth.small_decode("pin_append_mla", MLA_SMALL, [0, 1, 64, 65, 300], seed=41)
+    else:
+        spec = synth.small_decode("pin_append_tiny", replace(synth.TINY, topk=256), [0, 1, 15, 16, 17, 200],
+                                  seed=42)
+    w = synth.make(spec, keep_logical=True)
+    sh = w["shape"]
+    new_kv, new_idx_k = synth.new_tokens(w)
+    w2 = oracle.append(w, new_kv, new_idx_k)
+    ctx = w["context_lens"]
+    live = [b for b in range(len(ctx)) if ctx[b] > 0]
+    changed_kv = np.nonzero(np.any(w2["kv"].reshape(-1, sh.qk_dim) != w["kv"].reshape(-1, sh.qk_dim), axis=1))[0]
+    changed_ik = np.nonzero(np.any(w2["idx_k"].reshape(-1, sh.idx_dim) != w["idx_k"].reshape(-1, sh.idx_dim),
+                                   axis=1))[0]
+    assert len(changed_kv) == len(live) and len(changed_ik) == len(live)
+    new_rows = {tuple(new_kv[b]) for b in live}
+    assert all(tuple(w2["kv"].reshape(-1, sh.qk_dim)[i]) in new_rows for i in changed_kv)
+    # the logical view after the append
+    kv_log = [np.array(a, copy=True) for a in w["kv_logical"]]
+    ik_log = [np.array(a, copy=True) for a in w["idx_k_logical"]]
+    for b in live:
+        kv_log[b][ctx[b] - 1] = new_kv[b]
+        ik_log[b][ctx[b] - 1] = new_idx_k[b]
+    res = oracle.run(w2, want_scores=True)
+    scale = float(np.float32(sh.softmax_scale))
+    wl = dict(w2, idx_k_logical=ik_log)
+    for b in range(len(ctx)):
+        n = int(ctx[b])
+        assert n <= sh.topk
+        if n == 0:
+            assert np.all(res["topk"][b] == -1) and np.all(res["out"][b] == 0)
+            continue
+        o, lse = _dense_attention(_logical_f32(w["q"][b]), _logical_f32(kv_log[b][:n]), np.arange(n), scale,
+                                  sh.v_dim)
+        np.testing.assert_allclose(res["out"][b], o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][b], lse, rtol=1e-12, atol=1e-12)
+        x8 = _int_scores_x(wl, b, 8)
+        assert np.array_equal((res["scores"][b][:n].astype(np.float64) * 8).astype(np.int64), x8)
