@@ -260,7 +260,7 @@ def cpu_baseline(args, w):
                       f"budget); {el:.1f}s: indexer {stage[0]:.1f}s, sort {stage[1]:.1f}s, attention {stage[2]:.1f}s"}
 
 
-TRAFFIC_KERNEL = "idx_score_decode_kernel<128, 2>"
+TRAFFIC_KERNEL = "idx_score_decode_kernel<128, 2, true>"
 TRAFFIC_SOURCES = ["indexer.hpp", "device_common.hpp"]
 
 
