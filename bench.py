@@ -180,17 +180,56 @@ def run_other_decodes(args, torch, sa, synth, names):
     return res
 
 
-def run_prefill(args, torch, sa, synth):
-    spec = synth.WORKLOADS["prefill_L32k"]
+def prefill_pieces(w):
+    """(first row, rows, first position) of every non-empty sequence of a prefill workload."""
+    if w["mode"] == "varlen":
+        cu, qs = w["cu_seqlens"], w["q_starts"]
+        return [(int(cu[s]), int(cu[s + 1] - cu[s]), int(qs[s])) for s in range(len(qs)) if cu[s + 1] > cu[s]]
+    return [(0, int(w["rows"]), int(w["q_start"]))]
+
+
+def prefill_select_kernels(pieces, topk):
+    """Kernel names of the select stage in launch order (mirrors the library's
+    planning: chunks of rows whose fp32 scores take at most 1 GiB, in multiples
+    of 16 rows, at most 64 pieces of one sequence per chunk; the indexer only
+    where some row sees more than topk keys)."""
+    total = sum(n for _, n, _ in pieces)
+    stride = (max(q + n for _, n, q in pieces) + 63) // 64 * 64
+    chunk = min(max(16, ((1 << 30) // (stride * 4)) // 16 * 16), (total + 15) // 16 * 16)
+    names, r0 = [], 0
+    while r0 < total:
+        rmax, parts, r1 = min(total, r0 + chunk), [], r0
+        for a, n, q in pieces:
+            if a + n <= r0 or len(parts) == 64 or r1 >= rmax:
+                continue
+            lo, hi = max(r0, a), min(rmax, a + n)
+            parts.append(q + hi - a)  # the last position in the chunk, + 1
+            r1 = hi
+        if any(e > topk for e in parts):
+            names.append("indexer")
+        names.append("topk")
+        r0 = r1
+    return names
+
+
+def run_prefill(args, torch, sa, synth, name="prefill_L32k"):
+    spec = synth.WORKLOADS[name]
     log(f"generating {spec.name}")
     w = synth.make(spec)
     d = sa.to_device(w)
     p = sa.Params.from_shape(w["shape"])
-    L = spec.rows
-    ws = torch.empty(sa.prefill_workspace_size(p, L, 0), dtype=torch.uint8, device="cuda")
+    L = int(w["rows"])
     outs = sa._outputs(p, L, "cuda", True)
-    call = lambda ev: sa.sparse_attn_prefill_profiled(p, d["cache"], 0, d["q"], d["idx_q"], d["idx_w"], ev,
-                                                      workspace=ws, outputs=outs)
+    if w["mode"] == "varlen":
+        ws = torch.empty(sa.prefill_varlen_workspace_size(p, w["cu_seqlens"], w["q_starts"]), dtype=torch.uint8,
+                         device="cuda")
+        call = lambda ev: sa.sparse_attn_prefill_varlen(p, d["cache"], w["cu_seqlens"], w["q_starts"], d["q"],
+                                                        d["idx_q"], d["idx_w"], workspace=ws, outputs=outs,
+                                                        events=ev)
+    else:
+        ws = torch.empty(sa.prefill_workspace_size(p, L, w["q_start"]), dtype=torch.uint8, device="cuda")
+        call = lambda ev: sa.sparse_attn_prefill_profiled(p, d["cache"], w["q_start"], d["q"], d["idx_q"],
+                                                          d["idx_w"], ev, workspace=ws, outputs=outs)
     n_marks = call([])[3]
     torch.cuda.synchronize()
     steps = max(1, args.prefill_steps)
@@ -202,12 +241,8 @@ def run_prefill(args, torch, sa, synth):
     ms = (time.perf_counter() - t0) * 1e3 / steps
     # launch order: per chunk [indexer?, topk], then attention (+ merge)
     sh = w["shape"]
-    plan_rows = sa_chunk_rows(sa, p, L)
-    names = []
-    for r0 in range(0, L, plan_rows):
-        if r0 + min(plan_rows, L - r0) > p.topk:
-            names.append("indexer")
-        names.append("topk")
+    pieces = prefill_pieces(w)
+    names = prefill_select_kernels(pieces, p.topk)
     n_attn = n_marks - 1 - len(names)
     if n_attn < 1:
         raise SystemExit(f"prefill marks ({n_marks}) do not match the chunk plan ({len(names)} select kernels)")
@@ -216,24 +251,19 @@ def run_prefill(args, torch, sa, synth):
     for ev in evs:
         for i, k in enumerate(names):
             tot[k] = tot.get(k, 0.0) + ev[i].elapsed_ms(ev[i + 1]) / steps
-    idx_flops = 2.0 * sh.idx_heads * sh.idx_dim * L * (L + 1) / 2
-    attn_flops = 2.0 * sh.num_heads * (sh.qk_dim + sh.v_dim) * sum(min(i + 1, sh.topk) for i in range(L))
+    # causal pairs: row i of a piece at position q + i sees q + i + 1 keys
+    pairs = sum(n * q + n * (n + 1) // 2 for _, n, q in pieces)
+    kept = sum(min(q + i + 1, sh.topk) for _, n, q in pieces for i in range(n))
+    idx_flops = 2.0 * sh.idx_heads * sh.idx_dim * pairs
+    attn_flops = 2.0 * sh.num_heads * (sh.qk_dim + sh.v_dim) * kept
     res = dict(workload=spec.name, ms_per_step=round(ms, 3), value=round(L / (ms / 1e3), 1), unit="query tokens/s",
                stages_ms={k: round(v, 3) for k, v in tot.items()},
                indexer_tflops=round(idx_flops / (tot.get("indexer", float("nan")) / 1e3) / 1e12, 1),
                attention_tflops=round(attn_flops / (tot["attention"] / 1e3) / 1e12, 1))
     res["indexer_mfma_frac"] = round(res["indexer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
     res["attention_mfma_frac"] = round(res["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
-    log(f"prefill: {ms:.2f} ms/step, stages {res['stages_ms']}")
+    log(f"{spec.name}: {ms:.2f} ms/step, stages {res['stages_ms']}")
     return res
-
-
-def sa_chunk_rows(sa, p, L):
-    """Rows per prefill indexer/top-k chunk (mirrors the library's planning: scores of
-    a chunk take at most 1 GiB, in multiples of 16 rows)."""
-    stride = (L + 63) // 64 * 64
-    rows = max(16, ((1 << 30) // (stride * 4)) // 16 * 16)
-    return min(rows, (L + 15) // 16 * 16)
 
 
 def cpu_baseline(args, w):
@@ -414,6 +444,7 @@ def main():
                                  "added_us": round((dec["append_ms"] - dec["ms"]) * 1e3, 2)}
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, torch, sa, synth)
+        line["prefill_varlen"] = run_prefill(args, torch, sa, synth, "prefill_varlen_8x4k")
     others = [x for x in args.other_workloads.split(",") if x and x != "none" and x != args.workload]
     if others:
         line["other_workloads"] = run_other_decodes(args, torch, sa, synth, others)

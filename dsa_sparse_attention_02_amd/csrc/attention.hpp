@@ -62,8 +62,8 @@ struct AttnArgs {
     float *lse;                  // splits == 1, nullable: [rows][H]
     int64_t num_blocks;
     int num_heads, max_blocks, bs_log2, k;
-    int decode;                  // 1: row r = sequence r, limit ctx_lens[r]; 0: sequence 0, limit limit_base + r + 1
-    int limit_base;
+    int decode;                  // 1: row r = sequence r, limit ctx_lens[r]; 0: prefill rows of the pieces in rows_map
+    SeqMap rows_map;             // prefill: row r's sequence and position (limit = position + 1)
     int tokens_per_split, splits, out_bf16;
     float scale_log2;            // softmax_scale * log2(e)
 };
@@ -169,8 +169,15 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     const int wave = wave_uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     __builtin_assume(wave >= 0 && wave < NW);  // lets copy kinds resolve at compile time
     const int col = lane & 31, half = lane >> 5;
-    const int seq = a.decode ? r : 0;
-    const int limit = a.decode ? a.ctx_lens[r] : a.limit_base + r + 1;
+    int seq, limit;
+    if (a.decode) {
+        seq = r;
+        limit = a.ctx_lens[r];
+    } else {
+        const int pc = map_piece(a.rows_map, r);
+        seq = a.rows_map.bt_row[pc];
+        limit = a.rows_map.pos0[pc] + (r - a.rows_map.row0[pc]) + 1;
+    }
     const int j0 = split * a.tokens_per_split;
     const int cnt = max(0, min(a.tokens_per_split, a.k - j0));
     const int ntiles = (cnt + 31) / 32;

@@ -172,6 +172,36 @@ __device__ __forceinline__ uint32_t score_key(float f)
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Prefill over several sequences in one launch ("Day-0 Adaptation: Running
+// Trillion-Parameter Models on Domestic AI Accelerators", 3.3: the prefill
+// pathway; "Engineering Practices for Day-0 Adaptation of Million-Token Context
+// Models on Domestic AI Chips" names multi-sequence load balance for it).  The
+// rows of one launch are cut into pieces, each a run of consecutive query rows
+// of one sequence.  The map travels by value in the kernel arguments, so the
+// host builds it without a copy to the device.
+constexpr int kMapPieces = 64;
+struct SeqMap {
+    int npieces;
+    int first[kMapPieces + 1];  // ascending search keys: first row (top-k, attention) or first 16-row block (indexer)
+    int row0[kMapPieces];       // the piece's first row, counted from the launch's first row
+    int nrows[kMapPieces];
+    int pos0[kMapPieces];       // position of the piece's first row in its sequence
+    int bt_row[kMapPieces];     // the sequence's block-table row
+};
+
+// The piece whose key range holds `key` (wave-uniform: a search over kernel
+// arguments).
+__device__ inline int map_piece(const SeqMap &m, int key)
+{
+    int lo = 0, hi = m.npieces - 1;
+    while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (m.first[mid] <= key) lo = mid;
+        else hi = mid - 1;
+    }
+    return lo;
+}
+
 // The current token of each decode sequence written into the paged cache
 // ("Engineering Practices for Day-0 Adaptation of Million-Token Context Models
 // on Domestic AI Chips", Four Key Layers items 2 and 3: block-level

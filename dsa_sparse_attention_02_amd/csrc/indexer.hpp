@@ -408,9 +408,9 @@ constexpr int kPrefillRing = 4;
 
 template <int IDX_DIM, int IDX_TILES, bool BLOCK_TILE>
 __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
-    const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int bs_log2,
+    const uint16_t *__restrict__ idx_k, const int32_t *__restrict__ block_table, int bt_stride, int bs_log2,
     const uint16_t *__restrict__ idx_q, const float *__restrict__ idx_w, int idx_heads, int relu,
-    int pos0, int nrows, float *__restrict__ scores, int64_t score_stride, f32x2 *__restrict__ tile_mm,
+    const SeqMap blocks_map, float *__restrict__ scores, int64_t score_stride, f32x2 *__restrict__ tile_mm,
     int64_t mm_stride)
 {
     constexpr int KS = IDX_DIM / 16;
@@ -424,12 +424,18 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
     __shared__ __attribute__((aligned(1024))) uint8_t ring[R][TILE];
     __shared__ __attribute__((aligned(16))) float wts[kPrefillRowsPerBlock][HP];
 
+    // 16-row block g of piece pc (the pieces are listed shortest context first
+    // and the blocks run from the last one, so the longest rows start first)
     const int g = gridDim.x - 1 - blockIdx.x;
-    const int r0 = g * kPrefillRowsPerBlock;
+    const int pc = map_piece(blocks_map, g);
+    const int r0 = (g - blocks_map.first[pc]) * kPrefillRowsPerBlock;  // first row within the piece
+    const int prow = blocks_map.row0[pc] + r0;                           // ... within the launch's rows
+    const int p0 = blocks_map.pos0[pc] + r0;                             // ... its position
+    block_table += (int64_t)blocks_map.bt_row[pc] * bt_stride;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int col = lane & 31, half = lane >> 5;
-    const int rows_here = min(kPrefillRowsPerBlock, nrows - r0);
-    const int nkeys = pos0 + r0 + rows_here;  // keys visible to the block's last row
+    const int rows_here = min(kPrefillRowsPerBlock, blocks_map.nrows[pc] - r0);
+    const int nkeys = p0 + rows_here;  // keys visible to the block's last row
     const int bmask = (1 << bs_log2) - 1;
     const int ntiles = (nkeys + 31) / 32;
 
@@ -460,18 +466,18 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
 
     for (int e = threadIdx.x; e < kPrefillRowsPerBlock * HP; e += blockDim.x) {
         const int rr = e / HP, hj = e % HP;
-        wts[rr][hj] = (rr < rows_here && hj < idx_heads) ? idx_w[(int64_t)(r0 + rr) * idx_heads + hj] : 0.0f;
+        wts[rr][hj] = (rr < rows_here && hj < idx_heads) ? idx_w[(int64_t)(prow + rr) * idx_heads + hj] : 0.0f;
     }
     bf16x8 qa[2][IDX_TILES][KS];
     int pos[2];
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const int r = 2 * wave + rr;
-        pos[rr] = r < rows_here ? pos0 + r0 + r : -1;
+        pos[rr] = r < rows_here ? p0 + r : -1;
 #pragma unroll
         for (int t = 0; t < IDX_TILES; ++t) {
             const int head = 32 * t + col;
-            const uint16_t *qp = idx_q + ((int64_t)(r0 + r) * idx_heads + head) * IDX_DIM + half * (IDX_DIM / 2);
+            const uint16_t *qp = idx_q + ((int64_t)(prow + r) * idx_heads + head) * IDX_DIM + half * (IDX_DIM / 2);
 #pragma unroll
             for (int ks = 0; ks < KS; ++ks)
                 qa[rr][t][ks] = (r < rows_here && head < idx_heads) ? as_bf16x8(load16(qp + 8 * ks))
@@ -531,7 +537,7 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
             else head_sum(std::false_type{});
             const float tot = add_wave_halves(part);
             const int s = s0 + col;
-            if (half == 0 && s <= pos[rr]) scores[(int64_t)(r0 + lr) * score_stride + s] = tot + 0.0f;
+            if (half == 0 && s <= pos[rr]) scores[(int64_t)(prow + lr) * score_stride + s] = tot + 0.0f;
             if (s <= pos[rr]) {  // lane-local running range of the row's scores
                 rlo[rr] = fminf(rlo[rr], tot + 0.0f);
                 rhi[rr] = fmaxf(rhi[rr], tot + 0.0f);
@@ -544,7 +550,7 @@ __global__ __launch_bounds__(512) void idx_score_prefill_kernel(
 #pragma unroll
     for (int rr = 0; rr < 2; ++rr) {
         const f32x2 lohi = minmax32(rlo[rr], true), hilo = minmax32(rhi[rr], true);
-        if (lane == 0 && pos[rr] >= 0) tile_mm[(int64_t)(r0 + 2 * wave + rr) * mm_stride] = f32x2{lohi[0], hilo[1]};
+        if (lane == 0 && pos[rr] >= 0) tile_mm[(int64_t)(prow + 2 * wave + rr) * mm_stride] = f32x2{lohi[0], hilo[1]};
     }
 }
 

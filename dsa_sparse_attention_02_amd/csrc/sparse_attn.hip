@@ -5,15 +5,19 @@
 // caller's stream in this order:
 //   decode : indexer scan -> per-row top-k -> split attention -> split merge
 //   prefill: per chunk of rows { indexer tile scan -> per-row top-k },
-//            then attention over all rows (split + merge only when k > 2048)
+//            then attention over all rows (split + merge only when k > 2048);
+//            the rows of one or several sequences, cut into pieces of one
+//            sequence each (at most kMapPieces per launch)
 // The decode/prefill separation over one cache and one index format follows
 // "Day-0 Adaptation: Running Trillion-Parameter Models on Domestic AI
 // Accelerators", sections 3.1 and 3.3.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <vector>
 
 #include "../../include/sparse_attn.h"
 #include "attention.hpp"
@@ -129,11 +133,11 @@ struct PrefillPlan {
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
 };
 
-PrefillPlan plan_prefill(const sa_params *p, int num_rows, int q_start)
+// num_rows: query rows of the call; max_ctx: the most keys any row sees
+PrefillPlan plan_prefill(const sa_params *p, int num_rows, int64_t max_ctx)
 {
     PrefillPlan d{};
-    const int64_t ctx = (int64_t)q_start + num_rows;
-    d.score_stride = round_up(ctx, 64);
+    d.score_stride = round_up(std::max<int64_t>(max_ctx, 1), 64);
     int64_t rows = (int64_t)(kPrefillScoreBudget / (size_t)(d.score_stride * 4));
     rows = std::max<int64_t>(kPrefillRowsPerBlock, rows / kPrefillRowsPerBlock * kPrefillRowsPerBlock);
     d.chunk_rows = (int)std::min<int64_t>(rows, round_up(num_rows, kPrefillRowsPerBlock));
@@ -185,6 +189,107 @@ sa_status check_prefill(const sa_params *p, const sa_paged_cache *c, int num_row
         (int64_t)q_start + num_rows > INT32_MAX - 64)
         return SA_ERR_SHAPE;
     return SA_OK;
+}
+
+// A run of consecutive query rows of one sequence: rows [row0, row0 + n) of
+// the call, at positions pos0 .. pos0 + n - 1, block-table row bt_row.
+struct Piece {
+    int64_t row0;
+    int n, pos0, bt_row;
+};
+
+struct PrefillRows {
+    std::vector<Piece> pieces;  // non-empty, in row order, covering rows [0, total)
+    int total = 0;
+    int64_t max_ctx = 0;
+};
+
+PrefillRows one_sequence(int num_rows, int q_start)
+{
+    PrefillRows r;
+    r.pieces.push_back(Piece{0, num_rows, q_start, 0});
+    r.total = num_rows;
+    r.max_ctx = (int64_t)q_start + num_rows;
+    return r;
+}
+
+// cu_seqlens/q_starts (host) of the varlen call; max_tokens = 0: no cache bound
+sa_status varlen_rows(int num_seqs, const int32_t *cu, const int32_t *qs, int64_t max_tokens, PrefillRows *r)
+{
+    if (!cu || !qs) return SA_ERR_NULL;
+    if (num_seqs < 1 || cu[0] != 0) return SA_ERR_SHAPE;
+    r->pieces.clear();
+    r->max_ctx = 0;
+    for (int b = 0; b < num_seqs; ++b) {
+        const int64_t n = (int64_t)cu[b + 1] - cu[b];
+        if (n < 0 || qs[b] < 0) return SA_ERR_SHAPE;
+        if (n == 0) continue;
+        const int64_t end = (int64_t)qs[b] + n;
+        if (end > INT32_MAX - 64 || (max_tokens > 0 && end > max_tokens)) return SA_ERR_SHAPE;
+        r->pieces.push_back(Piece{cu[b], (int)n, qs[b], b});
+        r->max_ctx = std::max(r->max_ctx, end);
+    }
+    if (cu[num_seqs] < 1 || (int64_t)cu[num_seqs] > INT32_MAX - 64) return SA_ERR_SHAPE;
+    r->total = cu[num_seqs];
+    return SA_OK;
+}
+
+// The pieces of rows [r0, r1), with r1 <= rmax as large as kMapPieces pieces
+// allow.  `from` is the index of the first piece that may hold row r0.
+int cut_rows(const PrefillRows &rows, size_t &from, int r0, int rmax, std::vector<Piece> &parts)
+{
+    parts.clear();
+    while (from < rows.pieces.size() && rows.pieces[from].row0 + rows.pieces[from].n <= r0) ++from;
+    int r1 = r0;
+    for (size_t j = from; j < rows.pieces.size() && (int)parts.size() < kMapPieces && r1 < rmax; ++j) {
+        const Piece &pc = rows.pieces[j];
+        const int a = std::max<int64_t>(r0, pc.row0), b = std::min<int64_t>(rmax, pc.row0 + pc.n);
+        parts.push_back(Piece{a, b - a, pc.pos0 + (int)(a - pc.row0), pc.bt_row});
+        r1 = b;
+    }
+    return r1;
+}
+
+// Map of the parts for the top-k and attention launches: keyed by row, rows
+// counted from r0.
+SeqMap rows_map(const std::vector<Piece> &parts, int r0)
+{
+    SeqMap m{};
+    m.npieces = (int)parts.size();
+    for (int i = 0; i < m.npieces; ++i) {
+        m.first[i] = m.row0[i] = (int)(parts[i].row0 - r0);
+        m.nrows[i] = parts[i].n;
+        m.pos0[i] = parts[i].pos0;
+        m.bt_row[i] = parts[i].bt_row;
+    }
+    m.first[m.npieces] = (int)(parts.back().row0 + parts.back().n - r0);
+    return m;
+}
+
+// Map for the prefill indexer: keyed by 16-row block, pieces ordered by their
+// last position (the kernel runs the blocks from the last one, so the rows
+// with the most keys start first).  Returns the block count.
+int blocks_map(const std::vector<Piece> &parts, int r0, SeqMap *m)
+{
+    std::vector<int> order(parts.size());
+    for (size_t i = 0; i < parts.size(); ++i) order[i] = (int)i;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+        return parts[a].pos0 + parts[a].n < parts[b].pos0 + parts[b].n;
+    });
+    *m = SeqMap{};
+    m->npieces = (int)parts.size();
+    int nb = 0;
+    for (int i = 0; i < m->npieces; ++i) {
+        const Piece &pc = parts[order[i]];
+        m->first[i] = nb;
+        m->row0[i] = (int)(pc.row0 - r0);
+        m->nrows[i] = pc.n;
+        m->pos0[i] = pc.pos0;
+        m->bt_row[i] = pc.bt_row;
+        nb += (pc.n + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock;
+    }
+    m->first[m->npieces] = nb;
+    return nb;
 }
 
 sa_status check_ws(const void *ws, size_t have, size_t need)
@@ -251,30 +356,31 @@ void idx_decode(const sa_params *p, const sa_paged_cache *c, int batch, const vo
 
 template <int D, int T>
 void launch_idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w,
-                        int pos0, int nrows, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride,
+                        const SeqMap &bm, int nblocks, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride,
                         hipStream_t st)
 {
-    dim3 grid((nrows + kPrefillRowsPerBlock - 1) / kPrefillRowsPerBlock);
+    dim3 grid(nblocks);
     if (p->block_size >= 32)
         hipLaunchKernelGGL((idx_score_prefill_kernel<D, T, true>), grid, dim3(512), 0, st, (const uint16_t *)c->idx_k,
-                           c->block_table, ilog2(p->block_size), idx_q, idx_w, p->idx_heads, p->idx_relu, pos0,
-                           nrows, scores, stride, mm, mm_stride);
+                           c->block_table, c->max_blocks_per_seq, ilog2(p->block_size), idx_q, idx_w, p->idx_heads,
+                           p->idx_relu, bm, scores, stride, mm, mm_stride);
     else
         hipLaunchKernelGGL((idx_score_prefill_kernel<D, T, false>), grid, dim3(512), 0, st,
-                           (const uint16_t *)c->idx_k, c->block_table, ilog2(p->block_size), idx_q, idx_w,
-                           p->idx_heads, p->idx_relu, pos0, nrows, scores, stride, mm, mm_stride);
+                           (const uint16_t *)c->idx_k, c->block_table, c->max_blocks_per_seq, ilog2(p->block_size),
+                           idx_q, idx_w, p->idx_heads, p->idx_relu, bm, scores, stride, mm, mm_stride);
 }
 
-void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w, int pos0,
-                 int nrows, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride, hipStream_t st)
+void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *idx_q, const float *idx_w,
+                 const SeqMap &bm, int nblocks, float *scores, int64_t stride, f32x2 *mm, int64_t mm_stride,
+                 hipStream_t st)
 {
     const bool two = p->idx_heads > 32;
     if (p->idx_dim == 128) {
-        if (two) launch_idx_prefill<128, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
-        else launch_idx_prefill<128, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
+        if (two) launch_idx_prefill<128, 2>(p, c, idx_q, idx_w, bm, nblocks, scores, stride, mm, mm_stride, st);
+        else launch_idx_prefill<128, 1>(p, c, idx_q, idx_w, bm, nblocks, scores, stride, mm, mm_stride, st);
     } else {
-        if (two) launch_idx_prefill<32, 2>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
-        else launch_idx_prefill<32, 1>(p, c, idx_q, idx_w, pos0, nrows, scores, stride, mm, mm_stride, st);
+        if (two) launch_idx_prefill<32, 2>(p, c, idx_q, idx_w, bm, nblocks, scores, stride, mm, mm_stride, st);
+        else launch_idx_prefill<32, 1>(p, c, idx_q, idx_w, bm, nblocks, scores, stride, mm, mm_stride, st);
     }
 }
 
@@ -384,7 +490,7 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
                            mst, counts, d.mb_chunks, topk_idx);
     } else {
         hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, 0, c->context_lens, 0, p->topk, topk_idx, ap);
+                           d.mm_stride, 0, c->context_lens, SeqMap{}, p->topk, topk_idx, ap);
     }
     if (mk) mk->mark();
 }
@@ -401,45 +507,52 @@ void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const
     attend(p, a, batch, st, mk);
 }
 
-void select_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *idx_q,
+void select_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *idx_q,
                     const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d, hipStream_t st,
                     StageMarks *mk)
 {
     float *scores = (float *)((char *)ws + d.off_scores);
     f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
-    for (int r0 = 0; r0 < num_rows; r0 += d.chunk_rows) {
-        const int nr = std::min(d.chunk_rows, num_rows - r0);
-        const int pos0 = q_start + r0;
+    std::vector<Piece> parts;
+    size_t from = 0;
+    for (int r0 = 0, r1; r0 < rows.total; r0 = r1) {
+        r1 = cut_rows(rows, from, r0, std::min(rows.total, r0 + d.chunk_rows), parts);
         // rows whose whole context fits in k need no scores
-        if (pos0 + nr > p->topk) {
+        bool scan = false;
+        for (const Piece &pc : parts) scan |= (int64_t)pc.pos0 + pc.n > p->topk;
+        if (scan) {
+            SeqMap bm;
+            const int nb = blocks_map(parts, r0, &bm);
             idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
-                        idx_w + (int64_t)r0 * p->idx_heads, pos0, nr, scores, d.score_stride, mm, d.mm_stride, st);
+                        idx_w + (int64_t)r0 * p->idx_heads, bm, nb, scores, d.score_stride, mm, d.mm_stride, st);
             if (mk) mk->mark();
         }
-        hipLaunchKernelGGL(topk_rows_kernel, dim3(nr), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, 1, (const int32_t *)nullptr, pos0, p->topk, topk_idx + (int64_t)r0 * p->topk,
-                           no_append());
+        hipLaunchKernelGGL(topk_rows_kernel, dim3(r1 - r0), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
+                           d.mm_stride, 1, (const int32_t *)nullptr, rows_map(parts, r0), p->topk,
+                           topk_idx + (int64_t)r0 * p->topk, no_append());
         if (mk) mk->mark();
     }
 }
 
-void attend_prefill(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *q,
+void attend_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *q,
                     const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d, hipStream_t st,
                     StageMarks *mk)
 {
-    for (int r0 = 0; r0 < num_rows; r0 += d.attn_chunk_rows) {
-        const int nr = std::min(d.attn_chunk_rows, num_rows - r0);
+    std::vector<Piece> parts;
+    size_t from = 0;
+    for (int r0 = 0, r1; r0 < rows.total; r0 = r1) {
+        r1 = cut_rows(rows, from, r0, std::min(rows.total, r0 + d.attn_chunk_rows), parts);
         AttnArgs a = attn_args(p, c, (const uint16_t *)q + (int64_t)r0 * p->num_heads * p->qk_dim,
                                topk_idx + (int64_t)r0 * p->topk,
                                (char *)out + (int64_t)r0 * p->num_heads * p->v_dim * (p->out_dtype ? 2 : 4),
                                lse ? lse + (int64_t)r0 * p->num_heads : nullptr);
         a.decode = 0;
-        a.limit_base = q_start + r0;
+        a.rows_map = rows_map(parts, r0);
         a.tokens_per_split = d.tokens_per_split;
         a.splits = d.splits;
         a.part_o = (float *)((char *)ws + d.off_part_o);
         a.part_ml = (float *)((char *)ws + d.off_part_ml);
-        attend(p, a, nr, st, mk);
+        attend(p, a, r1 - r0, st, mk);
     }
 }
 
@@ -479,7 +592,19 @@ sa_status sa_prefill_workspace_size(const sa_params *p, int32_t num_rows, int32_
     if (s != SA_OK) return s;
     if (!bytes) return SA_ERR_NULL;
     if (num_rows < 1 || q_start < 0 || (int64_t)q_start + num_rows > INT32_MAX - 64) return SA_ERR_SHAPE;
-    *bytes = plan_prefill(p, num_rows, q_start).total;
+    *bytes = plan_prefill(p, num_rows, (int64_t)q_start + num_rows).total;
+    return SA_OK;
+}
+
+sa_status sa_prefill_varlen_workspace_size(const sa_params *p, int32_t num_seqs, const int32_t *cu_seqlens,
+                                           const int32_t *q_starts, size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    PrefillRows rows;
+    if ((s = varlen_rows(num_seqs, cu_seqlens, q_starts, 0, &rows)) != SA_OK) return s;
+    *bytes = plan_prefill(p, rows.total, rows.max_ctx).total;
     return SA_OK;
 }
 
@@ -573,10 +698,11 @@ sa_status sparse_attn_select_prefill(const sa_params *p, const sa_paged_cache *c
     sa_status s = check_prefill(p, c, num_rows, q_start, false, true);
     if (s != SA_OK) return s;
     if (!idx_q || !idx_w || !topk_idx) return SA_ERR_NULL;
-    const PrefillPlan d = plan_prefill(p, num_rows, q_start);
+    const PrefillRows rows = one_sequence(num_rows, q_start);
+    const PrefillPlan d = plan_prefill(p, rows.total, rows.max_ctx);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     clear_hip_error();
-    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream, nullptr);
+    select_prefill(p, c, rows, idx_q, idx_w, topk_idx, workspace, d, (hipStream_t)stream, nullptr);
     return launched();
 }
 
@@ -587,10 +713,31 @@ sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *c
     sa_status s = check_prefill(p, c, num_rows, q_start, true, false);
     if (s != SA_OK) return s;
     if (!q || !topk_idx || !out) return SA_ERR_NULL;
-    const PrefillPlan d = plan_prefill(p, num_rows, q_start);
+    const PrefillRows rows = one_sequence(num_rows, q_start);
+    const PrefillPlan d = plan_prefill(p, rows.total, rows.max_ctx);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     clear_hip_error();
-    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream, nullptr);
+    attend_prefill(p, c, rows, q, topk_idx, out, lse, workspace, d, (hipStream_t)stream, nullptr);
+    return launched();
+}
+
+static sa_status prefill_rows_impl(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows,
+                                   const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx,
+                                   void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                                   StageMarks *mk)
+{
+    if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
+    const PrefillPlan d = plan_prefill(p, rows.total, rows.max_ctx);
+    sa_status s = check_ws(workspace, workspace_bytes, d.total);
+    if (s != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    clear_hip_error();
+    if (mk) {
+        mk->stream = st;
+        mk->mark();
+    }
+    select_prefill(p, c, rows, idx_q, idx_w, topk_idx, workspace, d, st, mk);
+    attend_prefill(p, c, rows, q, topk_idx, out, lse, workspace, d, st, mk);
     return launched();
 }
 
@@ -598,20 +745,52 @@ static sa_status prefill_impl(const sa_params *p, const sa_paged_cache *c, int32
                               const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
                               float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk)
 {
-    sa_status s = check_prefill(p, c, num_rows, q_start, true, true);
+    const sa_status s = check_prefill(p, c, num_rows, q_start, true, true);
     if (s != SA_OK) return s;
-    if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
-    const PrefillPlan d = plan_prefill(p, num_rows, q_start);
-    if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
-    hipStream_t st = (hipStream_t)stream;
-    clear_hip_error();
-    if (mk) {
-        mk->stream = st;
-        mk->mark();
-    }
-    select_prefill(p, c, num_rows, q_start, idx_q, idx_w, topk_idx, workspace, d, st, mk);
-    attend_prefill(p, c, num_rows, q_start, q, topk_idx, out, lse, workspace, d, st, mk);
-    return launched();
+    return prefill_rows_impl(p, c, one_sequence(num_rows, q_start), q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                             workspace_bytes, stream, mk);
+}
+
+static sa_status prefill_varlen_impl(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
+                                     const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
+                                     const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!c) return SA_ERR_NULL;
+    if ((s = check_cache(p, c, true, true, false)) != SA_OK) return s;
+    PrefillRows rows;
+    if ((s = varlen_rows(num_seqs, cu_seqlens, q_starts, (int64_t)c->max_blocks_per_seq * p->block_size, &rows)) !=
+        SA_OK)
+        return s;
+    return prefill_rows_impl(p, c, rows, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
+                             mk);
+}
+
+sa_status sparse_attn_prefill_varlen(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
+                                     const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
+                                     const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream)
+{
+    return prefill_varlen_impl(p, c, num_seqs, cu_seqlens, q_starts, q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                               workspace_bytes, stream, nullptr);
+}
+
+sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
+                                              const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
+                                              const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                                              float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                                              void *const *events, int32_t num_events, int32_t *num_marks)
+{
+    if (!num_marks || (num_events > 0 && !events)) return SA_ERR_NULL;
+    StageMarks mk;
+    mk.events = events;
+    mk.capacity = num_events;
+    const sa_status s = prefill_varlen_impl(p, c, num_seqs, cu_seqlens, q_starts, q, idx_q, idx_w, topk_idx, out,
+                                            lse, workspace, workspace_bytes, stream, &mk);
+    *num_marks = mk.count;
+    return s;
 }
 
 sa_status sparse_attn_prefill(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,

@@ -216,18 +216,25 @@ __device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int3
 }
 
 // Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
-// else n = n_base + r + 1 (prefill row at position n_base + r).  tile_mm holds
+// else n = p + 1 for a prefill row at position p, found through the piece map
+// (rows counted from the launch's first row).  tile_mm holds
 // score ranges (min, max) at row stride mm_stride: one per 32-key tile
 // (mm_per_row == 0) or mm_per_row entries covering the whole row.
 __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
     const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
-    int mm_per_row, const int32_t *__restrict__ ctx_lens, int n_base, int k, int32_t *__restrict__ out,
+    int mm_per_row, const int32_t *__restrict__ ctx_lens, const SeqMap rows_map, int k, int32_t *__restrict__ out,
     const AppendArgs ap)
 {
     __shared__ TopkShared sh;
     const int r = blockIdx.x;
     append_rows(ap, r, threadIdx.x, kTopkThreads);  // (decode row r = sequence r; before the attention reads it)
-    const int n = ctx_lens ? ctx_lens[r] : n_base + r + 1;
+    int n;
+    if (ctx_lens) {
+        n = ctx_lens[r];
+    } else {
+        const int pc = map_piece(rows_map, r);
+        n = rows_map.pos0[pc] + (r - rows_map.row0[pc]) + 1;
+    }
     int32_t *o = out + (int64_t)r * k;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (n <= k) {

@@ -12,6 +12,8 @@ import os
 from dataclasses import dataclass
 from typing import Optional
 
+import numpy as np
+
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsparse_attn.so")
 
@@ -23,6 +25,7 @@ EXPORTS = (
     "sa_decode_workspace_size", "sparse_attn_decode", "sparse_attn_select_decode", "sparse_attn_attend_decode",
     "sa_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_select_prefill", "sparse_attn_attend_prefill",
     "sparse_attn_decode_profiled", "sparse_attn_prefill_profiled", "sparse_attn_decode_append",
+    "sa_prefill_varlen_workspace_size", "sparse_attn_prefill_varlen", "sparse_attn_prefill_varlen_profiled",
 )
 
 
@@ -74,6 +77,10 @@ def lib():
             "sparse_attn_prefill_profiled": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P, P, i32,
                                                             ctypes.POINTER(i32)]),
             "sparse_attn_decode_append": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, P, P, sz, P]),
+            "sa_prefill_varlen_workspace_size": (ctypes.c_int, [pp, i32, P, P, ctypes.POINTER(sz)]),
+            "sparse_attn_prefill_varlen": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, sz, P]),
+            "sparse_attn_prefill_varlen_profiled": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, sz, P,
+                                                                   P, i32, ctypes.POINTER(i32)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -276,6 +283,55 @@ def sparse_attn_prefill_profiled(p: Params, cache: PagedCache, q_start: int, q, 
     return topk_idx, out, lse, n.value
 
 
+def _host_i32(a, name, n):
+    a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
+    if a.shape != (n,):
+        raise SparseAttnError(f"{name}: expected {n} int32 entries, got shape {a.shape}")
+    return a
+
+
+def prefill_varlen_workspace_size(p: Params, cu_seqlens, q_starts) -> int:
+    q_starts = np.asarray(q_starts)
+    cu = _host_i32(cu_seqlens, "cu_seqlens", len(q_starts) + 1)
+    qs = _host_i32(q_starts, "q_starts", len(q_starts))
+    n = ctypes.c_size_t()
+    _check(lib().sa_prefill_varlen_workspace_size(ctypes.byref(p.c()), len(qs), cu.ctypes.data, qs.ctypes.data,
+                                                  ctypes.byref(n)), "sa_prefill_varlen_workspace_size")
+    return n.value
+
+
+def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_starts, q, idx_q, idx_w, *,
+                               want_lse=True, workspace=None, outputs=None, stream=None, events=None):
+    """Prefill of several sequences in one call: sequence s owns packed rows
+    cu_seqlens[s] .. cu_seqlens[s+1]-1 (host int32 arrays), its row i at
+    position q_starts[s] + i, block-table row s.  With `events`, the profiling
+    entry point records them around the kernels and the mark count is returned
+    as a fourth value."""
+    torch = _torch()
+    q_starts = np.asarray(q_starts)
+    cu = _host_i32(cu_seqlens, "cu_seqlens", len(q_starts) + 1)
+    qs = _host_i32(q_starts, "q_starts", len(q_starts))
+    L = q.shape[0]
+    _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
+    if int(cu[-1]) != L:
+        raise SparseAttnError(f"cu_seqlens ends at {int(cu[-1])}, but q has {L} rows")
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(prefill_varlen_workspace_size(p, cu, qs), q.device)
+    args = (ctypes.byref(p.c()), ctypes.byref(cache.c()), len(qs), cu.ctypes.data, qs.ctypes.data, q.data_ptr(),
+            idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
+            ws.numel(), _stream(stream))
+    if events is None:
+        _check(lib().sparse_attn_prefill_varlen(*args), "sparse_attn_prefill_varlen")
+        return topk_idx, out, lse
+    ev = (ctypes.c_void_p * max(1, len(events)))(*[e.handle for e in events])
+    n = ctypes.c_int32()
+    _check(lib().sparse_attn_prefill_varlen_profiled(*args, ev, len(events), ctypes.byref(n)),
+           "sparse_attn_prefill_varlen_profiled")
+    return topk_idx, out, lse, n.value
+
+
 class HipEvent:
     """A raw hipEvent_t (created with the HIP runtime) for the profiling entry points."""
     _hip = None
@@ -397,7 +453,6 @@ def sparse_attn_attend_prefill(p: Params, cache: PagedCache, q_start: int, q, to
 def to_device(w: dict, device="cuda"):
     """Copy a synth workload's arrays to `device` (bf16 data keeps its bit patterns)."""
     torch = _torch()
-    import numpy as np
 
     def t(a, dt=None):
         x = torch.from_numpy(np.ascontiguousarray(a))

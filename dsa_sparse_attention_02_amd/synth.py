@@ -71,7 +71,10 @@ MLA = Shape(num_heads=128, qk_dim=576, v_dim=512, idx_heads=64, idx_dim=128, blo
 class Spec:
     """One workload.  mode 'decode': `batch` sequences, query b sits at position
     ctx_b - 1.  mode 'prefill': one sequence of `rows` tokens, row i sits at
-    position q_start + i and the cache holds q_start + rows tokens."""
+    position q_start + i and the cache holds q_start + rows tokens.  mode
+    'varlen': sequence s has seq_rows[s] query rows (packed one sequence after
+    another), its row i at position q_starts[s] + i, and the cache holds
+    q_starts[s] + seq_rows[s] tokens of it."""
     name: str
     mode: str
     shape: Shape
@@ -81,6 +84,8 @@ class Spec:
     rows: int = 0                            # prefill rows L
     q_start: int = 0
     seed: int = 1000
+    seq_rows: Optional[Sequence[int]] = None   # varlen: query rows per sequence
+    q_starts: Optional[Sequence[int]] = None   # varlen: position of each sequence's first row
 
 
 WORKLOADS = {
@@ -95,6 +100,11 @@ WORKLOADS = {
                                    ctx_uniform=(16384, 131072), seed=1003),
     # long-context decode, batch 4, each context 1,048,576.
     "decode_b4_ctx1m": Spec("decode_b4_ctx1m", "decode", MLA, batch=4, ctx=[1 << 20] * 4, seed=1004),
+    # chunked prefill of 8 sequences in one call: 4096 new rows each after cached
+    # prefixes of 0, 4096, ..., 28672 tokens (the same 32768 rows and causal
+    # pairs as the single 32K prefill, spread over 8 block-table rows).
+    "prefill_varlen_8x4k": Spec("prefill_varlen_8x4k", "varlen", MLA, batch=8, seq_rows=[4096] * 8,
+                                q_starts=[4096 * i for i in range(8)], seed=1005),
 }
 
 
@@ -128,6 +138,9 @@ def _ints_bf16(seed: int, ids: tuple, n: int, a: int) -> np.ndarray:
 def context_lengths(spec: Spec) -> np.ndarray:
     if spec.mode == "prefill":
         return np.array([spec.q_start + spec.rows], dtype=np.int32)
+    if spec.mode == "varlen":
+        return (np.asarray(spec.q_starts, dtype=np.int64) + np.asarray(spec.seq_rows, dtype=np.int64)).astype(
+            np.int32)
     if spec.ctx is not None:
         c = np.asarray(spec.ctx, dtype=np.int32)
         assert c.shape == (spec.batch,)
@@ -204,7 +217,12 @@ def make(spec: Spec, keep_logical: bool = False, workers: Optional[int] = None) 
     with ThreadPoolExecutor(workers or _workers()) as ex:
         list(ex.map(fill, jobs))
 
-    T = spec.batch if spec.mode == "decode" else spec.rows
+    if spec.mode == "decode":
+        T = spec.batch
+    elif spec.mode == "prefill":
+        T = spec.rows
+    else:
+        T = int(sum(spec.seq_rows))
     # per-row streams so large prefill queries are drawn in parallel too
     q = np.empty((T, sh.num_heads, sh.qk_dim), dtype=np.uint16)
     rows_per = max(1, (1 << 22) // (sh.num_heads * sh.qk_dim))
@@ -225,6 +243,9 @@ def make(spec: Spec, keep_logical: bool = False, workers: Optional[int] = None) 
     out = dict(spec=spec, shape=sh, mode=spec.mode, q=q, idx_q=idx_q, idx_w=idx_w,
                kv=kv, idx_k=idx_k, block_table=table, context_lens=ctx,
                num_blocks=pool, max_blocks=max_blocks, rows=T, q_start=spec.q_start)
+    if spec.mode == "varlen":
+        out["cu_seqlens"] = np.concatenate([[0], np.cumsum(spec.seq_rows)]).astype(np.int32)
+        out["q_starts"] = np.asarray(spec.q_starts, dtype=np.int32)
     if keep_logical:
         out["kv_logical"] = kv_log
         out["idx_k_logical"] = ik_log
@@ -249,3 +270,10 @@ def small_decode(name: str, shape: Shape, ctx: Sequence[int], seed: int = 7, **k
 
 def small_prefill(name: str, shape: Shape, rows: int, q_start: int = 0, seed: int = 7, **kw) -> Spec:
     return Spec(name, "prefill", replace(shape, **kw) if kw else shape, rows=rows, q_start=q_start, seed=seed)
+
+
+def small_varlen(name: str, shape: Shape, seq_rows: Sequence[int], q_starts: Sequence[int], seed: int = 7,
+                 **kw) -> Spec:
+    assert len(seq_rows) == len(q_starts)
+    return Spec(name, "varlen", replace(shape, **kw) if kw else shape, batch=len(seq_rows), seq_rows=list(seq_rows),
+                q_starts=list(q_starts), seed=seed)

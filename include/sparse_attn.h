@@ -220,6 +220,43 @@ sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *c
                                      const int32_t *topk_idx, void *out, float *lse,
                                      void *workspace, size_t workspace_bytes, void *stream);
 
+/* ------------------------------------------------------- varlen prefill --
+ * Prefill rows of several sequences in one call (section 3.3 of the page on
+ * domestic AI accelerators: the prefill pathway over the shared paged cache;
+ * the page on million-token context models names balancing the load of many
+ * sequences at block level and pipelining the select and attention stages by
+ * chunk).  Sequence s owns the packed query rows [cu_seqlens[s],
+ * cu_seqlens[s+1]) of q, idx_q, idx_w, topk_idx, out and lse, and row s of the
+ * block table; its row i sits at position q_starts[s] + i and sees keys
+ * [0, q_starts[s] + i].  Each row gets exactly the result that
+ * sparse_attn_prefill gives it when called for its sequence alone.
+ *   cu_seqlens (host) int32 [num_seqs + 1]: cu_seqlens[0] = 0, non-decreasing
+ *              (empty sequences are allowed), cu_seqlens[num_seqs] >= 1 rows
+ *   q_starts   (host) int32 [num_seqs]: >= 0; the cache must hold
+ *              q_starts[s] + (cu_seqlens[s+1] - cu_seqlens[s]) tokens of a
+ *              non-empty sequence s, within max_blocks_per_seq * block_size
+ *   the block table must have num_seqs rows (not checkable from here)
+ * Both host arrays are read during the call only.  One launch of each kernel
+ * covers up to 64 runs of rows of one sequence (more sequences take more
+ * launches); the indexer launch starts the rows that see the most keys first.
+ * Errors: SA_ERR_NULL for a missing host array, SA_ERR_SHAPE for any
+ * violation of the rules above, otherwise as sparse_attn_prefill.
+ */
+sa_status sa_prefill_varlen_workspace_size(const sa_params *p, int32_t num_seqs, const int32_t *cu_seqlens,
+                                           const int32_t *q_starts, size_t *bytes /* host, out */);
+sa_status sparse_attn_prefill_varlen(const sa_params *p, const sa_paged_cache *cache, int32_t num_seqs,
+                                     const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
+                                     const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                                     float *lse, void *workspace, size_t workspace_bytes, void *stream);
+/* Profiling variant (marks as for sparse_attn_prefill_profiled). */
+sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged_cache *cache,
+                                              int32_t num_seqs, const int32_t *cu_seqlens,
+                                              const int32_t *q_starts, const void *q, const void *idx_q,
+                                              const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                              void *workspace, size_t workspace_bytes, void *stream,
+                                              void *const *events, int32_t num_events,
+                                              int32_t *num_marks);
+
 #ifdef __cplusplus
 }
 #endif

@@ -97,6 +97,40 @@ def run(w: dict, rows=None, want_scores: bool = False, stage_seconds=None):
     return res
 
 
+def run_varlen(w: dict, rows=None, want_scores: bool = False) -> dict:
+    """The oracle on a multi-sequence prefill workload (mode 'varlen' of the
+    synth module): each packed row is a prefill row of its own sequence, at
+    position q_starts[s] + i, over block-table row s; computed one sequence at
+    a time with `run` on that sequence alone.  Returns run's dict for the
+    listed packed rows."""
+    cu = np.asarray(w["cu_seqlens"], dtype=np.int64)
+    qs = np.asarray(w["q_starts"], dtype=np.int64)
+    T = int(cu[-1])
+    rows = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    seq_of = np.searchsorted(cu, rows, side="right") - 1
+    parts = {}
+    for s in np.unique(seq_of):
+        s = int(s)
+        sel = np.nonzero(seq_of == s)[0]
+        a, b = int(cu[s]), int(cu[s + 1])
+        sub = dict(w, mode="prefill", rows=b - a, q_start=int(qs[s]), q=w["q"][a:b], idx_q=w["idx_q"][a:b],
+                   idx_w=w["idx_w"][a:b], block_table=w["block_table"][s:s + 1],
+                   context_lens=np.asarray([qs[s] + b - a], dtype=np.int32))
+        parts[s] = (sel, run(sub, rows=rows[sel] - a, want_scores=want_scores))
+    sh = w["shape"]
+    nr = len(rows)
+    res = dict(topk=np.empty((nr, sh.topk), dtype=np.int32), out=np.empty((nr, sh.num_heads, sh.v_dim)),
+               lse=np.empty((nr, sh.num_heads)), rows=rows)
+    if want_scores:
+        res["scores"] = np.full((nr, max(1, int(np.max(w["context_lens"])))), np.nan, dtype=np.float32)
+    for sel, r in parts.values():
+        for key in ("topk", "out", "lse"):
+            res[key][sel] = r[key]
+        if want_scores:
+            res["scores"][sel, :r["scores"].shape[1]] = r["scores"]
+    return res
+
+
 def append(w: dict, new_kv: np.ndarray, new_idx_k: np.ndarray) -> dict:
     """Decode workload `w` with each sequence's current token (position
     context_lens[b] - 1) replaced by new_kv[b] / new_idx_k[b] in copies of its

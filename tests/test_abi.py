@@ -155,3 +155,52 @@ def test_decode_append_validation(L):
     assert _decode_append(L, p, c, max_ctx=257) == sa.SA_ERR_SHAPE
     assert _decode_append(L, _params(idx_dim=64), c) == sa.SA_ERR_UNSUPPORTED
     assert _decode_append(L, p, c, ws_bytes=16) == sa.SA_ERR_WORKSPACE
+
+
+def _i32(*v):
+    return (ctypes.c_int32 * max(1, len(v)))(*v)
+
+
+def _varlen(L, p, c, cu=(0, 3, 3, 10), qs=(0, 5, 200), ws_bytes=1 << 40, n=None, **ptrs):
+    args = dict(q=FAKE, idx_q=FAKE, idx_w=FAKE, topk=FAKE, out=FAKE, lse=None, ws=FAKE)
+    args.update(ptrs)
+    cu_a = _i32(*cu) if cu is not None else None
+    qs_a = _i32(*qs) if qs is not None else None
+    return L.sparse_attn_prefill_varlen(ctypes.byref(p) if p is not None else None,
+                                        ctypes.byref(c) if c is not None else None,
+                                        (3 if qs is None else len(qs)) if n is None else n, cu_a, qs_a, args["q"], args["idx_q"],
+                                        args["idx_w"], args["topk"], args["out"], args["lse"], args["ws"], ws_bytes,
+                                        None)
+
+
+def test_prefill_varlen_validation(L):
+    """The multi-sequence prefill checks its host arrays (start at 0, never
+    decrease, some row, every non-empty sequence within the cache), then what
+    the single-sequence prefill checks, before any HIP call."""
+    p, c = _params(), _cache()  # cache: 4 blocks per sequence of 64 tokens = 256 positions
+    assert _varlen(L, p, c, cu=None) == sa.SA_ERR_NULL
+    assert _varlen(L, p, c, qs=None) == sa.SA_ERR_NULL
+    assert _varlen(L, None, c) == sa.SA_ERR_NULL
+    assert _varlen(L, p, None) == sa.SA_ERR_NULL
+    assert _varlen(L, p, c, q=None) == sa.SA_ERR_NULL
+    assert _varlen(L, p, _cache(idx_k=None)) == sa.SA_ERR_NULL
+    assert _varlen(L, p, c, n=0) == sa.SA_ERR_SHAPE
+    assert _varlen(L, p, c, cu=(1, 3, 3, 10)) == sa.SA_ERR_SHAPE      # must start at 0
+    assert _varlen(L, p, c, cu=(0, 3, 2, 10)) == sa.SA_ERR_SHAPE      # decreasing
+    assert _varlen(L, p, c, cu=(0, 0, 0, 0)) == sa.SA_ERR_SHAPE       # no row at all
+    assert _varlen(L, p, c, qs=(0, -1, 200)) == sa.SA_ERR_SHAPE       # negative start (empty sequence too)
+    assert _varlen(L, p, c, qs=(0, 5, 250)) == sa.SA_ERR_SHAPE        # 250 + 7 rows > 256 positions
+    # an empty sequence's start is not bounded by the cache: validation passes
+    # and the workspace check stops the call (before any launch)
+    assert _varlen(L, p, c, qs=(0, 300, 249), ws_bytes=16) == sa.SA_ERR_WORKSPACE
+    assert _varlen(L, _params(idx_dim=64), c) == sa.SA_ERR_UNSUPPORTED
+    assert _varlen(L, p, c, ws_bytes=16) == sa.SA_ERR_WORKSPACE
+    # the workspace of the varlen call is that of one sequence of the same rows
+    # and longest context
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.sa_prefill_varlen_workspace_size(ctypes.byref(p), 3, _i32(0, 3, 3, 10), _i32(0, 5, 200),
+                                              ctypes.byref(a)) == sa.SA_OK
+    assert L.sa_prefill_workspace_size(ctypes.byref(p), 10, 197, ctypes.byref(b)) == sa.SA_OK
+    assert a.value == b.value > 0
+    assert L.sa_prefill_varlen_workspace_size(ctypes.byref(p), 3, None, _i32(0, 5, 200),
+                                              ctypes.byref(a)) == sa.SA_ERR_NULL

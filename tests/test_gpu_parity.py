@@ -49,6 +49,10 @@ def run_gpu(dev, w, out_bf16=False, staged=False):
             res = (tk, out, lse)
         else:
             res = sa.sparse_attn_decode(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"])
+    elif w["mode"] == "varlen":
+        assert not staged
+        res = sa.sparse_attn_prefill_varlen(p, d["cache"], w["cu_seqlens"], w["q_starts"], d["q"], d["idx_q"],
+                                            d["idx_w"])
     else:
         if staged:
             tk = sa.sparse_attn_select_prefill(p, d["cache"], w["q_start"], d["idx_q"], d["idx_w"])
@@ -61,8 +65,8 @@ def run_gpu(dev, w, out_bf16=False, staged=False):
 
 
 def compare(w, res, rows=None, tag=""):
-    tk_all, out_all, lse_all = res
-    ref = oracle.run(w, rows=rows)
+    tk_all, out_all, lse_all = res[:3]
+    ref = oracle.run_varlen(w, rows=rows) if w["mode"] == "varlen" else oracle.run(w, rows=rows)
     rows = ref["rows"]
     idx = __import__("torch").as_tensor(rows, device=tk_all.device)
     tk = tk_all.index_select(0, idx).cpu().numpy()
@@ -169,6 +173,7 @@ FULL_ROWS = {
     "decode_b64_ctx16k_128k": "ends",                # shortest, longest and a few more
     "decode_b4_ctx1m": [0, 3],
     "prefill_L32k": [0, 1, 2046, 2047, 2048, 2049, 4095, 16000, 31999, 32767],
+    "prefill_varlen_8x4k": [0, 1, 2047, 4095, 4096, 8191, 12345, 20480, 28671, 28672, 30000, 32767],
 }
 
 
@@ -232,3 +237,63 @@ def test_decode_append_parity(dev, name):
     assert np.array_equal(ik_after, w2["idx_k"]), f"{name}: idx_k pool differs after the append"
     rows = None if w["rows"] <= 64 else [0, 1, 15, 31]
     compare(w2, res, rows=rows, tag=f"{name} (appended)")
+
+
+def _seventy_sequences():
+    rng = np.random.default_rng(131)
+    rows = [int(x) for x in rng.integers(0, 21, size=70)]
+    rows[5] = 0
+    assert sum(r > 0 for r in rows) > 64
+    return synth.small_varlen("varlen_70", synth.TINY, rows, [int(x) for x in rng.integers(0, 301, size=70)],
+                              seed=131)
+
+
+VARLEN_CASES = {
+    # ragged rows, an empty sequence, cached prefixes; some rows select, some keep every key
+    "varlen_tiny_ragged": lambda: synth.small_varlen("varlen_tiny", synth.TINY, [3, 0, 17, 1, 40, 256],
+                                                     [0, 5, 30, 63, 10, 700], seed=132),
+    "varlen_mla_mixed": lambda: synth.small_varlen("varlen_mla", MLA, [1, 700, 0, 33, 1500], [0, 1800, 10, 3000, 0],
+                                                   seed=133),
+    # more sequences than one launch's 64 pieces: two launches per stage
+    "varlen_70_sequences": _seventy_sequences,
+    # k = 3000: attention in two splits plus the merge
+    "varlen_k3000_splits": lambda: synth.small_varlen("varlen_k3000", MLA, [500, 2600], [2800, 0], seed=134,
+                                                      topk=3000),
+}
+
+
+@pytest.mark.parametrize("name", list(VARLEN_CASES))
+def test_prefill_varlen_parity(dev, name):
+    """sparse_attn_prefill_varlen against the oracle's per-sequence prefill."""
+    spec = VARLEN_CASES[name]()
+    say(f"[gpu] varlen prefill {name}")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w), tag=name)
+
+
+def test_prefill_varlen_equals_one_call_per_sequence(dev):
+    """Each packed row of the multi-sequence call gets bit for bit what the
+    single-sequence prefill gives it for its own sequence alone (block-table
+    row s passed as a one-row table)."""
+    torch, sa = dev
+    spec = VARLEN_CASES["varlen_mla_mixed"]()
+    say("[gpu] varlen prefill = one call per sequence")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    tk, out, lse = sa.sparse_attn_prefill_varlen(p, d["cache"], w["cu_seqlens"], w["q_starts"], d["q"], d["idx_q"],
+                                                 d["idx_w"])
+    cu, qs = w["cu_seqlens"], w["q_starts"]
+    for s in range(len(qs)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if a == b:
+            continue
+        cache = sa.PagedCache(kv=d["cache"].kv, idx_k=d["cache"].idx_k,
+                              block_table=d["cache"].block_table[s:s + 1].contiguous(),
+                              context_lens=d["cache"].context_lens[s:s + 1].contiguous())
+        tk1, out1, lse1 = sa.sparse_attn_prefill(p, cache, int(qs[s]), d["q"][a:b].contiguous(),
+                                                 d["idx_q"][a:b].contiguous(), d["idx_w"][a:b].contiguous())
+        torch.cuda.synchronize()
+        assert torch.equal(tk[a:b], tk1), f"sequence {s}: indices differ"
+        assert torch.equal(out[a:b], out1), f"sequence {s}: outputs differ"
+        assert torch.equal(lse[a:b], lse1), f"sequence {s}: lse differs"

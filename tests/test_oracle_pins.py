@@ -336,3 +336,56 @@ def test_append_writes_the_current_token(which):
         np.testing.assert_allclose(res["lse"][b], lse, rtol=1e-12, atol=1e-12)
         x8 = _int_scores_x(wl, b, 8)
         assert np.array_equal((res["scores"][b][:n].astype(np.float64) * 8).astype(np.int64), x8)
+
+
+def test_varlen_rows_follow_their_own_sequence():
+    """Multi-sequence prefill in the oracle, pinned to the logical (never paged)
+    rows the generator keeps: with k covering every context, each packed row
+    equals dense brute-force attention over its own sequence's first
+    q_starts[s] + i + 1 rows, and its indexer scores equal the exact integer
+    closed form over that sequence's keys.  Ragged rows, an empty sequence and
+    prefixes already in the cache."""
+    spec = synth.small_varlen("pin_varlen", replace(synth.TINY, topk=256), [3, 0, 17, 1, 40], [0, 5, 30, 63, 10],
+                              seed=51)
+    w = synth.make(spec, keep_logical=True)
+    sh = w["shape"]
+    res = oracle.run_varlen(w, want_scores=True)
+    scale = float(np.float32(sh.softmax_scale))
+    cu, qs = w["cu_seqlens"], w["q_starts"]
+    checked = 0
+    for s in range(len(qs)):
+        for i in range(int(cu[s + 1] - cu[s])):
+            r = int(cu[s]) + i
+            n = int(qs[s]) + i + 1
+            assert list(res["topk"][r][:n]) == list(range(n)) and np.all(res["topk"][r][n:] == -1)
+            o, lse = _dense_attention(_logical_f32(w["q"][r]), _logical_f32(w["kv_logical"][s][:n]), np.arange(n),
+                                      scale, sh.v_dim)
+            np.testing.assert_allclose(res["out"][r], o, rtol=1e-12, atol=1e-12)
+            np.testing.assert_allclose(res["lse"][r], lse, rtol=1e-12, atol=1e-12)
+            iq = synth.bf16_bits_to_f32(w["idx_q"][r]).astype(np.int64)
+            ik = synth.bf16_bits_to_f32(w["idx_k_logical"][s][:n]).astype(np.int64)
+            d = ik @ iq.T
+            if sh.idx_relu:
+                d = np.maximum(d, 0)
+            wi = w["idx_w"][r].astype(np.float64) * 8
+            x8 = d @ wi.astype(np.int64)
+            assert np.array_equal((res["scores"][r][:n].astype(np.float64) * 8).astype(np.int64), x8)
+            checked += 1
+    assert checked == int(cu[-1])
+
+
+def test_varlen_single_rows_equal_decode():
+    """A multi-sequence prefill whose sequences each hold one row at position
+    ctx - 1 is the decode of that batch: the oracle's varlen path (per-sequence
+    prefill over its block-table row) and its decode path (row b over
+    block-table row b, limit ctx_b) agree, with selection active (ctx > k)."""
+    ctx = [1, 64, 65, 3000, 2049]
+    vspec = synth.small_varlen("pin_varlen_dec", MLA_SMALL, [1] * len(ctx), [c - 1 for c in ctx], seed=52)
+    w = synth.make(vspec)
+    dec = dict(w, mode="decode", rows=len(ctx), q_start=0)
+    a = oracle.run_varlen(w)
+    b = oracle.run(dec)
+    assert np.array_equal(a["topk"], b["topk"])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["lse"], b["lse"], rtol=1e-12, atol=1e-12)
+    assert np.sum(a["topk"][3] >= 0) == MLA_SMALL.topk
