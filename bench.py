@@ -130,6 +130,27 @@ def run_decode(args, torch, sa, synth):
         torch.cuda.synchronize()
         again = (time.perf_counter() - tb) * 1e3 / args.steps
         log(f"decode with append: {append_ms:.3f} ms/step (plain step again after it: {again:.3f} ms)")
+    # Block-granular selection over the same batch: k / block_size whole cache
+    # blocks per row (the same number of attended token slots), timed the same way.
+    blocks_ms = None
+    if args.blocks_steps > 0:
+        from dataclasses import replace
+        sh = w["shape"]
+        pb = sa.Params.from_shape(replace(sh, topk=sh.topk // sh.block_size))
+        wsb = torch.empty(sa.decode_blocks_workspace_size(pb, B, max_ctx), dtype=torch.uint8, device="cuda")
+        outb = sa._outputs(pb, B, "cuda", True)
+        blk = lambda: sa.sparse_attn_decode_blocks(pb, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"],
+                                                   workspace=wsb, outputs=outb)
+        for _ in range(args.warmup):
+            blk()
+        torch.cuda.synchronize()
+        tb = time.perf_counter()
+        for _ in range(args.blocks_steps):
+            blk()
+        torch.cuda.synchronize()
+        blocks_ms = (time.perf_counter() - tb) * 1e3 / args.blocks_steps
+        log(f"decode with block selection ({pb.topk} blocks of {sh.block_size}): {blocks_ms:.3f} ms/step")
+        del wsb, outb
     events = [[sa.HipEvent() for _ in range(n_marks)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t2 = time.perf_counter()
@@ -159,7 +180,7 @@ def run_decode(args, torch, sa, synth):
         del flush
     alg = decode_algorithmic(w)
     return w, dict(ms=ms, stages=stages, cold_ms=statistics.median(cold) if cold else None, alg=alg,
-                   per_kernel=per_kernel, append_ms=append_ms, ms_marked=ms_marked)
+                   per_kernel=per_kernel, append_ms=append_ms, ms_marked=ms_marked, blocks_ms=blocks_ms)
 
 
 def run_other_decodes(args, torch, sa, synth, names):
@@ -168,6 +189,7 @@ def run_other_decodes(args, torch, sa, synth, names):
     for name in names:
         sub = argparse.Namespace(**vars(args))
         sub.workload, sub.steps, sub.warmup, sub.flush_steps, sub.append_steps = name, 20, 20, 0, 0
+        sub.blocks_steps = 0
         w, dec = run_decode(sub, torch, sa, synth)
         B = len(w["context_lens"])
         res[name] = {"ms_per_step": round(dec["ms"], 4), "tokens_per_s": round(B / (dec["ms"] / 1e3), 1),
@@ -357,6 +379,9 @@ def main():
     ap.add_argument("--append-steps", type=int, default=20,
                     help="steps of the decode call that also appends each sequence's current token to the "
                          "cache (sparse_attn_decode_append), timed like the plain steps right after them")
+    ap.add_argument("--blocks-steps", type=int, default=20,
+                    help="steps of block-granular decode (sparse_attn_decode_blocks, k / block_size blocks per "
+                         "row) over the same batch")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--other-workloads", default="none",
@@ -442,6 +467,11 @@ def main():
         line["decode_append"] = {"ms_per_step": round(dec["append_ms"], 4),
                                  "tokens_per_s": round(B / (dec["append_ms"] / 1e3), 1),
                                  "added_us": round((dec["append_ms"] - dec["ms"]) * 1e3, 2)}
+    if dec.get("blocks_ms"):
+        # supplementary: block-granular selection over the same batch
+        line["decode_blocks"] = {"ms_per_step": round(dec["blocks_ms"], 4),
+                                 "tokens_per_s": round(B / (dec["blocks_ms"] / 1e3), 1),
+                                 "kept_blocks": sh.topk // sh.block_size, "block_size": sh.block_size}
     if not args.no_prefill:
         line["prefill"] = run_prefill(args, torch, sa, synth)
         line["prefill_varlen"] = run_prefill(args, torch, sa, synth, "prefill_varlen_8x4k")

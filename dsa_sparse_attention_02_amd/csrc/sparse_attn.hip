@@ -21,6 +21,7 @@
 
 #include "../../include/sparse_attn.h"
 #include "attention.hpp"
+#include "blocks.hpp"
 #include "indexer.hpp"
 #include "topk.hpp"
 
@@ -133,14 +134,15 @@ struct PrefillPlan {
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
 };
 
-// num_rows: query rows of the call; max_ctx: the most keys any row sees
-PrefillPlan plan_prefill(const sa_params *p, int num_rows, int64_t max_ctx)
+// num_rows: query rows of the call; max_ctx: the most keys any row sees;
+// chunks of rows are multiples of row_multiple (a power of two >= 16)
+PrefillPlan plan_prefill(const sa_params *p, int num_rows, int64_t max_ctx, int row_multiple = kPrefillRowsPerBlock)
 {
     PrefillPlan d{};
     d.score_stride = round_up(std::max<int64_t>(max_ctx, 1), 64);
     int64_t rows = (int64_t)(kPrefillScoreBudget / (size_t)(d.score_stride * 4));
-    rows = std::max<int64_t>(kPrefillRowsPerBlock, rows / kPrefillRowsPerBlock * kPrefillRowsPerBlock);
-    d.chunk_rows = (int)std::min<int64_t>(rows, round_up(num_rows, kPrefillRowsPerBlock));
+    rows = std::max<int64_t>(row_multiple, rows / row_multiple * row_multiple);
+    d.chunk_rows = (int)std::min<int64_t>(rows, round_up(num_rows, row_multiple));
     const int k = p->topk;
     d.splits = (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens;
     d.tokens_per_split = (int)round_up((k + d.splits - 1) / d.splits, 32);
@@ -556,6 +558,131 @@ void attend_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRo
     }
 }
 
+// ------------------------------------------------ block-granular selection --
+// p->topk = k counts KV blocks (cache blocks); the attention then runs over
+// k * block_size token slots per row.
+struct BlockPlan {
+    sa_params pa;          // p with topk = k * block_size (the attention's view)
+    int q_block, groups;   // rows per query block; query blocks per select chunk (decode: the batch)
+    int64_t bstride, bmm_stride;
+    size_t off_bscore, off_bmm, off_ncand, off_tokens, total;
+};
+
+sa_status check_blocks(const sa_params *p)
+{
+    if ((int64_t)p->topk * p->block_size > kMaxTopk) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+// the block-mode areas after `base` bytes: block scores and ranges of `groups`
+// query blocks of at most max_ctx positions, candidate counts, and the
+// expanded token lists of `rows` rows
+void plan_block_areas(const sa_params *p, BlockPlan &b, size_t base, int groups, int64_t max_ctx, int rows)
+{
+    const int64_t nblk = (std::max<int64_t>(max_ctx, 1) + p->block_size - 1) / p->block_size;
+    b.groups = groups;
+    b.bstride = round_up(nblk, 64);
+    b.bmm_stride = b.bstride / 32;
+    size_t off = align_up(base, kAlign);
+    b.off_bscore = off;
+    off = align_up(off + (size_t)groups * b.bstride * 4, kAlign);
+    b.off_bmm = off;
+    off = align_up(off + (size_t)groups * b.bmm_stride * 8, kAlign);
+    b.off_ncand = off;
+    off = align_up(off + (size_t)groups * 4, kAlign);
+    b.off_tokens = off;
+    off = align_up(off + (size_t)rows * b.pa.topk * 4, kAlign);
+    b.total = off;
+}
+
+BlockPlan plan_decode_blocks(const sa_params *p, int batch, int max_ctx, DecodePlan *dp)
+{
+    BlockPlan b{};
+    b.pa = *p;
+    b.pa.topk = p->topk * p->block_size;
+    b.q_block = 1;
+    *dp = plan_decode(&b.pa, batch, max_ctx);
+    plan_block_areas(p, b, dp->total, batch, max_ctx, batch);
+    return b;
+}
+
+BlockPlan plan_prefill_blocks(const sa_params *p, int num_rows, int q_start, int q_block, PrefillPlan *pp)
+{
+    BlockPlan b{};
+    b.pa = *p;
+    b.pa.topk = p->topk * p->block_size;
+    b.q_block = q_block;
+    *pp = plan_prefill(&b.pa, num_rows, (int64_t)q_start + num_rows, std::max(kPrefillRowsPerBlock, q_block));
+    plan_block_areas(p, b, pp->total, pp->chunk_rows / q_block, (int64_t)q_start + num_rows, num_rows);
+    return b;
+}
+
+// Block scores of `groups` query blocks, then the top-k over them into
+// block_idx (k per query block).
+void select_blocks(const sa_params *p, const BlockPlan &b, const float *scores, int64_t score_stride,
+                   const int32_t *ctx_lens, int pos0, int nrows, int32_t *block_idx, void *ws, hipStream_t st)
+{
+    const int groups = (nrows + b.q_block - 1) / b.q_block;
+    float *bscore = (float *)((char *)ws + b.off_bscore);
+    f32x2 *bmm = (f32x2 *)((char *)ws + b.off_bmm);
+    int32_t *ncand = (int32_t *)((char *)ws + b.off_ncand);
+    hipLaunchKernelGGL(block_score_kernel, dim3(groups, (unsigned)(b.bstride / 32)), dim3(kBlockScoreThreads), 0, st,
+                       scores, score_stride, ctx_lens, pos0, b.q_block, nrows, ilog2(p->block_size), p->topk, bscore,
+                       b.bstride, bmm, b.bmm_stride, ncand);
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(groups), dim3(kTopkThreads), 0, st, (const float *)bscore, b.bstride,
+                       (const f32x2 *)bmm, b.bmm_stride, 0, (const int32_t *)ncand, SeqMap{}, p->topk, block_idx,
+                       no_append());
+}
+
+void decode_blocks_impl(const sa_params *p, const sa_paged_cache *c, int batch, int max_ctx, const void *q,
+                        const void *idx_q, const float *idx_w, int32_t *block_idx, void *out, float *lse, void *ws,
+                        const BlockPlan &b, const DecodePlan &d, hipStream_t st, StageMarks *mk)
+{
+    float *scores = (float *)((char *)ws + d.off_scores);
+    f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
+    // token scores only where some sequence has more candidate blocks than k
+    if ((int64_t)max_ctx > (int64_t)p->topk * p->block_size) {
+        idx_decode(p, c, batch, idx_q, idx_w, scores, d.score_stride, mm, d.mm_stride, d.scan_blocks, no_append(),
+                   st);
+        if (mk) mk->mark();
+    }
+    select_blocks(p, b, scores, d.score_stride, c->context_lens, 0, batch, block_idx, ws, st);
+    if (mk) mk->mark();
+    int32_t *tokens = (int32_t *)((char *)ws + b.off_tokens);
+    hipLaunchKernelGGL(expand_blocks_kernel, dim3(batch), dim3(256), 0, st, (const int32_t *)block_idx, p->topk,
+                       c->context_lens, 0, 1, ilog2(p->block_size), tokens);
+    attend_decode(&b.pa, c, batch, q, tokens, out, lse, ws, d, st, mk);
+}
+
+void prefill_blocks_impl(const sa_params *p, const sa_paged_cache *c, int num_rows, int q_start, const void *q,
+                         const void *idx_q, const float *idx_w, int32_t *block_idx, void *out, float *lse, void *ws,
+                         const BlockPlan &b, const PrefillPlan &d, hipStream_t st, StageMarks *mk)
+{
+    float *scores = (float *)((char *)ws + d.off_scores);
+    f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
+    const PrefillRows rows = one_sequence(num_rows, q_start);
+    std::vector<Piece> parts;
+    size_t from = 0;
+    for (int r0 = 0, r1; r0 < num_rows; r0 = r1) {  // chunks of whole query blocks
+        r1 = cut_rows(rows, from, r0, std::min(num_rows, r0 + d.chunk_rows), parts);
+        const int64_t last = (int64_t)q_start + r1 - 1;
+        if ((last >> ilog2(p->block_size)) + 1 > p->topk) {
+            SeqMap bm;
+            const int nb = blocks_map(parts, r0, &bm);
+            idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
+                        idx_w + (int64_t)r0 * p->idx_heads, bm, nb, scores, d.score_stride, mm, d.mm_stride, st);
+            if (mk) mk->mark();
+        }
+        select_blocks(p, b, scores, d.score_stride, nullptr, q_start + r0, r1 - r0,
+                      block_idx + (int64_t)(r0 / b.q_block) * p->topk, ws, st);
+        if (mk) mk->mark();
+    }
+    int32_t *tokens = (int32_t *)((char *)ws + b.off_tokens);
+    hipLaunchKernelGGL(expand_blocks_kernel, dim3(num_rows), dim3(256), 0, st, (const int32_t *)block_idx, p->topk,
+                       (const int32_t *)nullptr, q_start, b.q_block, ilog2(p->block_size), tokens);
+    attend_prefill(&b.pa, c, rows, q, tokens, out, lse, ws, d, st, mk);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------- C ABI --
@@ -815,6 +942,74 @@ sa_status sparse_attn_prefill_profiled(const sa_params *p, const sa_paged_cache 
                                      workspace_bytes, stream, &mk);
     *num_marks = mk.count;
     return s;
+}
+
+// ------------------------------------------------ block-granular selection --
+static sa_status check_q_block(int q_block)
+{
+    if (q_block < 1) return SA_ERR_SHAPE;
+    if (!is_pow2(q_block) || q_block > 128) return SA_ERR_UNSUPPORTED;
+    return SA_OK;
+}
+
+sa_status sa_decode_blocks_workspace_size(const sa_params *p, int32_t batch, int32_t max_ctx, size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if ((s = check_blocks(p)) != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    if (batch < 1 || max_ctx < 0) return SA_ERR_SHAPE;
+    DecodePlan d;
+    *bytes = plan_decode_blocks(p, batch, max_ctx, &d).total;
+    return SA_OK;
+}
+
+sa_status sparse_attn_decode_blocks(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                    const void *q, const void *idx_q, const float *idx_w, int32_t *block_idx,
+                                    void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_decode(p, c, batch, max_ctx, true, true);
+    if (s != SA_OK) return s;
+    if ((s = check_blocks(p)) != SA_OK) return s;
+    if (!q || !idx_q || !idx_w || !block_idx || !out) return SA_ERR_NULL;
+    DecodePlan d;
+    const BlockPlan b = plan_decode_blocks(p, batch, max_ctx, &d);
+    if ((s = check_ws(workspace, workspace_bytes, b.total)) != SA_OK) return s;
+    clear_hip_error();
+    decode_blocks_impl(p, c, batch, max_ctx, q, idx_q, idx_w, block_idx, out, lse, workspace, b, d,
+                       (hipStream_t)stream, nullptr);
+    return launched();
+}
+
+sa_status sa_prefill_blocks_workspace_size(const sa_params *p, int32_t num_rows, int32_t q_start, int32_t q_block,
+                                           size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if ((s = check_blocks(p)) != SA_OK || (s = check_q_block(q_block)) != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    if (num_rows < 1 || q_start < 0 || (int64_t)q_start + num_rows > INT32_MAX - 64) return SA_ERR_SHAPE;
+    PrefillPlan d;
+    *bytes = plan_prefill_blocks(p, num_rows, q_start, q_block, &d).total;
+    return SA_OK;
+}
+
+sa_status sparse_attn_prefill_blocks(const sa_params *p, const sa_paged_cache *c, int32_t num_rows, int32_t q_start,
+                                     int32_t q_block, const void *q, const void *idx_q, const float *idx_w,
+                                     int32_t *block_idx, void *out, float *lse, void *workspace,
+                                     size_t workspace_bytes, void *stream)
+{
+    sa_status s = check_prefill(p, c, num_rows, q_start, true, true);
+    if (s != SA_OK) return s;
+    if ((s = check_blocks(p)) != SA_OK || (s = check_q_block(q_block)) != SA_OK) return s;
+    if (!q || !idx_q || !idx_w || !block_idx || !out) return SA_ERR_NULL;
+    PrefillPlan d;
+    const BlockPlan b = plan_prefill_blocks(p, num_rows, q_start, q_block, &d);
+    if ((s = check_ws(workspace, workspace_bytes, b.total)) != SA_OK) return s;
+    clear_hip_error();
+    prefill_blocks_impl(p, c, num_rows, q_start, q, idx_q, idx_w, block_idx, out, lse, workspace, b, d,
+                        (hipStream_t)stream, nullptr);
+    return launched();
 }
 
 }  // extern "C"

@@ -26,6 +26,8 @@ EXPORTS = (
     "sa_prefill_workspace_size", "sparse_attn_prefill", "sparse_attn_select_prefill", "sparse_attn_attend_prefill",
     "sparse_attn_decode_profiled", "sparse_attn_prefill_profiled", "sparse_attn_decode_append",
     "sa_prefill_varlen_workspace_size", "sparse_attn_prefill_varlen", "sparse_attn_prefill_varlen_profiled",
+    "sa_decode_blocks_workspace_size", "sparse_attn_decode_blocks", "sa_prefill_blocks_workspace_size",
+    "sparse_attn_prefill_blocks",
 )
 
 
@@ -81,6 +83,10 @@ def lib():
             "sparse_attn_prefill_varlen": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, sz, P]),
             "sparse_attn_prefill_varlen_profiled": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, sz, P,
                                                                    P, i32, ctypes.POINTER(i32)]),
+            "sa_decode_blocks_workspace_size": (ctypes.c_int, [pp, i32, i32, ctypes.POINTER(sz)]),
+            "sparse_attn_decode_blocks": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P]),
+            "sa_prefill_blocks_workspace_size": (ctypes.c_int, [pp, i32, i32, i32, ctypes.POINTER(sz)]),
+            "sparse_attn_prefill_blocks": (ctypes.c_int, [pp, pc, i32, i32, i32, P, P, P, P, P, P, P, sz, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -330,6 +336,61 @@ def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_start
     _check(lib().sparse_attn_prefill_varlen_profiled(*args, ev, len(events), ctypes.byref(n)),
            "sparse_attn_prefill_varlen_profiled")
     return topk_idx, out, lse, n.value
+
+
+def decode_blocks_workspace_size(p: Params, batch: int, max_ctx: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sa_decode_blocks_workspace_size(ctypes.byref(p.c()), batch, max_ctx, ctypes.byref(n)),
+           "sa_decode_blocks_workspace_size")
+    return n.value
+
+
+def prefill_blocks_workspace_size(p: Params, num_rows: int, q_start: int, q_block: int) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sa_prefill_blocks_workspace_size(ctypes.byref(p.c()), num_rows, q_start, q_block, ctypes.byref(n)),
+           "sa_prefill_blocks_workspace_size")
+    return n.value
+
+
+def sparse_attn_decode_blocks(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, want_lse=True,
+                              workspace=None, outputs=None, stream=None):
+    """Block-granular decode: p.topk counts kept KV blocks (cache blocks) per
+    row.  Returns (block_idx [B][k] int32, out [B][H][D_v], lse [B][H] or None)."""
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    blk, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(decode_blocks_workspace_size(p, B, max_ctx), q.device)
+    _check(lib().sparse_attn_decode_blocks(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
+                                           idx_q.data_ptr(), idx_w.data_ptr(), blk.data_ptr(), out.data_ptr(),
+                                           _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)),
+           "sparse_attn_decode_blocks")
+    return blk, out, lse
+
+
+def sparse_attn_prefill_blocks(p: Params, cache: PagedCache, q_start: int, q_block: int, q, idx_q, idx_w, *,
+                               want_lse=True, workspace=None, stream=None):
+    """Block-granular prefill of sequence 0: query blocks of q_block rows, p.topk
+    kept KV blocks each.  Returns (block_idx [ceil(L/q_block)][k] int32, out, lse)."""
+    torch = _torch()
+    L = q.shape[0]
+    _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
+    groups = (L + max(1, q_block) - 1) // max(1, q_block)
+    blk = torch.empty((groups, p.topk), dtype=torch.int32, device=q.device)
+    out = torch.empty((L, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
+                      device=q.device)
+    lse = torch.empty((L, p.num_heads), dtype=torch.float32, device=q.device) if want_lse else None
+    ws = workspace if workspace is not None else _workspace(prefill_blocks_workspace_size(p, L, q_start, q_block),
+                                                            q.device)
+    _check(lib().sparse_attn_prefill_blocks(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start, q_block,
+                                            q.data_ptr(), idx_q.data_ptr(), idx_w.data_ptr(), blk.data_ptr(),
+                                            out.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)),
+           "sparse_attn_prefill_blocks")
+    return blk, out, lse
 
 
 class HipEvent:

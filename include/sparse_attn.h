@@ -257,6 +257,45 @@ sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged
                                               void *const *events, int32_t num_events,
                                               int32_t *num_marks);
 
+/* ------------------------------------------- block-granular selection --
+ * The index selection keeps whole KV blocks per query block (section 3.1 of
+ * the page on domestic AI accelerators: the selection operator chooses which
+ * key-value blocks take part for each query block, keeps topk of them, under a
+ * mask, with the block mapping the attention uses).  Here:
+ *   - a KV block is a cache block: logical tokens [j*block_size, (j+1)*block_size)
+ *   - a query block is one decode row, or q_block consecutive prefill rows
+ *     (the last one may be shorter)
+ *   - p->topk = K counts KV blocks; K * block_size <= 16384
+ *   - block score of KV block j for query block G = max of the token indexer
+ *     scores score_i(s) over rows i of G and tokens s of block j with
+ *     s <= pos_i; the candidates are blocks 0 .. (last position of G) /
+ *     block_size
+ *   - kept: the K candidates of highest block score, equal scores keeping the
+ *     lower block id; all candidates when there are at most K
+ *   - row i attends (softmax, as in sparse_attn_decode) over the tokens
+ *     s <= pos_i of its query block's kept blocks (the causal mask); a
+ *     prefill row none of whose kept tokens is visible gets O = 0 and
+ *     lse = -inf
+ *   block_idx (device, out) int32 [query blocks][K]: kept block ids,
+ *     ascending, -1 padded
+ *   q, idx_q, idx_w, out, lse: as for the token-level calls
+ * Errors as for the token-level calls; SA_ERR_UNSUPPORTED when K *
+ * block_size > 16384 or q_block is not a power of two <= 128, SA_ERR_SHAPE
+ * when q_block < 1.
+ */
+sa_status sa_decode_blocks_workspace_size(const sa_params *p, int32_t batch, int32_t max_ctx,
+                                          size_t *bytes /* host, out */);
+sa_status sparse_attn_decode_blocks(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
+                                    int32_t max_ctx, const void *q, const void *idx_q, const float *idx_w,
+                                    int32_t *block_idx, void *out, float *lse, void *workspace,
+                                    size_t workspace_bytes, void *stream);
+sa_status sa_prefill_blocks_workspace_size(const sa_params *p, int32_t num_rows, int32_t q_start,
+                                           int32_t q_block, size_t *bytes /* host, out */);
+sa_status sparse_attn_prefill_blocks(const sa_params *p, const sa_paged_cache *cache, int32_t num_rows,
+                                     int32_t q_start, int32_t q_block, const void *q, const void *idx_q,
+                                     const float *idx_w, int32_t *block_idx, void *out, float *lse,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

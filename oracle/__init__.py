@@ -131,6 +131,79 @@ def run_varlen(w: dict, rows=None, want_scores: bool = False) -> dict:
     return res
 
 
+def _bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def run_blocks(w: dict, q_block: int = 1, rows=None) -> dict:
+    """Block-granular selection ("Day-0 Adaptation: Running Trillion-Parameter
+    Models on Domestic AI Accelerators", 3.1: the selection keeps the top-k
+    key-value blocks for each query block, under a mask, with the attention's
+    block mapping), read as follows.  K = shape.topk counts kept blocks; a KV
+    block is a cache block (block_size logical tokens); a query block is one
+    decode row, or q_block consecutive rows of a one-sequence prefill.
+      1. token scores score_i(s) of each row of the query block G (the
+         oracle's indexer, through `run`);
+      2. block score of block j = max of score_i(s) over rows i of G and
+         tokens s of block j with s <= pos_i; candidates j = 0 .. last_G // bs;
+      3. kept = the K candidates of highest block score, ties to the lower j
+         (the oracle's top-k on the block scores), ascending, -1 padded;
+      4. row i: softmax(scale * q_i . k_s) over the kept tokens s <= pos_i,
+         output the weighted latent rows' first v_dim entries, in float64
+         (no visible kept token: output 0, lse -inf).
+    Returns dict(groups, blocks [groups][K], out [rows][H][v_dim], lse
+    [rows][H], rows) for the listed rows (all rows by default)."""
+    sh = w["shape"]
+    K, bs = sh.topk, sh.block_size
+    T = int(w["rows"])
+    decode = w["mode"] == "decode"
+    qb = 1 if decode else int(q_block)
+    rows = np.arange(T, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    ctx = np.asarray(w["context_lens"], dtype=np.int64)
+    pos = (ctx - 1) if decode else (int(w["q_start"]) + np.arange(T, dtype=np.int64))
+    groups = np.unique(rows // qb)
+    blocks = np.full((len(groups), K), -1, dtype=np.int32)
+    kept_of = {}
+    for gi, g in enumerate(groups):
+        members = np.arange(g * qb, min(T, (g + 1) * qb), dtype=np.int64)
+        last = int(pos[members].max())
+        n = last // bs + 1 if last >= 0 else 0
+        if n <= K:
+            kept = np.arange(n, dtype=np.int32)
+        else:
+            sc = run(w, rows=members, want_scores=True)["scores"]
+            bscore = np.full(n, -np.inf, dtype=np.float32)
+            for m, i in enumerate(members):
+                p = int(pos[i])
+                for j in range(min(n, p // bs + 1)):
+                    bscore[j] = max(bscore[j], sc[m, j * bs:min(p, j * bs + bs - 1) + 1].max())
+            kept = topk(bscore, K)
+            kept = kept[kept >= 0]
+        blocks[gi, :len(kept)] = kept
+        kept_of[int(g)] = kept
+    nr = len(rows)
+    out = np.zeros((nr, sh.num_heads, sh.v_dim))
+    lse = np.full((nr, sh.num_heads), -np.inf)
+    scale = float(np.float32(sh.softmax_scale))
+    for r, i in enumerate(rows):
+        kept = kept_of[int(i // qb)]
+        toks = (kept[:, None].astype(np.int64) * bs + np.arange(bs)[None, :]).ravel()
+        toks = toks[toks <= pos[i]]
+        if len(toks) == 0:
+            continue
+        seq = int(i) if decode else 0
+        phys = w["block_table"][seq][toks // bs]
+        kv = _bf16_to_f64(w["kv"][phys, toks % bs])          # [n][qk_dim]
+        q = _bf16_to_f64(w["q"][i])                          # [H][qk_dim]
+        logits = scale * (q @ kv.T)                          # [H][n]
+        mx = logits.max(axis=1, keepdims=True)
+        e = np.exp(logits - mx)
+        z = e.sum(axis=1, keepdims=True)
+        out[r] = (e @ kv[:, :sh.v_dim]) / z
+        lse[r] = (mx + np.log(z))[:, 0]
+    return dict(groups=groups, blocks=blocks, out=out, lse=lse, rows=rows)
+
+
 def append(w: dict, new_kv: np.ndarray, new_idx_k: np.ndarray) -> dict:
     """Decode workload `w` with each sequence's current token (position
     context_lens[b] - 1) replaced by new_kv[b] / new_idx_k[b] in copies of its

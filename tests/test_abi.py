@@ -204,3 +204,32 @@ def test_prefill_varlen_validation(L):
     assert a.value == b.value > 0
     assert L.sa_prefill_varlen_workspace_size(ctypes.byref(p), 3, None, _i32(0, 5, 200),
                                               ctypes.byref(a)) == sa.SA_ERR_NULL
+
+
+def test_block_selection_validation(L):
+    """The block-granular calls check K * block_size <= 16384 and q_block (a
+    power of two <= 128) besides what the token calls check, before any HIP
+    call."""
+    p, c = _params(topk=32), _cache()
+    F = FAKE
+
+    def dec(pp=p, cc=c, batch=2, max_ctx=256, ws=1 << 40, q=F):
+        return L.sparse_attn_decode_blocks(ctypes.byref(pp), ctypes.byref(cc), batch, max_ctx, q, F, F, F, F, None,
+                                           F, ws, None)
+
+    def pre(pp=p, cc=c, rows=100, q_start=0, qb=16, ws=1 << 40, q=F):
+        return L.sparse_attn_prefill_blocks(ctypes.byref(pp), ctypes.byref(cc), rows, q_start, qb, q, F, F, F, F,
+                                            None, F, ws, None)
+
+    assert dec(q=None) == sa.SA_ERR_NULL and pre(q=None) == sa.SA_ERR_NULL
+    assert dec(pp=_params(topk=257)) == sa.SA_ERR_UNSUPPORTED      # 257 * 64 > 16384
+    assert pre(pp=_params(topk=257)) == sa.SA_ERR_UNSUPPORTED
+    assert dec(batch=0) == sa.SA_ERR_SHAPE and dec(max_ctx=257) == sa.SA_ERR_SHAPE
+    assert pre(qb=0) == sa.SA_ERR_SHAPE
+    assert pre(qb=24) == sa.SA_ERR_UNSUPPORTED and pre(qb=256) == sa.SA_ERR_UNSUPPORTED
+    assert pre(rows=200, q_start=100) == sa.SA_ERR_SHAPE            # 300 > 256 positions
+    assert dec(ws=16) == sa.SA_ERR_WORKSPACE and pre(ws=16) == sa.SA_ERR_WORKSPACE
+    n = ctypes.c_size_t()
+    assert L.sa_decode_blocks_workspace_size(ctypes.byref(p), 2, 256, ctypes.byref(n)) == sa.SA_OK and n.value > 0
+    assert L.sa_prefill_blocks_workspace_size(ctypes.byref(p), 100, 0, 128, ctypes.byref(n)) == sa.SA_OK
+    assert L.sa_prefill_blocks_workspace_size(ctypes.byref(p), 100, 0, 3, ctypes.byref(n)) == sa.SA_ERR_UNSUPPORTED

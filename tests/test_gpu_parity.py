@@ -74,6 +74,12 @@ def compare(w, res, rows=None, tag=""):
     lse = lse_all.index_select(0, idx).cpu().numpy().astype(np.float64)
     bad = np.nonzero(~np.all(tk == ref["topk"], axis=1))[0]
     assert len(bad) == 0, f"{tag}: indices differ on rows {rows[bad][:8]}"
+    check_outputs(ref, out, lse, rows, tag)
+    return ref
+
+
+def check_outputs(ref, out, lse, rows, tag):
+    """Outputs (float64 copies of the listed rows) against the oracle's."""
     assert np.isfinite(out).all(), f"{tag}: non-finite output"
     rms_all = float(np.sqrt(np.mean(ref["out"] ** 2)))
     rms = np.sqrt(np.mean(ref["out"] ** 2, axis=(1, 2), keepdims=True))
@@ -87,7 +93,6 @@ def compare(w, res, rows=None, tag=""):
         f"err/global-rms max {gerr.max():.3e} mean {gerr.mean():.3e} (rms {rms_all:.3f}); lse err max {lerr.max():.2e}")
     assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, tag
     assert lerr.max() <= LSE_ABS, tag
-    return ref
 
 
 MLA = synth.MLA
@@ -297,3 +302,73 @@ def test_prefill_varlen_equals_one_call_per_sequence(dev):
         assert torch.equal(tk[a:b], tk1), f"sequence {s}: indices differ"
         assert torch.equal(out[a:b], out1), f"sequence {s}: outputs differ"
         assert torch.equal(lse[a:b], lse1), f"sequence {s}: lse differs"
+
+
+# ------------------------------------------------- block-granular selection --
+BLOCK_CASES = {  # name: (spec, q_block, rows checked (None: all))
+    "blk_decode_ragged": (lambda: synth.small_decode("blk_dec", replace(MLA, topk=32),
+                                                     [0, 1, 63, 64, 65, 2048, 2049, 5000, 9001, 20000], seed=141),
+                          1, None),
+    "blk_decode_ties": (lambda: synth.small_decode("blk_ties", replace(MLA, topk=8, idx_int_max=1),
+                                                   [600, 4000, 12345], seed=142), 1, None),
+    "blk_decode_tiny": (lambda: synth.small_decode("blk_tiny", replace(synth.TINY, topk=4), [0, 3, 16, 64, 65, 300],
+                                                   seed=143), 1, None),
+    "blk_decode_k64_splits": (lambda: synth.small_decode("blk_k64", replace(MLA, topk=64), [5000, 9000], seed=144),
+                              1, None),
+    "blk_prefill_2500_q64": (lambda: synth.small_prefill("blk_p2500", replace(MLA, topk=16), rows=2500, seed=145),
+                             64, [0, 1, 63, 64, 1000, 2047, 2048, 2499]),
+    "blk_prefill_tiny_q16": (lambda: synth.small_prefill("blk_ptiny", replace(synth.TINY, topk=4), rows=256,
+                                                         q_start=40, seed=146), 16, None),
+    "blk_prefill_q1": (lambda: synth.small_prefill("blk_pq1", replace(MLA, topk=8), rows=300, q_start=1000,
+                                                   seed=147), 1, [0, 1, 150, 299]),
+    # last query block ragged (44 rows); early rows of a block may see none of its kept blocks
+    "blk_prefill_q128": (lambda: synth.small_prefill("blk_pq128", replace(synth.TINY, topk=3), rows=300, seed=148),
+                         128, None),
+}
+
+
+def run_blocks_gpu(dev, w, q_block):
+    torch, sa = dev
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    if w["mode"] == "decode":
+        res = sa.sparse_attn_decode_blocks(p, d["cache"], int(w["context_lens"].max()), d["q"], d["idx_q"],
+                                           d["idx_w"])
+    else:
+        res = sa.sparse_attn_prefill_blocks(p, d["cache"], w["q_start"], q_block, d["q"], d["idx_q"], d["idx_w"])
+    torch.cuda.synchronize()
+    return res
+
+
+def compare_blocks(w, res, q_block, rows=None, tag=""):
+    torch = __import__("torch")
+    blk, out_all, lse_all = res
+    ref = oracle.run_blocks(w, q_block=q_block, rows=rows)
+    got = blk.index_select(0, torch.as_tensor(ref["groups"], device=blk.device)).cpu().numpy()
+    bad = np.nonzero(~np.all(got == ref["blocks"], axis=1))[0]
+    assert len(bad) == 0, f"{tag}: kept blocks differ for query blocks {ref['groups'][bad][:8]}"
+    idx = torch.as_tensor(ref["rows"], device=out_all.device)
+    out = out_all.index_select(0, idx).float().cpu().numpy().astype(np.float64)
+    lse = lse_all.index_select(0, idx).cpu().numpy().astype(np.float64)
+    check_outputs(ref, out, lse, ref["rows"], tag)
+
+
+@pytest.mark.parametrize("name", list(BLOCK_CASES))
+def test_block_selection_parity(dev, name):
+    """Block-granular selection against the oracle's block path: kept block
+    ids bit for bit, outputs and lse to the usual bar."""
+    spec, qb, rows = BLOCK_CASES[name]
+    say(f"[gpu] block selection {name}")
+    w = synth.make(spec())
+    compare_blocks(w, run_blocks_gpu(dev, w, qb), qb, rows=rows, tag=name)
+
+
+def test_block_selection_full_size(dev):
+    """The mixed-length decode batch (64 rows, contexts 16K-128K) keeping 32
+    blocks of 64 tokens per row, on sampled rows."""
+    spec = replace(synth.WORKLOADS["decode_b64_ctx16k_128k"], shape=replace(MLA, topk=32))
+    say("[gpu] block selection, decode_b64_ctx16k_128k, 32 blocks")
+    w = synth.make(spec)
+    ctx = w["context_lens"]
+    rows = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 63})
+    compare_blocks(w, run_blocks_gpu(dev, w, 1), 1, rows=rows, tag="blk_decode_b64")

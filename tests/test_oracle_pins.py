@@ -389,3 +389,76 @@ def test_varlen_single_rows_equal_decode():
     np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
     np.testing.assert_allclose(a["lse"], b["lse"], rtol=1e-12, atol=1e-12)
     assert np.sum(a["topk"][3] >= 0) == MLA_SMALL.topk
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_blocks_of_one_token_are_tokens(mode):
+    """Block-granular selection with one-token blocks and one-row query blocks
+    is token selection: the oracle's block path (numpy block maxima, float64
+    attention in numpy) gives the token path's indices (C oracle), and the
+    same outputs."""
+    shape = replace(synth.TINY, block_size=1, topk=8)
+    if mode == "decode":
+        spec = synth.small_decode("pin_blk1_dec", shape, [0, 1, 8, 9, 40, 200], seed=61)
+    else:
+        spec = synth.small_prefill("pin_blk1_pre", shape, rows=40, q_start=5, seed=62)
+    w = synth.make(spec)
+    a = oracle.run_blocks(w, q_block=1)
+    b = oracle.run(w)
+    assert np.array_equal(a["blocks"], b["topk"])
+    np.testing.assert_allclose(a["out"], b["out"], rtol=1e-12, atol=1e-12)
+    np.testing.assert_allclose(a["lse"], b["lse"], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_blocks_covering_the_context_are_dense(mode):
+    """When every candidate block is kept, each row attends over its whole
+    causal context: dense brute force over the logical rows."""
+    if mode == "decode":
+        spec = synth.small_decode("pin_blk_dense", replace(synth.TINY, topk=32), [0, 1, 15, 16, 17, 300], seed=63)
+        qb = 1
+    else:
+        spec = synth.small_prefill("pin_blk_dense_p", replace(synth.TINY, topk=32), rows=100, q_start=200, seed=64)
+        qb = 16
+    w = synth.make(spec, keep_logical=True)
+    sh = w["shape"]
+    res = oracle.run_blocks(w, q_block=qb)
+    scale = float(np.float32(sh.softmax_scale))
+    for r in range(w["rows"]):
+        seq, n = (r, int(w["context_lens"][r])) if mode == "decode" else (0, w["q_start"] + r + 1)
+        if n == 0:
+            assert np.all(res["out"][r] == 0) and np.all(np.isneginf(res["lse"][r]))
+            continue
+        o, lse = _dense_attention(_logical_f32(w["q"][r]), _logical_f32(w["kv_logical"][seq][:n]), np.arange(n),
+                                  scale, sh.v_dim)
+        np.testing.assert_allclose(res["out"][r], o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(res["lse"][r], lse, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("mode", ["decode", "prefill"])
+def test_block_ranking_from_exact_integer_scores(mode):
+    """The kept blocks follow from the exact integer indexer (int64 closed form
+    over the logical keys): block maxima over the query block's rows and their
+    visible tokens, ranked by score, ties to the lower block id."""
+    if mode == "decode":
+        spec = synth.small_decode("pin_blk_rank", replace(MLA_SMALL, topk=8), [1000, 3000, 700], seed=65)
+        qb = 1
+    else:
+        spec = synth.small_prefill("pin_blk_rank_p", replace(synth.TINY, topk=3, idx_int_max=1), rows=64,
+                                   q_start=100, seed=66)
+        qb = 16
+    w = synth.make(spec, keep_logical=True)
+    sh = w["shape"]
+    res = oracle.run_blocks(w, q_block=qb)
+    bs = sh.block_size
+    for gi, g in enumerate(res["groups"]):
+        members = range(g * qb, min(w["rows"], (g + 1) * qb))
+        best = {}
+        for i in members:
+            x8 = _int_scores_x(w, i, 8)            # 8 * score of every visible token, exact
+            for s, v in enumerate(x8):
+                best[s // bs] = max(best.get(s // bs, v), v)
+        order = sorted(best, key=lambda j: (-best[j], j))
+        want = sorted(order[:sh.topk])
+        got = [int(j) for j in res["blocks"][gi] if j >= 0]
+        assert got == want, (g, got, want)
