@@ -130,6 +130,24 @@ def run_decode(args, torch, sa, synth):
         torch.cuda.synchronize()
         again = (time.perf_counter() - tb) * 1e3 / args.steps
         log(f"decode with append: {append_ms:.3f} ms/step (plain step again after it: {again:.3f} ms)")
+    # Run-time tuning of the attention split count on this batch, then the
+    # configured call timed like the plain one.
+    tuned = None
+    if args.tune:
+        splits, tune_us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=10)
+        wst = torch.empty(sa.decode_workspace_size_cfg(p, B, max_ctx, splits), dtype=torch.uint8, device="cuda")
+        cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"],
+                                                workspace=wst, outputs=outs)
+        for _ in range(args.warmup):
+            cfg()
+        torch.cuda.synchronize()
+        tc = time.perf_counter()
+        for _ in range(args.steps):
+            cfg()
+        torch.cuda.synchronize()
+        tuned = dict(attn_splits=splits, ms=(time.perf_counter() - tc) * 1e3 / args.steps, tune_us=tune_us)
+        log(f"tuned: {splits} attention splits per row, {tuned['ms']:.3f} ms/step (tuner's own mean {tune_us:.1f} us)")
+        del wst
     # Block-granular selection over the same batch: k / block_size whole cache
     # blocks per row (the same number of attended token slots), timed the same way.
     blocks_ms = None
@@ -180,7 +198,8 @@ def run_decode(args, torch, sa, synth):
         del flush
     alg = decode_algorithmic(w)
     return w, dict(ms=ms, stages=stages, cold_ms=statistics.median(cold) if cold else None, alg=alg,
-                   per_kernel=per_kernel, append_ms=append_ms, ms_marked=ms_marked, blocks_ms=blocks_ms)
+                   per_kernel=per_kernel, append_ms=append_ms, ms_marked=ms_marked, blocks_ms=blocks_ms,
+                   tuned=tuned)
 
 
 def run_other_decodes(args, torch, sa, synth, names):
@@ -197,6 +216,10 @@ def run_other_decodes(args, torch, sa, synth, names):
                      "hbm_frac": round(dec["alg"]["bytes"] / (dec["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
                      "algorithmic_bytes_per_step": dec["alg"]["bytes"],
                      "stages_us": {k: round(v * 1e3, 2) for k, v in dec["stages"].items()}}
+        if dec["tuned"]:
+            res[name]["tuned"] = {"attn_splits": dec["tuned"]["attn_splits"],
+                                  "ms_per_step": round(dec["tuned"]["ms"], 4),
+                                  "tokens_per_s": round(B / (dec["tuned"]["ms"] / 1e3), 1)}
         del w, dec
         torch.cuda.empty_cache()
     return res
@@ -382,6 +405,8 @@ def main():
     ap.add_argument("--blocks-steps", type=int, default=20,
                     help="steps of block-granular decode (sparse_attn_decode_blocks, k / block_size blocks per "
                          "row) over the same batch")
+    ap.add_argument("--no-tune", dest="tune", action="store_false",
+                    help="skip the run-time tuning of the attention split count (sa_decode_tune)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--other-workloads", default="none",
@@ -467,6 +492,11 @@ def main():
         line["decode_append"] = {"ms_per_step": round(dec["append_ms"], 4),
                                  "tokens_per_s": round(B / (dec["append_ms"] / 1e3), 1),
                                  "added_us": round((dec["append_ms"] - dec["ms"]) * 1e3, 2)}
+    if dec.get("tuned"):
+        # supplementary: the split count picked by sa_decode_tune on this batch
+        t = dec["tuned"]
+        line["decode_tuned"] = {"attn_splits": t["attn_splits"], "ms_per_step": round(t["ms"], 4),
+                                "tokens_per_s": round(B / (t["ms"] / 1e3), 1)}
     if dec.get("blocks_ms"):
         # supplementary: block-granular selection over the same batch
         line["decode_blocks"] = {"ms_per_step": round(dec["blocks_ms"], 4),

@@ -1,7 +1,8 @@
 // libsparse_attn: C ABI (include/sparse_attn.h) over the gfx950 kernels.
 //
 // Every check runs before the first HIP call; the library never allocates,
-// never synchronises and keeps no mutable global state.  Work is queued on the
+// never synchronises (the tuner aside, which measures) and keeps no mutable
+// global state.  Work is queued on the
 // caller's stream in this order:
 //   decode : indexer scan -> per-row top-k -> split attention -> split merge
 //   prefill: per chunk of rows { indexer tile scan -> per-row top-k },
@@ -84,13 +85,15 @@ struct DecodePlan {
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
 };
 
-DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx)
+// want_splits > 0 asks for that many attention splits per row (clamped to
+// what k allows); 0 takes one attention workgroup per CU over the batch
+DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_splits = 0)
 {
     DecodePlan d{};
     d.score_stride = round_up(max_ctx > 0 ? max_ctx : 1, 64);
     const int k = p->topk;
     const int vsplit = p->v_dim > 256 ? 2 : 1;  // value halves per (row, split), as in the attention kernel
-    int splits = std::max(1, kTargetAttnBlocks / (batch * vsplit));
+    int splits = want_splits > 0 ? want_splits : std::max(1, kTargetAttnBlocks / (batch * vsplit));
     splits = std::max(1, std::min(splits, (k + 31) / 32));
     splits = std::max(splits, (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens);
     int tps = (int)round_up((k + splits - 1) / splits, 32);
@@ -766,12 +769,12 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *c,
 static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
                              float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk,
-                             const void *new_kv = nullptr, const void *new_idx_k = nullptr)
+                             const void *new_kv = nullptr, const void *new_idx_k = nullptr, int want_splits = 0)
 {
     sa_status s = check_decode(p, c, batch, max_ctx, true, true);
     if (s != SA_OK) return s;
     if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
-    const DecodePlan d = plan_decode(p, batch, max_ctx);
+    const DecodePlan d = plan_decode(p, batch, max_ctx, want_splits);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     clear_hip_error();
@@ -942,6 +945,109 @@ sa_status sparse_attn_prefill_profiled(const sa_params *p, const sa_paged_cache 
                                      workspace_bytes, stream, &mk);
     *num_marks = mk.count;
     return s;
+}
+
+// ------------------------------------------------------- run-time tuning --
+static sa_status check_cfg(const sa_decode_config *cfg)
+{
+    if (cfg && (cfg->attn_splits < 0 || cfg->attn_splits > 1024)) return SA_ERR_SHAPE;
+    return SA_OK;
+}
+
+sa_status sa_decode_workspace_size_cfg(const sa_params *p, int32_t batch, int32_t max_ctx,
+                                       const sa_decode_config *cfg, size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if ((s = check_cfg(cfg)) != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    if (batch < 1 || max_ctx < 0) return SA_ERR_SHAPE;
+    *bytes = plan_decode(p, batch, max_ctx, cfg ? cfg->attn_splits : 0).total;
+    return SA_OK;
+}
+
+sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                 const sa_decode_config *cfg, const void *q, const void *idx_q, const float *idx_w,
+                                 int32_t *topk_idx, void *out, float *lse, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    const sa_status s = check_cfg(cfg);
+    if (s != SA_OK) return s;
+    return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
+                       nullptr, nullptr, nullptr, cfg ? cfg->attn_splits : 0);
+}
+
+// The split counts the tuner tries: every count the plan can realise (k is
+// split into 32-token multiples of at most 2048 tokens), up to 64.
+static std::vector<int> tune_candidates(const sa_params *p, int batch, int max_ctx)
+{
+    std::vector<int> out;
+    for (int want = 1; want <= 64; ++want) {
+        const int got = plan_decode(p, batch, max_ctx, want).splits;
+        if (std::find(out.begin(), out.end(), got) == out.end()) out.push_back(got);
+    }
+    return out;
+}
+
+sa_status sa_decode_tune_workspace_size(const sa_params *p, int32_t batch, int32_t max_ctx, size_t *bytes)
+{
+    sa_status s = check_params(p);
+    if (s != SA_OK) return s;
+    if (!bytes) return SA_ERR_NULL;
+    if (batch < 1 || max_ctx < 0) return SA_ERR_SHAPE;
+    size_t need = plan_decode(p, batch, max_ctx).total;
+    for (int sp : tune_candidates(p, batch, max_ctx)) need = std::max(need, plan_decode(p, batch, max_ctx, sp).total);
+    *bytes = need;
+    return SA_OK;
+}
+
+sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx, const void *q,
+                         const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                         void *workspace, size_t workspace_bytes, void *stream, int32_t reps,
+                         sa_decode_config *best, float *best_us)
+{
+    sa_status s = check_decode(p, c, batch, max_ctx, true, true);
+    if (s != SA_OK) return s;
+    if (!q || !idx_q || !idx_w || !topk_idx || !out || !best) return SA_ERR_NULL;
+    if (reps < 1 || reps > 1000) return SA_ERR_SHAPE;
+    size_t need = 0;
+    if ((s = sa_decode_tune_workspace_size(p, batch, max_ctx, &need)) != SA_OK) return s;
+    if ((s = check_ws(workspace, workspace_bytes, need)) != SA_OK) return s;
+    hipStream_t st = (hipStream_t)stream;
+    hipEvent_t e0 = nullptr, e1 = nullptr;
+    if (hipEventCreate(&e0) != hipSuccess || hipEventCreate(&e1) != hipSuccess) {
+        if (e0) (void)hipEventDestroy(e0);
+        return SA_ERR_HIP;
+    }
+    float best_t = INFINITY;
+    int best_sp = 0;
+    s = SA_OK;
+    for (int sp : tune_candidates(p, batch, max_ctx)) {
+        // one untimed call, then reps timed back to back
+        for (int i = 0; i <= reps && s == SA_OK; ++i) {
+            if (i == 1 && hipEventRecord(e0, st) != hipSuccess) s = SA_ERR_HIP;
+            if (s == SA_OK)
+                s = decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                                workspace_bytes, stream, nullptr, nullptr, nullptr, sp);
+        }
+        float ms = 0.0f;
+        if (s == SA_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+                           hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
+            s = SA_ERR_HIP;
+        if (s != SA_OK) break;
+        const float us = ms * 1000.0f / reps;
+        if (us < best_t) {
+            best_t = us;
+            best_sp = sp;
+        }
+    }
+    (void)hipEventDestroy(e0);
+    (void)hipEventDestroy(e1);
+    if (s != SA_OK) return s;
+    *best = sa_decode_config{};
+    best->attn_splits = best_sp;
+    if (best_us) *best_us = best_t;
+    return SA_OK;
 }
 
 // ------------------------------------------------ block-granular selection --

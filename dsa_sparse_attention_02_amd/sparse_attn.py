@@ -27,8 +27,13 @@ EXPORTS = (
     "sparse_attn_decode_profiled", "sparse_attn_prefill_profiled", "sparse_attn_decode_append",
     "sa_prefill_varlen_workspace_size", "sparse_attn_prefill_varlen", "sparse_attn_prefill_varlen_profiled",
     "sa_decode_blocks_workspace_size", "sparse_attn_decode_blocks", "sa_prefill_blocks_workspace_size",
-    "sparse_attn_prefill_blocks",
+    "sparse_attn_prefill_blocks", "sa_decode_workspace_size_cfg", "sparse_attn_decode_cfg",
+    "sa_decode_tune_workspace_size", "sa_decode_tune",
 )
+
+
+class sa_decode_config(ctypes.Structure):
+    _fields_ = [("attn_splits", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
 
 
 class sa_params(ctypes.Structure):
@@ -87,6 +92,11 @@ def lib():
             "sparse_attn_decode_blocks": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P]),
             "sa_prefill_blocks_workspace_size": (ctypes.c_int, [pp, i32, i32, i32, ctypes.POINTER(sz)]),
             "sparse_attn_prefill_blocks": (ctypes.c_int, [pp, pc, i32, i32, i32, P, P, P, P, P, P, P, sz, P]),
+            "sa_decode_workspace_size_cfg": (ctypes.c_int, [pp, i32, i32, P, ctypes.POINTER(sz)]),
+            "sparse_attn_decode_cfg": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, P, sz, P]),
+            "sa_decode_tune_workspace_size": (ctypes.c_int, [pp, i32, i32, ctypes.POINTER(sz)]),
+            "sa_decode_tune": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P, i32, P,
+                                              ctypes.POINTER(ctypes.c_float)]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -391,6 +401,55 @@ def sparse_attn_prefill_blocks(p: Params, cache: PagedCache, q_start: int, q_blo
                                             out.data_ptr(), _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)),
            "sparse_attn_prefill_blocks")
     return blk, out, lse
+
+
+def _cfg(attn_splits: int):
+    return sa_decode_config(attn_splits=attn_splits)
+
+
+def decode_workspace_size_cfg(p: Params, batch: int, max_ctx: int, attn_splits: int = 0) -> int:
+    n = ctypes.c_size_t()
+    _check(lib().sa_decode_workspace_size_cfg(ctypes.byref(p.c()), batch, max_ctx,
+                                              ctypes.byref(_cfg(attn_splits)), ctypes.byref(n)),
+           "sa_decode_workspace_size_cfg")
+    return n.value
+
+
+def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_splits: int, q, idx_q, idx_w, *,
+                           want_lse=True, workspace=None, outputs=None, stream=None):
+    """sparse_attn_decode with attn_splits attention splits per row (0 = default)."""
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size_cfg(p, B, max_ctx, attn_splits),
+                                                            q.device)
+    _check(lib().sparse_attn_decode_cfg(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
+                                        ctypes.byref(_cfg(attn_splits)), q.data_ptr(), idx_q.data_ptr(),
+                                        idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
+                                        ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode_cfg")
+    return topk_idx, out, lse
+
+
+def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, reps=10, stream=None):
+    """Run-time tuning of the decode split count on these inputs (waits for
+    the stream).  Returns (attn_splits, microseconds per call)."""
+    torch = _torch()
+    B = q.shape[0]
+    n = ctypes.c_size_t()
+    _check(lib().sa_decode_tune_workspace_size(ctypes.byref(p.c()), B, max_ctx, ctypes.byref(n)),
+           "sa_decode_tune_workspace_size")
+    ws = _workspace(n.value, q.device)
+    topk_idx, out, lse = _outputs(p, B, q.device, True)
+    best = sa_decode_config()
+    us = ctypes.c_float()
+    _check(lib().sa_decode_tune(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
+                                idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
+                                ws.data_ptr(), ws.numel(), _stream(stream), reps, ctypes.byref(best),
+                                ctypes.byref(us)), "sa_decode_tune")
+    return best.attn_splits, us.value
 
 
 class HipEvent:

@@ -28,7 +28,8 @@
  *    library never allocates or frees device memory and keeps no mutable global
  *    state; calls on different streams with different workspaces may overlap.
  *  - Streams: all work is queued on `stream` (a hipStream_t; NULL = the null
- *    stream).  No call synchronises; SA_OK means "queued".
+ *    stream).  No call synchronises (except sa_decode_tune, which measures);
+ *    SA_OK means "queued".
  *  - Errors: every argument check runs before the first HIP call, so a
  *    rejected call touches no device state.  NULL required pointer ->
  *    SA_ERR_NULL; inconsistent sizes -> SA_ERR_SHAPE; a valid parameter set the
@@ -256,6 +257,47 @@ sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged
                                               void *workspace, size_t workspace_bytes, void *stream,
                                               void *const *events, int32_t num_events,
                                               int32_t *num_marks);
+
+/* ----------------------------------------------------- run-time tuning --
+ * Kernel tuning at run time (the page on the compute software stack names
+ * auto-tuning of block sizes and unrolling at run time as the next step for
+ * sparse attention operators).  The tunable here is the number of splits of
+ * each decode row's k keys across attention workgroups (merged afterwards):
+ * the default takes one attention workgroup per compute unit over the batch;
+ * the best count also depends on the context lengths and the cache's
+ * placement, which only a run on the caller's data measures.
+ *   attn_splits: 0 = the library's choice; otherwise requested splits per row,
+ *                clamped to what k allows (32-token multiples of at most 2048
+ *                tokens per split); results do not depend on it beyond
+ *                floating-point rounding order
+ */
+typedef struct {
+    int32_t attn_splits;
+    int32_t reserved[3];   /* zero */
+} sa_decode_config;
+
+/* sparse_attn_decode with a configuration (NULL = defaults).  SA_ERR_SHAPE
+ * for attn_splits outside [0, 1024]; otherwise as sparse_attn_decode. */
+sa_status sa_decode_workspace_size_cfg(const sa_params *p, int32_t batch, int32_t max_ctx,
+                                       const sa_decode_config *cfg, size_t *bytes /* host, out */);
+sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
+                                 int32_t max_ctx, const sa_decode_config *cfg, const void *q,
+                                 const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
+                                 float *lse, void *workspace, size_t workspace_bytes, void *stream);
+/* Times sparse_attn_decode_cfg on the given inputs for every split count the
+ * plan can realise (up to 64): one untimed call, then `reps` (1..1000) calls
+ * between two HIP events on `stream`, per count; writes the fastest into
+ * *best (and its mean microseconds per call into *best_us when non-NULL).
+ * Unlike every other call it creates two HIP events, waits for the stream
+ * and leaves the outputs of the last call tried.  The workspace must hold
+ * sa_decode_tune_workspace_size bytes (the largest of the candidates). */
+sa_status sa_decode_tune_workspace_size(const sa_params *p, int32_t batch, int32_t max_ctx,
+                                        size_t *bytes /* host, out */);
+sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *cache, int32_t batch, int32_t max_ctx,
+                         const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx,
+                         void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
+                         int32_t reps, sa_decode_config *best /* host, out */,
+                         float *best_us /* host, out, nullable */);
 
 /* ------------------------------------------- block-granular selection --
  * The index selection keeps whole KV blocks per query block (section 3.1 of

@@ -233,3 +233,35 @@ def test_block_selection_validation(L):
     assert L.sa_decode_blocks_workspace_size(ctypes.byref(p), 2, 256, ctypes.byref(n)) == sa.SA_OK and n.value > 0
     assert L.sa_prefill_blocks_workspace_size(ctypes.byref(p), 100, 0, 128, ctypes.byref(n)) == sa.SA_OK
     assert L.sa_prefill_blocks_workspace_size(ctypes.byref(p), 100, 0, 3, ctypes.byref(n)) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_decode_cfg_and_tune_validation(L):
+    """The configured decode and the tuner check the configuration, the
+    repetition count and the workspace before any HIP call."""
+    p, c = _params(), _cache()
+    F = FAKE
+
+    def cfg_call(cfg, ws=1 << 40):
+        return L.sparse_attn_decode_cfg(ctypes.byref(p), ctypes.byref(c), 2, 256,
+                                        ctypes.byref(cfg) if cfg is not None else None, F, F, F, F, F, None, F, ws,
+                                        None)
+
+    assert cfg_call(sa.sa_decode_config(attn_splits=-1)) == sa.SA_ERR_SHAPE
+    assert cfg_call(sa.sa_decode_config(attn_splits=2000)) == sa.SA_ERR_SHAPE
+    assert cfg_call(None, ws=16) == sa.SA_ERR_WORKSPACE
+    assert cfg_call(sa.sa_decode_config(attn_splits=7), ws=16) == sa.SA_ERR_WORKSPACE
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.sa_decode_workspace_size_cfg(ctypes.byref(p), 2, 256, None, ctypes.byref(a)) == sa.SA_OK
+    assert L.sa_decode_workspace_size(ctypes.byref(p), 2, 256, ctypes.byref(b)) == sa.SA_OK
+    assert a.value == b.value
+    assert L.sa_decode_tune_workspace_size(ctypes.byref(p), 2, 256, ctypes.byref(b)) == sa.SA_OK
+    assert b.value >= a.value
+    best, us = sa.sa_decode_config(), ctypes.c_float()
+
+    def tune(reps=5, ws=1 << 40, best_p=ctypes.byref(best)):
+        return L.sa_decode_tune(ctypes.byref(p), ctypes.byref(c), 2, 256, F, F, F, F, F, None, F, ws, None, reps,
+                                best_p, ctypes.byref(us))
+
+    assert tune(best_p=None) == sa.SA_ERR_NULL
+    assert tune(reps=0) == sa.SA_ERR_SHAPE
+    assert tune(ws=16) == sa.SA_ERR_WORKSPACE

@@ -372,3 +372,38 @@ def test_block_selection_full_size(dev):
     ctx = w["context_lens"]
     rows = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 63})
     compare_blocks(w, run_blocks_gpu(dev, w, 1), 1, rows=rows, tag="blk_decode_b64")
+
+
+# ------------------------------------------------------- run-time tuning --
+@pytest.mark.parametrize("splits", [1, 3, 7, 64])
+def test_decode_split_counts(dev, splits):
+    """The configured decode at several attention split counts (64 is clamped
+    to what k = 2048 allows) matches the oracle."""
+    torch, sa = dev
+    spec = CASES["decode_ragged"]()
+    say(f"[gpu] decode with {splits} attention splits")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    res = sa.sparse_attn_decode_cfg(p, d["cache"], int(w["context_lens"].max()), splits, d["q"], d["idx_q"],
+                                    d["idx_w"])
+    torch.cuda.synchronize()
+    compare(w, res, tag=f"decode_ragged splits={splits}")
+
+
+def test_decode_tune_then_run(dev):
+    """The tuner returns a split count the plan realises; the configured call
+    with it matches the oracle."""
+    torch, sa = dev
+    spec = CASES["decode_ragged"]()
+    say("[gpu] decode tuning")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    max_ctx = int(w["context_lens"].max())
+    splits, us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=3)
+    say(f"  tuned: {splits} splits, {us:.1f} us per call")
+    assert 1 <= splits <= 64 and us > 0
+    res = sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"])
+    torch.cuda.synchronize()
+    compare(w, res, tag=f"decode_ragged tuned splits={splits}")
