@@ -393,9 +393,9 @@ def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=100,
-                    help="untimed steps first; a few milliseconds of work leave the clocks below their "
-                         "loaded level, so the default warms up for about 30 ms")
+    ap.add_argument("--warmup", type=int, default=300,
+                    help="untimed steps first; tens of milliseconds of work can leave the clocks below their "
+                         "loaded level, so the default warms up for about 0.1 s")
     ap.add_argument("--workload", default="decode_b64_ctx16k_128k")
     ap.add_argument("--flush-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush")
     ap.add_argument("--prefill-steps", type=int, default=2)

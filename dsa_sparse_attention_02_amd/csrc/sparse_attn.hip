@@ -32,6 +32,10 @@ using namespace sa;
 
 constexpr int kMaxTopk = 16384;
 constexpr int kTargetAttnBlocks = 256;        // one attention workgroup per CU of an MI355X
+// Default split cap: past about 24 splits per row the merge of the partials
+// costs more than the extra workgroups gain (batches of 1, 2 and 4 at long
+// contexts ran 3-8% faster at 22 splits than at 32 or 64).
+constexpr int kMaxDefaultSplits = 24;
 constexpr int kCUs = 256;                     // compute units of an MI355X
 #ifndef SA_SCAN_BLOCKS_PER_CU
 #define SA_SCAN_BLOCKS_PER_CU 1
@@ -93,7 +97,8 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_spli
     d.score_stride = round_up(max_ctx > 0 ? max_ctx : 1, 64);
     const int k = p->topk;
     const int vsplit = p->v_dim > 256 ? 2 : 1;  // value halves per (row, split), as in the attention kernel
-    int splits = want_splits > 0 ? want_splits : std::max(1, kTargetAttnBlocks / (batch * vsplit));
+    int splits = want_splits > 0 ? want_splits
+                                 : std::max(1, std::min(kMaxDefaultSplits, kTargetAttnBlocks / (batch * vsplit)));
     splits = std::max(1, std::min(splits, (k + 31) / 32));
     splits = std::max(splits, (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens);
     int tps = (int)round_up((k + splits - 1) / splits, 32);

@@ -375,20 +375,23 @@ def test_block_selection_full_size(dev):
 
 
 # ------------------------------------------------------- run-time tuning --
-@pytest.mark.parametrize("splits", [1, 3, 7, 64])
-def test_decode_split_counts(dev, splits):
-    """The configured decode at several attention split counts (64 is clamped
-    to what k = 2048 allows) matches the oracle."""
+@pytest.mark.parametrize("case,splits", [("decode_ragged", 1), ("decode_ragged", 3), ("decode_ragged", 7),
+                                         ("decode_ragged", 64), ("decode_v64_splits", 32),
+                                         ("decode_v64_splits", 64)])
+def test_decode_split_counts(dev, case, splits):
+    """The configured decode at several attention split counts matches the
+    oracle; value width 64 with 32 and 64 splits drives the merge's
+    partial-wave column loop with more splits than active lanes."""
     torch, sa = dev
-    spec = CASES["decode_ragged"]()
-    say(f"[gpu] decode with {splits} attention splits")
+    spec = CASES[case]()
+    say(f"[gpu] {case} with {splits} attention splits")
     w = synth.make(spec)
     d = sa.to_device(w)
     p = sa.Params.from_shape(w["shape"])
     res = sa.sparse_attn_decode_cfg(p, d["cache"], int(w["context_lens"].max()), splits, d["q"], d["idx_q"],
                                     d["idx_w"])
     torch.cuda.synchronize()
-    compare(w, res, tag=f"decode_ragged splits={splits}")
+    compare(w, res, tag=f"{case} splits={splits}")
 
 
 def test_decode_tune_then_run(dev):
