@@ -410,3 +410,14 @@ def test_decode_tune_then_run(dev):
     res = sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"])
     torch.cuda.synchronize()
     compare(w, res, tag=f"decode_ragged tuned splits={splits}")
+
+
+def test_block_selection_prefill_chunks(dev):
+    """Block-granular prefill over 32768 rows at up to 32K keys: the scores
+    come in chunks of 8192 rows (1 GiB each), so query blocks of 64 rows in
+    four chunks; rows sampled on both sides of the chunk boundaries."""
+    spec = replace(synth.WORKLOADS["prefill_L32k"], shape=replace(MLA, topk=32))
+    say("[gpu] block selection, prefill 32K rows in four chunks, query blocks of 64")
+    w = synth.make(spec)
+    rows = [0, 63, 8191, 8192, 16383, 16384, 20000, 32767]
+    compare_blocks(w, run_blocks_gpu(dev, w, 64), 64, rows=rows, tag="blk_prefill_L32k_q64")
