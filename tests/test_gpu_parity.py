@@ -215,6 +215,8 @@ APPEND_CASES = {
                                                   idx_int_max=1),
     "append_tiny": lambda: synth.small_decode("append_tiny", synth.TINY, [0, 3, 16, 64, 65, 300], seed=123),
     "append_decode_b32_ctx8k": lambda: synth.WORKLOADS["decode_b32_ctx8k"],
+    # longer than 262144 keys: the many-workgroup top-k stores the new rows
+    "append_long_mb": lambda: synth.small_decode("append_long", V64, [300_001, 262_145, 1, 0], seed=124),
 }
 
 
