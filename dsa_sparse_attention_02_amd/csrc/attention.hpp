@@ -593,15 +593,18 @@ __device__ __forceinline__ float combine_block_reduce(float v, bool is_max, floa
     return t;
 }
 
-template <int V>
-__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
-                                                      const float *__restrict__ part_ml, int splits,
-                                                      int num_heads, void *__restrict__ out, int out_bf16,
-                                                      float *__restrict__ lse)
+// HPB heads per workgroup, blockDim.x / HPB threads each (HPB > 1 only with
+// at most 64 splits, where every wave works on its own).
+template <int V, int HPB>
+__global__ __launch_bounds__(128 * HPB) void combine_kernel(const float *__restrict__ part_o,
+                                                            const float *__restrict__ part_ml, int splits,
+                                                            int num_heads, void *__restrict__ out, int out_bf16,
+                                                            float *__restrict__ lse)
 {
     __shared__ float wgt[kCombineWeights];
     __shared__ float red[2];
-    const int h = blockIdx.x, r = blockIdx.y, tid = threadIdx.x, nt = blockDim.x;
+    const int nt = blockDim.x / HPB, h = blockIdx.x * HPB + threadIdx.x / nt, r = blockIdx.y;
+    const int tid = threadIdx.x % nt;
     const int64_t base = (int64_t)r * splits * num_heads + h;  // partial (r, split 0, h)
     auto ml_of = [&](int s) { return *reinterpret_cast<const f32x4 *>(part_ml + (base + (int64_t)s * num_heads) * 4); };
     const bool wave_path = splits <= 64;  // (block-uniform) every wave on its own, one split per lane

@@ -416,11 +416,14 @@ void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st, StageMarks
     if (mk) mk->mark();
     if (a.splits > 1) {
         dim3 cg(p->num_heads, rows);
-        if (p->v_dim == 512)
-            hipLaunchKernelGGL((combine_kernel<512>), cg, dim3(128), 0, st, a.part_o, a.part_ml, a.splits,
+        if (p->v_dim == 512 && a.splits <= 64 && p->num_heads % 4 == 0)  // 4 heads per workgroup
+            hipLaunchKernelGGL((combine_kernel<512, 4>), dim3(p->num_heads / 4, rows), dim3(512), 0, st, a.part_o,
+                               a.part_ml, a.splits, p->num_heads, a.out, a.out_bf16, a.lse);
+        else if (p->v_dim == 512)
+            hipLaunchKernelGGL((combine_kernel<512, 1>), cg, dim3(128), 0, st, a.part_o, a.part_ml, a.splits,
                                p->num_heads, a.out, a.out_bf16, a.lse);
         else
-            hipLaunchKernelGGL((combine_kernel<64>), cg, dim3(64), 0, st, a.part_o, a.part_ml, a.splits,
+            hipLaunchKernelGGL((combine_kernel<64, 1>), cg, dim3(64), 0, st, a.part_o, a.part_ml, a.splits,
                                p->num_heads, a.out, a.out_bf16, a.lse);
         if (mk) mk->mark();
     }
