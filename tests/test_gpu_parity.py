@@ -423,3 +423,15 @@ def test_block_selection_prefill_chunks(dev):
     w = synth.make(spec)
     rows = [0, 63, 8191, 8192, 16383, 16384, 20000, 32767]
     compare_blocks(w, run_blocks_gpu(dev, w, 64), 64, rows=rows, tag="blk_prefill_L32k_q64")
+
+
+def test_decode_large_batch(dev):
+    """512 rows of 2049-4000 keys: each persistent scan workgroup's pairs of
+    tiles run across many row boundaries (a query and weight reload at each),
+    and the attention runs one split per row with no merge."""
+    rng = np.random.default_rng(151)
+    ctx = [int(x) for x in rng.integers(2049, 4001, size=512)]
+    spec = synth.small_decode("decode_b512", MLA, ctx, seed=151)
+    say("[gpu] decode, 512 rows of 2049-4000 keys")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w), rows=[0, 1, 2, 255, 256, 257, 400, 511], tag="decode_b512")
