@@ -16,29 +16,34 @@
 // the next tile's gather is in flight while the current one is computed (same
 // item: prefetch of the next KV block during attention).
 //
-// gfx950 mapping.  One workgroup = one (row, split, value half); wave w owns heads
-// 32w..32w+31 and keeps their query rows in registers for the whole split.  Per
+// gfx950 mapping.  One workgroup = one (row, split) over all heads: 2 * HB waves,
+// two per 32-head block.  The two waves of a head block ("partners" x = 0, 1)
+// split both contractions: for q.k, partner x holds the query of its 32 heads
+// over half of the QK dims (QK = 576: 72 registers) and computes a partial S^T
+// over that half; for P.V it owns half of the V value columns (V = 512: 32 x
+// 256 fp32 accumulators, 128 registers).  The partners add their partial S^T
+// through LDS, so no logit is computed twice, and with 8 waves two run on each
+// SIMD (256 registers each), hiding each other's LDS and MFMA latencies.  Per
 // tile of 32 kept tokens:
 //   * the 32 latent rows are copied HBM -> LDS by buffer-form LDS-DMA, one
 //     resource per token row: a 64-lane copy of its first 1 KiB and an 8-lane
 //     copy of its 128-byte tail; the main rows' 16-byte pieces are XOR-swizzled
 //     by token (through the copy's per-lane source offsets) so that MFMA
-//     operand reads do not collide on LDS banks; a ring of 4 tile buffers
-//     keeps 3 tiles' copies in flight while one tile is computed;
-//   * the query of 32 heads (QK = 576: 144 registers per lane) and the 32 x 512
-//     fp32 output accumulators (256 registers) of one wave do not fit in the
-//     512-entry register file next to the q.k accumulator, so for V = 512 two
-//     workgroups share a (row, split), each owning 256 value columns and each
-//     computing the logits itself;
-//   * S^T[token][head] = K . Q^T on 32x32x16 bf16 MFMAs (K from LDS, Q^T from
-//     registers, contraction over QK in 16-wide steps);
+//     operand reads do not collide on LDS banks; a ring of 3 tile buffers keeps
+//     the next tile's copies in flight while one tile's values and the
+//     following tile's keys are read;
+//   * partial S^T[token][head] = K . Q^T on 32x32x16 bf16 MFMAs (K from LDS,
+//     Q^T from registers, contraction over the partner's QK half in 16-wide
+//     steps), exchanged through LDS and summed;
 //   * softmax in base 2 in fp32 against a per-head reference max taken from
 //     the first tile with a valid token; it never moves, so the output
 //     accumulators are touched only by MFMAs (a split whose logits outgrow the
 //     reference by more than 64 is recomputed exactly with its true max);
 //   * the S^T accumulator already has the register layout of the B operand of
 //     O^T[v][head] += V^T[v][token] . P^T[token][head]: P is only rounded to bf16.
-//     The softmax denominator sums the same rounded P.
+//     Rows that keep fewer than kPreciseBelow keys carry P as a pair of bf16
+//     values (hi + lo, two MFMAs), so the weights are exact to about 2^-16; the
+//     softmax denominator sums exactly the weights the MFMAs multiply.
 //     The V^T operand comes straight from the token-major tile through
 //     transposed LDS reads (ds_read_b64_tr_b16), four tokens per read.
 #pragma once
@@ -49,6 +54,11 @@ namespace sa {
 
 constexpr int kAttnMaxSplitTokens = 2048;
 constexpr uint32_t kNoRow = 0xFFFFFFFFu;
+// Rows keeping fewer keys than this multiply V by P as a hi/lo pair of bf16
+// values.  A row's output error from rounding P to bf16 alone is about
+// 2^-9 / sqrt(effective keys) of its values, which for rows of a few keys is
+// several percent of the output RMS of a batch of longer rows.
+constexpr int kPreciseBelow = 2048;
 
 struct AttnArgs {
     const uint16_t *q;           // [rows][H][QK]
@@ -69,17 +79,13 @@ struct AttnArgs {
 };
 
 #ifndef SA_ATTN_KPF
-#define SA_ATTN_KPF 6  // K operand steps read ahead of their MFMA
+#define SA_ATTN_KPF 4  // K operand steps read ahead of their MFMA
 #endif
 #ifndef SA_ATTN_VPF
-#define SA_ATTN_VPF 4  // V operand steps read ahead of their MFMAs
-#endif
-#ifndef SA_ATTN_FENCE
-#define SA_ATTN_FENCE 1  // 1: a scheduling fence closes every MFMA step
+#define SA_ATTN_VPF 3  // V operand steps read ahead of their MFMAs
 #endif
 
-constexpr int kAttnBuffers = 4;  // tile ring: kAttnBuffers - 1 tiles in flight while one is computed
-
+constexpr int kAttnBuffers = 4;  // tile ring: two tiles in flight while two are read
 
 template <int N>
 __device__ __forceinline__ void attn_wait_vmcnt()
@@ -88,11 +94,11 @@ __device__ __forceinline__ void attn_wait_vmcnt()
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int QK, int V>
+template <int QK, int V, int NP>
 struct AttnShape {
     static constexpr int KS = QK / 16;                   // MFMA steps of q.k
-    static constexpr int VSPLIT = V > 256 ? 2 : 1;       // workgroups sharing one (row, split), by v range
-    static constexpr int VW = V / VSPLIT;                // v columns per workgroup
+    static constexpr int KP = KS / NP;                   // steps per partner
+    static constexpr int VW = V / NP;                    // value columns per partner
     static constexpr int NVT = VW / 32;                  // 32-column output tiles per wave
     static constexpr int PIECES = QK / 8;                // 16-byte pieces per latent row
     // LDS image of a 32-token tile.  Main rows: pieces 0..63 of each token
@@ -108,7 +114,7 @@ struct AttnShape {
     static constexpr int TAIL_BASE = 32 * MAIN_STRIDE;
     static constexpr int TILE_BYTES = TAIL_BASE + 32 * TAIL_STRIDE;
     static constexpr int COPIES_PER_TOKEN = (MAIN ? 1 : 0) + 1;  // main row, tail
-    static_assert(QK % 16 == 0 && VW % 32 == 0 && V <= QK, "shape family");
+    static_assert(KS % NP == 0 && V % (32 * NP) == 0 && V <= QK, "shape family");
     static_assert(TAIL == 8, "the tail is one 8-lane copy of 128 bytes");
     static_assert(V <= 8 * (MAIN ? MAIN : TAIL), "value columns must lie in one row region");
 };
@@ -132,6 +138,8 @@ __device__ __attribute__((aligned(16))) const uint8_t kZeroLatentRow[2048] = {};
 __device__ __forceinline__ uint32_t lane_read(uint32_t v, int l) { return __builtin_amdgcn_readlane(v, l); }
 __device__ __forceinline__ int wave_uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 // l + the two bf16 values packed in w (each times 1.0)
 __device__ __forceinline__ float add_bf16_pair(uint32_t w, float l)
 {
@@ -142,32 +150,54 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t w, float l)
 
 // Workgroup id -> logical block.  Workgroups are dealt to the 8 XCDs in turn
 // (id mod 8); this map gives each XCD a contiguous range of logical blocks, so
-// the blocks of one query row (its splits and value halves), which read the
-// same query and the same latent rows, share one L2.
+// the blocks of one query row (its splits), which read the same query, share
+// one L2.
 __device__ __forceinline__ int xcd_block(int id, int n)
 {
     const int q = n >> 3, rem = n & 7, x = id & 7;
     return x * q + min(x, rem) + (id >> 3);
 }
 
-// NW waves per workgroup, wave w owning heads 32w..32w+31 (NW = ceil(H / 32)).
-// One-dimensional grid of rows * splits * VSPLIT workgroups.
-template <int QK, int V, int NW>
-__global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
+// Compile-time choices of one wave's tile loop: its partner index and whether
+// P goes to the MFMAs as a hi/lo pair.
+template <int PX_, bool PREC_>
+struct TileCfg {
+    static constexpr int PX = PX_;
+    static constexpr bool PREC = PREC_;
+};
+
+// 2 * HB waves per workgroup: wave w is partner x = w / HB of head block
+// hb = w % HB.  A workgroup covers the 32 * HB heads of one head group; the
+// one-dimensional grid has rows * splits * head groups workgroups.
+template <int QK, int V, int HB>
+__global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
 {
-    using S = AttnShape<QK, V>;
-    constexpr int KS = S::KS, VW = S::VW;
-    __shared__ __attribute__((aligned(1024))) uint8_t tile[kAttnBuffers][S::TILE_BYTES];
+    using S = AttnShape<QK, V, 2>;
+    constexpr int KP = S::KP, VW = S::VW, NVT = S::NVT;
+    constexpr int NW = 2 * HB, nthreads = 64 * NW;
+    constexpr int NB = kAttnBuffers;
+    static_assert(32 % NW == 0, "tokens per wave");
+    constexpr int TOK_W = 32 / NW;  // tokens each wave copies per tile
+    // The partners' partial S^T pass through the main rows of a spent tile
+    // buffer (the rows the reading wave itself refills next), or through an
+    // array of their own for rows without main rows.
+    constexpr bool XIN = S::MAIN > 0 && TOK_W >= 4;
+    constexpr int XN = XIN ? 1 : NW, XJ = XIN ? 1 : 4, XL = XIN ? 1 : 64;
+    __shared__ __attribute__((aligned(1024))) uint8_t tile[NB][S::TILE_BYTES];
+    __shared__ __attribute__((aligned(16))) f32x4 xchs[XN][XJ][XL];
     __shared__ uint32_t rows[kAttnMaxSplitTokens];
     __shared__ uint32_t vbits[kAttnMaxSplitTokens / 32];
-    __shared__ int last_tile, overflow_flag;
+    __shared__ int first_tile, last_tile, overflow_flag;
 
-    const int per_row = a.splits * S::VSPLIT;
+    // the head groups of one (row, split) are consecutive logical blocks: they
+    // gather the same latent rows, through one L2
+    const int hgroups = (a.num_heads + 32 * HB - 1) / (32 * HB);
     const int lb = xcd_block(blockIdx.x, gridDim.x);
-    const int r = lb / per_row, split = (lb % per_row) / S::VSPLIT, vh = lb % S::VSPLIT;
-    constexpr int nthreads = 64 * NW;
+    const int r = lb / (a.splits * hgroups), split = (lb / hgroups) % a.splits, hg = lb % hgroups;
     const int wave = wave_uniform(threadIdx.x >> 6), lane = threadIdx.x & 63;
     __builtin_assume(wave >= 0 && wave < NW);  // lets copy kinds resolve at compile time
+    const int hb = wave % HB, px = wave / HB;   // head block, partner index
+    const int partner = px == 0 ? wave + HB : wave - HB;
     const int col = lane & 31, half = lane >> 5;
     int seq, limit;
     if (a.decode) {
@@ -184,19 +214,22 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     const int32_t *sel = a.topk_idx + (int64_t)r * a.k + j0;
     const int32_t *tbl = a.block_table + (int64_t)seq * a.max_blocks;
     const int bmask = (1 << a.bs_log2) - 1;
+    // block-uniform: the row keeps few keys, so P goes to the MFMAs as hi + lo
+    const bool precise = min(limit, a.k) < kPreciseBelow;
 
-    const int head = 32 * wave + col;
+    const int head = 32 * (HB * hg + hb) + col;
     const bool hok = head < a.num_heads;
-    // q^T operand of step ks for this lane: q[head][16ks + 8half .. +7]
-    // (issued first: these loads overlap the row look-ups below).  Lanes of
-    // heads past num_heads load the last head instead: their S^T columns feed
-    // only their own, never stored, output columns.
-    bf16x8 qb[KS];
+    // q^T operand of step ks (of this partner's half) for this lane:
+    // q[head][16(KP px + ks) + 8half .. +7] (issued first: these loads overlap
+    // the row look-ups below).  Lanes of heads past num_heads load the last
+    // head instead: their S^T columns feed only their own, never stored, output
+    // columns.
+    bf16x8 qb[KP];
     {
         const int qhead = hok ? head : a.num_heads - 1;
-        const uint16_t *qp = a.q + ((int64_t)r * a.num_heads + qhead) * QK + 8 * half;
+        const uint16_t *qp = a.q + ((int64_t)r * a.num_heads + qhead) * QK + 16 * KP * px + 8 * half;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) qb[ks] = as_bf16x8(load16(qp + 16 * ks));
+        for (int ks = 0; ks < KP; ++ks) qb[ks] = as_bf16x8(load16(qp + 16 * ks));
     }
 
     // Physical row of every kept token of this split (kNoRow = padding) and a
@@ -227,57 +260,74 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         }
     }
     if (threadIdx.x == 0) {
+        first_tile = kAttnMaxSplitTokens;
         last_tile = -1;
         overflow_flag = 0;
     }
-    f32x16 oacc[S::NVT];  // O^T tile vt: columns 32vt.. of this block's value range
+    f32x16 oacc[NVT];  // O^T tile vt: columns 32vt.. of this partner's value range
 #pragma unroll
-    for (int vt = 0; vt < S::NVT; ++vt) oacc[vt] = f32x16{};
-    // m: reference max (log2 units); l: sum of the bf16-rounded weights (output
-    // normaliser); le: sum of the unrounded weights (log-sum-exp)
+    for (int vt = 0; vt < NVT; ++vt) oacc[vt] = f32x16{};
+    // m: reference max (log2 units); l: sum of the weights the MFMAs multiply
+    // (output normaliser); le: sum of the unrounded weights (log-sum-exp)
     float m = -INFINITY, l = 0.0f, le = 0.0f;
     bool ovf = false;
     __syncthreads();
     for (int t = threadIdx.x; t < ntiles; t += nthreads)
-        if (vbits[t]) atomicMax(&last_tile, t);
+        if (vbits[t]) {
+            atomicMax(&last_tile, t);
+            atomicMin(&first_tile, t);
+        }
     __syncthreads();
     const int nt_eff = last_tile + 1;  // tiles after the last valid token are skipped
+    const int t_ref = first_tile;      // the tile that fixes the reference max
 
-    // Copies.  Wave w copies tokens w, w + NW, ... of a tile, TOK_W of them (a
-    // surplus repeats token 31, which writes the same bytes again).  Per token:
-    // a buffer resource over its latent row (a zero row for padding tokens and
-    // for tiles at or past nt_eff), then the main-row copy (64 lanes x 16 bytes)
-    // and the tail copy (lanes 0..7 x 16 bytes), both buffer-form LDS-DMA.  The
-    // memory counter of every wave thus advances by DMA_W per tile.  `myrow` is
-    // the row of token lane % 32 of the tile.
-    constexpr int TOK_W = (32 + NW - 1) / NW;
+    // Copies.  Wave w copies tokens w, w + NW, ... of a tile, TOK_W of them.
+    // Per token: a buffer resource over its latent row (a zero row for padding
+    // tokens and for tiles at or past nt_eff), then the main-row copy (64 lanes
+    // x 16 bytes) and the tail copy (lanes 0..7 x 16 bytes), both buffer-form
+    // LDS-DMA.  The memory counter of every wave thus advances by DMA_W per
+    // tile.
     constexpr int DMA_W = TOK_W * S::COPIES_PER_TOKEN;
     const uint64_t kv_addr = reinterpret_cast<uint64_t>(a.kv);
     uint64_t zero_addr = reinterpret_cast<uint64_t>(kZeroLatentRow);
     asm volatile("" : "+s"(zero_addr));  // keep the address in registers, out of the copy code
-    auto tile_row = [&](int tn) -> uint32_t {
+    // 64-bit address of the latent row of token lane % 32 of tile tn (the zero
+    // row for padding and for tiles at or past nt_eff), computed for all 32
+    // tokens at once; each copy then reads its token's address from a lane.
+    auto tile_base = [&](int tn) -> uint64_t {
         const uint32_t v = rows[max(0, min(tn, kAttnMaxSplitTokens / 32 - 1)) * 32 + (lane & 31)];
-        return tn >= 0 && tn < nt_eff ? v : kNoRow;
+        const uint32_t row = tn >= 0 && tn < nt_eff ? v : kNoRow;
+        return row != kNoRow ? kv_addr + (uint64_t)row * (QK * 2) : zero_addr;
     };
-    // `dstb`: the LDS base of the buffer, from opaque_lds (the tile reads that
-    // follow use other buffers, and the ring waits order the rest)
-    auto copy_token = [&](uint32_t myrow, int n, SA_LDS uint8_t *dstb) {
-        const int ii = min(wave + NW * n, 31);  // wave-uniform
-        const uint32_t row = lane_read(myrow, ii);
-        // (a mask blend rather than a conditional, so no branch splits the q.k steps)
-        const uint64_t keep = (uint64_t)0 - (uint64_t)(row != kNoRow);
-        const uint64_t base = ((kv_addr + (uint64_t)row * (QK * 2)) & keep) | (zero_addr & ~keep);
+    auto buffer_base = [&](int buf) { return (SA_LDS uint8_t *)opaque_lds((SA_LDS uint8_t *)&tile[buf][0]); };
+    auto copy_token = [&](uint64_t mybase, int n, SA_LDS uint8_t *dstb) {
+        const int ii = wave + NW * n;  // wave-uniform
+        const uint64_t base = ((uint64_t)lane_read((uint32_t)(mybase >> 32), ii) << 32) | lane_read((uint32_t)mybase, ii);
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const void *>(base), QK * 2);
         if constexpr (S::MAIN > 0)  // lane i fetches the piece stored at position i
             buf_dma16_to_lds(rs, (lane * 16) ^ (16 * main_swizzle(ii)), dstb + ii * S::MAIN_STRIDE);
         if (lane < 8) buf_dma16_to_lds(rs, S::MAIN * 16 + lane * 16, dstb + S::TAIL_BASE + ii * S::TAIL_STRIDE);
     };
-    auto buffer_base = [&](int buf) { return (SA_LDS uint8_t *)opaque_lds((SA_LDS uint8_t *)&tile[buf][0]); };
     auto issue_tile = [&](int tn, int buf) {
-        const uint32_t myrow = tile_row(tn);
+        const uint64_t mybase = tile_base(tn);
         SA_LDS uint8_t *dstb = buffer_base(buf);
 #pragma unroll
-        for (int n = 0; n < TOK_W; ++n) copy_token(myrow, n, dstb);
+        for (int n = 0; n < TOK_W; ++n) copy_token(mybase, n, dstb);
+    };
+
+    // Exchange slot j (of 4, 16 bytes per lane) of the partial that wave `reader`
+    // reads, for a tile whose partials pass through buffer buf: with XIN, the
+    // main row of the reader's own token reader + NW j, which the reader's next
+    // copy into that buffer overwrites only after it has read the slot.
+    auto xslot = [&](int buf, int reader, int j) -> SA_LDS f32x4 * {
+        if constexpr (XIN)
+            return (SA_LDS f32x4 *)((SA_LDS uint8_t *)&tile[buf][0] + (reader + NW * j) * S::MAIN_STRIDE) + lane;
+        else
+            return (SA_LDS f32x4 *)&xchs[reader][j][lane];
+    };
+    auto xch_write = [&](int buf, const f32x16 &s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) *xslot(buf, partner, j) = f32x4{s[4 * j], s[4 * j + 1], s[4 * j + 2], s[4 * j + 3]};
     };
 
     // LDS byte offset of this lane's K operand of step ks (S row c holds token
@@ -290,128 +340,111 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
                    ? tok * S::MAIN_STRIDE + ((32 * (ks & 7) + 16 * hf) ^ (16 * main_swizzle(tok))) + 256 * (ks >> 3)
                    : S::TAIL_BASE + tok * S::TAIL_STRIDE + 16 * (2 * ks - S::MAIN + hf);
     };
-
-    // Per tile: S^T = K Q^T (qk), the softmax weights of S^T (softmax), then
-    // O^T += V^T P^T (pv).  The loop below is software-pipelined across tiles:
-    // iteration t computes S^T of tile t+1 while the weights of tile t are
-    // formed (VALU beside the MFMAs), then multiplies tile t's values.  The
-    // schedule is pinned so that LDS operand reads run ahead of the MFMAs that
-    // use them: K operands KPF steps ahead, V operands VPF steps ahead.
     constexpr int KPF = SA_ATTN_KPF, VPF = SA_ATTN_VPF;
-    auto lane_id = [&]() {
-        // The lane id is made opaque per tile so that the lane-dependent values
-        // derived from it are recomputed (a few ALU ops) instead of being hoisted
-        // out of the tile loop, where they would compete with the accumulators.
-        int ln = lane;
-        asm volatile("" : "+v"(ln));
-        return ln;
-    };
-    // S^T of the tile in buffer buf; with_copies: the main copies of the tile
-    // whose lane rows are `myrow` go into buffer nbuf between the q.k steps, and
-    // after each MFMA a few VALU slots are left for independent work (the
-    // previous tile's softmax)
-    auto qk = [&](int buf, uint32_t myrow, int nbuf, auto with_copies, auto &&fill) -> f32x16 {
+    auto lane_id = [&]() { return lane; };
+    // This partner's S^T of the tile in buffer buf (steps KP px .. KP px + KP - 1);
+    // after MFMA step ks, fill(ks) places independent work (the previous tile's
+    // softmax, the next tile's copies) in the MFMA's shadow.
+    auto qk_half = [&](auto cfg, int buf, auto &&fill) -> f32x16 {
         const int ln = lane_id(), c = ln & 31, hf = ln >> 5;
         const uint8_t *tb = tile[buf];
-        SA_LDS uint8_t *dstb = nullptr;
-        if constexpr (decltype(with_copies)::value) dstb = buffer_base(nbuf);
-        bf16x8 kr[KS];
+        constexpr int ks0 = KP * decltype(cfg)::PX;
+        bf16x8 kr[KP];
 #pragma unroll
-        for (int u = 0; u < KPF && u < KS; ++u)
-            kr[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, u)));
+        for (int u = 0; u < KPF && u < KP; ++u)
+            kr[u] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, ks0 + u)));
         f32x16 s = f32x16{};
-        // Step ks: read the operand of step ks + KPF, multiply, issue this
-        // step's copies, then the caller's VALU work.
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            if (ks + KPF < KS)
-                kr[ks + KPF] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, ks + KPF)));
+        for (int ks = 0; ks < KP; ++ks) {
+            if (ks + KPF < KP)
+                kr[ks + KPF] = as_bf16x8(*reinterpret_cast<const u32x4 *>(tb + k_offset(c, hf, ks0 + ks + KPF)));
             s = mfma_32x32x16(kr[ks], qb[ks], s);
-            if constexpr (decltype(with_copies)::value) {
-                // tokens n with n * KS / TOK_W == ks
-                const int n_lo = (ks * TOK_W + KS - 1) / KS, n_hi = ((ks + 1) * TOK_W + KS - 1) / KS;
-#pragma unroll
-                for (int n = n_lo; n < n_hi; ++n) copy_token(myrow, n, dstb);
-            }
             fill(ks);
-#if SA_ATTN_FENCE
-            __builtin_amdgcn_sched_barrier(0);
-#endif
+            __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads KPF steps ahead, no further
         }
         return s;
     };
     auto no_fill = [](int) {};
-    // Weights of tile t from its S^T (branch-free).  Register i of half hf holds
-    // token 16(i/8) + 8hf + i%8.  The reference max is fixed by the first tile
-    // with a valid token for this head (until then O and l are 0, so nothing
-    // needs rescaling) and never moves afterwards: the output accumulators are
-    // only ever touched by the MFMAs.  Weights are exp2(min(s - m, 64)), finite
-    // in fp32 and bf16; a head whose logits outgrow its reference by more than
-    // 64 raises `ovf`, and the split is then recomputed exactly with its true
-    // max (below).
-    // The weights in kSmSteps small steps, so that the steps can sit between the
-    // next tile's q.k MFMAs: steps 0-3 mask, 4-7 reduce the max, 8 crosses the
-    // half-waves and sets the reference, 9-24 exponentiate, 25-32 round to bf16
-    // and sum.  State lives in `SmState`.
+    // Weights of a tile from its S^T in kSmSteps small steps, so that they can
+    // sit between the next tile's q.k MFMAs: steps 0-1 mask and reduce the max,
+    // 2 crosses the half-waves and sets the reference, 3-10 exponentiate, round
+    // and sum pair j = step - 3.  Register i of half hf holds token
+    // 16(i/8) + 8hf + i%8.  The reference max is fixed by the first tile with a
+    // valid token for this head (until then O and l are 0, so nothing needs
+    // rescaling) and never moves afterwards: the output accumulators are only
+    // ever touched by the MFMAs.  Weights are exp2(min(s - m, 64)), finite in
+    // fp32 and bf16; a head whose logits outgrow its reference by more than 64
+    // raises `ovf`, and the split is then recomputed exactly with its true max
+    // (below).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and wl[k2],
+    // the bf16 residues, for `precise` rows).
     struct SmState {
         f32x16 s;
         float tmax, mref;
-        float p[16];
-        u32x4 w[2];
         uint32_t vb;
+        bool full, set_ref;  // (workgroup-uniform) every token valid; the tile fixes the reference
+        u32x4 w[2], wl[2];
     };
-    constexpr int kSmSteps = 33;
-    auto sm_begin = [&](SmState &st, const f32x16 &s_in, int t) {
-        st.s = s_in;
-        st.vb = vbits[t] >> (8 * half);
+    constexpr int kSmSteps = 11;
+    auto sm_begin = [&](SmState &st, int t, bool set_ref) {
+        const uint32_t bits = vbits[t];
+        st.full = __builtin_amdgcn_readfirstlane(bits) == 0xFFFFFFFFu;
+        st.set_ref = set_ref;
+        st.vb = bits >> (8 * half);
     };
-    auto sm_step = [&](SmState &st, int step) {
-        if (step < 4) {
+    auto valid_bit = [&](uint32_t vb, int i) { return ((vb >> (16 * (i >> 3) + (i & 7))) & 1u) != 0; };
+    // Padding tokens have zero latent rows, so their logits are 0: the max
+    // that checks for overflow may include them (at worst a needless exact
+    // recompute when every valid logit lies far below 0), the reference max
+    // and the weights may not.
+    auto sm_step = [&](auto cfg, SmState &st, int step) {
+        if (step < 2) {
+            float mx = step == 0 ? -INFINITY : st.tmax;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int i = 4 * step + e;
-                st.s[i] = ((st.vb >> (16 * (i >> 3) + (i & 7))) & 1u) ? st.s[i] : -INFINITY;
-            }
-        } else if (step < 8) {
-            const int i0 = 4 * (step - 4);
-            const float mx = fmaxf(fmaxf(st.s[i0], st.s[i0 + 1]), fmaxf(st.s[i0 + 2], st.s[i0 + 3]));
-            st.tmax = step == 4 ? mx : fmaxf(st.tmax, mx);
-        } else if (step == 8) {
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, st.s[8 * step + e]);
+            st.tmax = mx;
+        } else if (step == 2) {
             // max over the two half-waves (they hold the other 16 tokens)
-            const uint32_t u = __float_as_uint(st.tmax);
-            const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-            const float tmax = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) * a.scale_log2;
-            m = m == -INFINITY ? tmax : m;
-            ovf |= tmax > m + 64.0f;
-            st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every s is -inf
-        } else if (step < 25) {
-            const int i = step - 9;
-            st.p[i] = exp2_hw(fminf(fmaf(st.s[i], a.scale_log2, -st.mref), 64.0f));
+            auto halves_max = [](float x) {
+                const uint32_t u = __float_as_uint(x);
+                const auto rr = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+                return fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]));
+            };
+            if (st.set_ref) {
+                float mv = -INFINITY;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) mv = fmaxf(mv, valid_bit(st.vb, i) ? st.s[i] : -INFINITY);
+                m = halves_max(mv) * a.scale_log2;
+            }
+            ovf |= m != -INFINITY && halves_max(st.tmax) * a.scale_log2 > m + 64.0f;
+            st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every weight is 0
         } else if (step < kSmSteps) {
-            const int j = step - 25, k2 = j >> 2, jj = j & 3;
-            const uint32_t w = pack_bf16x2(st.p[2 * j], st.p[2 * j + 1]);
-            st.w[k2][jj] = w;
-            // the normaliser sums the same bf16-rounded weights the MFMA
-            // multiplies V by, so the output is an exact weighted mean of the
-            // kept rows up to fp32 accumulation
-            l = add_bf16_pair(w, l);
-            le += st.p[2 * j] + st.p[2 * j + 1];
+            const int j = step - 3;
+            float e[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) e[h] = exp2_hw(fminf(fmaf(st.s[2 * j + h], a.scale_log2, -st.mref), 64.0f));
+            uint32_t hi = pack_bf16x2(e[0], e[1]);
+            uint32_t keep = 0xFFFFFFFFu;
+            if (!st.full) {
+                keep = (valid_bit(st.vb, 2 * j) ? 0x0000FFFFu : 0u) | (valid_bit(st.vb, 2 * j + 1) ? 0xFFFF0000u : 0u);
+                e[0] = valid_bit(st.vb, 2 * j) ? e[0] : 0.0f;
+                e[1] = valid_bit(st.vb, 2 * j + 1) ? e[1] : 0.0f;
+                hi &= keep;
+            }
+            st.w[j >> 2][j & 3] = hi;
+            le += e[0] + e[1];
+            if constexpr (decltype(cfg)::PREC) {
+                const uint32_t lo = pack_bf16x2(e[0] - bf16_lo_to_f32(hi), e[1] - bf16_hi_to_f32(hi)) & keep;
+                st.wl[j >> 2][j & 3] = lo;
+                l = add_bf16_pair(lo, l);
+            }
+            // the normaliser sums the same rounded weights the MFMA multiplies V
+            // by, so the output is an exact weighted mean of the kept rows up to
+            // fp32 accumulation
+            l = add_bf16_pair(hi, l);
         }
     };
-    auto sm_finish = [&](SmState &st, bf16x8 *pb) {
-        pb[0] = as_bf16x8(st.w[0]);
-        pb[1] = as_bf16x8(st.w[1]);
-    };
-    // the whole softmax of one tile, unpipelined
-    auto softmax = [&](const f32x16 &s_in, int t, bf16x8 *pb) {
-        SmState st;
-        sm_begin(st, s_in, t);
-#pragma unroll
-        for (int step = 0; step < kSmSteps; ++step) sm_step(st, step);
-        sm_finish(st, pb);
-    };
     // O^T += V^T P^T over the tile's two 16-token halves: step q = (k2, vt)
-    // multiplies output tile vt (value columns 32vt..32vt+31 of this block's
+    // multiplies output tile vt (value columns 32vt..32vt+31 of this partner's
     // range) by token half k2.  The V^T operand of lane (c, hf) is column c of
     // tokens 16k2 + 8hf + 0..7, read as two transposed 4-token reads
     // (ds_read_b64_tr_b16: within each 16 lanes, lane 4a + b receives element b
@@ -419,7 +452,8 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
     // L addresses token 16k2 + 8hf + 4s + ((L >> 2) & 3), columns 32vt + 16((L >> 4)
     // & 1) + 4(L & 3)..+3.  The operands of step q + VPF are read while step q
     // multiplies.
-    auto pv = [&](int buf, const bf16x8 *pb) {
+    auto pv = [&](auto cfg, int buf, const SmState &st) {
+        constexpr int PX = decltype(cfg)::PX;
         const int ln = lane_id();
         const int j = (ln >> 2) & 3, a4 = ln & 3, g1 = (ln >> 4) & 1, hfv = ln >> 5;
         const int xq = 2 * g1 + (a4 >> 1);  // piece within the 32-column tile
@@ -427,9 +461,9 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         // lane-constant part of the address, and the step part XORed into it
         int lb;
         if constexpr (S::MAIN > 0)
-            lb = (8 * hfv + j) * S::MAIN_STRIDE + 8 * (a4 & 1) + 64 * j + 16 * (xq ^ (2 * hfv)) + 16 * (vh * VW / 8);
+            lb = (8 * hfv + j) * S::MAIN_STRIDE + 8 * (a4 & 1) + 64 * j + 16 * (xq ^ (2 * hfv)) + 16 * (PX * VW / 8);
         else
-            lb = S::TAIL_BASE + (8 * hfv + j) * S::TAIL_STRIDE + 8 * (a4 & 1) + 16 * xq + 16 * (vh * VW / 8);
+            lb = S::TAIL_BASE + (8 * hfv + j) * S::TAIL_STRIDE + 8 * (a4 & 1) + 16 * xq + 16 * (PX * VW / 8);
         auto vaddr = [&](int k2, int sh, int vt) -> int {
             if constexpr (S::MAIN > 0)
                 return (lb ^ (64 * (vt & 3) + 16 * sh)) + (16 * k2 + 4 * sh) * S::MAIN_STRIDE + 256 * (vt >> 2);
@@ -438,112 +472,157 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
         };
         typedef short s16x4 __attribute__((ext_vector_type(4)));
         auto vread = [&](int q) -> bf16x8 {
-            const int k2 = q / S::NVT, vt = q % S::NVT;
+            const int k2 = q / NVT, vt = q % NVT;
             const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS s16x4 *)(tb + vaddr(k2, 0, vt)));
             const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((SA_LDS s16x4 *)(tb + vaddr(k2, 1, vt)));
             return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         };
-        constexpr int NQ = 2 * S::NVT;
+        constexpr int NQ = 2 * NVT;
         bf16x8 vd[NQ];
 #pragma unroll
         for (int q = 0; q < VPF && q < NQ; ++q) vd[q] = vread(q);
 #pragma unroll
         for (int q = 0; q < NQ; ++q) {
             if (q + VPF < NQ) vd[q + VPF] = vread(q + VPF);
-            const int k2 = q / S::NVT, vt = q % S::NVT;
-            oacc[vt] = mfma_32x32x16(vd[q], pb[k2], oacc[vt]);
-#if SA_ATTN_FENCE
-            __builtin_amdgcn_sched_barrier(0);
-#endif
+            const int k2 = q / NVT, vt = q % NVT;
+            oacc[vt] = mfma_32x32x16(vd[q], as_bf16x8(st.w[k2]), oacc[vt]);
+            if constexpr (decltype(cfg)::PREC) oacc[vt] = mfma_32x32x16(vd[q], as_bf16x8(st.wl[k2]), oacc[vt]);
+            __builtin_amdgcn_sched_barrier(0);  // keeps the operand reads VPF steps ahead, no further
         }
     };
 
-    // Ring of kAttnBuffers = 4 tile buffers, two tiles resident (t for its values,
-    // t+1 for its q.k) and two in flight.  The prologue issues tiles 0..2;
-    // iteration t (which computes S^T of tile t+1) issues tile t+3 into the buffer
-    // of tile t-1 (zeros past nt_eff).  Copies complete in order and every wave
-    // issues DMA_W per tile, so waiting for tile t+1 with only tile t+2 younger is
-    // "at most DMA_W copies in flight" (before the loop: tile 0, two younger).
-    // The barrier then makes every wave's share of tile t+1 visible and certifies
-    // that every wave is done with tile t-1's buffer.  Tiles of padding only are
-    // not computed (block-uniform).
-    static_assert(kAttnBuffers == 4, "the ring below holds two resident and two in-flight tiles");
-    constexpr int W2 = 2 * DMA_W < 63 ? 2 * DMA_W : 63;  // clamped: waiting for more is safe
-    constexpr int W1 = DMA_W < 63 ? DMA_W : 63;
-#pragma unroll
-    for (int j = 0; j < kAttnBuffers - 1; ++j) issue_tile(j, j);
-    f32x16 s_cur = f32x16{};
-    if (nt_eff > 0) {
-        attn_wait_vmcnt<W2>();
-        barrier_no_fence();
-        s_cur = qk(0, kNoRow, 0, std::false_type{}, no_fill);
-    }
-    for (int t = 0; t < nt_eff; ++t) {
-        bf16x8 pb[2];
-        f32x16 s_nxt = f32x16{};
-        if (t + 1 < nt_eff) {  // (block-uniform)
-            const uint32_t myrow = tile_row(t + 3);
+    // Ring of NB = 4 tile buffers.  The prologue issues tiles 0, 1 and 2 and
+    // computes this wave's partial S^T of tile 0.  Iteration t:
+    //   barrier A: every wave is done with tile t-1 (its buffer now holds the
+    //     partials of tile t for their readers), and tile t+1 has landed;
+    //   read the partner's partial of tile t;
+    //   partial S^T of tile t+1, with, between its MFMAs, the sum of tile t's
+    //     partials, tile t's weights, and the copies of tile t+3 into the
+    //     buffer of tile t-1 (each wave refills only rows it has just read);
+    //   O += V P of tile t;
+    //   wait for this wave's copies of tile t+2 (only tile t+3's are younger:
+    //     every wave issues DMA_W per tile, and copies complete in order);
+    //   barrier B: every wave is done with tile t, whose buffer then takes the
+    //     partials of tile t+1.
+    // Tiles of padding only are not computed (block-uniform); the last
+    // iteration computes the (unused) partial of an all-padding tile.
+    auto tiles = [&](auto cfg) {
+        static_assert(NB == 4, "the ring below holds two read tiles and two in flight");
+        constexpr int W1 = DMA_W < 63 ? DMA_W : 63;
+        constexpr int W2 = 2 * DMA_W < 63 ? 2 * DMA_W : 63;
+        issue_tile(0, 0);
+        issue_tile(1, 1);
+        issue_tile(2, 2);
+        f32x16 sp = f32x16{};
+        if (nt_eff > 0) {
+            attn_wait_vmcnt<W2>();
+            barrier_lds();
+            sp = qk_half(cfg, 0, no_fill);
+            xch_write(NB - 1, sp);
             attn_wait_vmcnt<W1>();
-            barrier_no_fence();
+        }
+        for (int t = 0; t < nt_eff; ++t) {
+            barrier_lds();  // A
+            const int xb = (t + NB - 1) % NB;
+            f32x4 pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) pr[j] = *xslot(xb, wave, j);
             SmState st;
-            sm_begin(st, s_cur, t);
-            // step ks of tile t's softmax after q.k step ks of tile t+1
-            s_nxt = qk((t + 1) % kAttnBuffers, myrow, (t + 3) % kAttnBuffers, std::true_type{},
-                       [&](int ks) { sm_step(st, ks); });
+            sm_begin(st, t, t == t_ref);
+            const uint64_t nbase = tile_base(t + 3);
+            SA_LDS uint8_t *dstb = buffer_base(xb);
+            constexpr int kAdd = KP > 2 ? 2 : 0;  // q.k step after which the partials are summed
+            f32x16 sn = qk_half(cfg, (t + 1) % NB, [&](int ks) {
+                if (ks == kAdd) {
+                    // S^T of tile t: partner 0's partial first, in both partners
 #pragma unroll
-            for (int step = KS; step < kSmSteps; ++step) sm_step(st, step);
-            sm_finish(st, pb);
-        } else {
-            softmax(s_cur, t, pb);
+                    for (int i = 0; i < 16; ++i)
+                        st.s[i] = decltype(cfg)::PX == 0 ? sp[i] + pr[i >> 2][i & 3] : pr[i >> 2][i & 3] + sp[i];
+                }
+                // the copies of tile t+3, after the partials have been read
+                if (ks > kAdd && ks - kAdd - 1 < TOK_W) copy_token(nbase, ks - kAdd - 1, dstb);
+                if (ks > kAdd && ks - kAdd - 1 < kSmSteps) sm_step(cfg, st, ks - kAdd - 1);
+            });
+            // (q.k steps too few to hold every copy or softmax step: the rest here)
+#pragma unroll
+            for (int n = KP - kAdd - 1; n < TOK_W; ++n) copy_token(nbase, n, dstb);
+#pragma unroll
+            for (int step = KP - kAdd - 1; step < kSmSteps; ++step) sm_step(cfg, st, step);
+            pv(cfg, t % NB, st);
+            sp = sn;
+            attn_wait_vmcnt<W1>();
+            barrier_lds();  // B
+            xch_write(t % NB, sp);
         }
-        pv(t % kAttnBuffers, pb);
-        s_cur = s_nxt;
-    }
-    attn_wait_vmcnt<0>();  // the last (zero) copies have landed
+        attn_wait_vmcnt<0>();  // the last (zero) copies have landed
 
-    // Exact recompute of the split when some head's logits outgrew its reference
-    // max by more than 64 (never for logits within a few dozen of each other):
-    // pass 1 finds every head's true max, pass 2 redoes the weighted sum with it.
-    if (ovf) overflow_flag = 1;
-    __syncthreads();
-    if (overflow_flag) {
-        float mt = -INFINITY;
-        for (int t = 0; t < nt_eff; ++t) {
-            issue_tile(t, 0);
-            attn_wait_vmcnt<0>();
-            __syncthreads();
-            const f32x16 s0 = qk(0, kNoRow, 0, std::false_type{}, no_fill);
-            const uint32_t vb = vbits[t] >> (8 * half);
+        // Exact recompute of the split when some head's logits outgrew its reference
+        // max by more than 64 (never for logits within a few dozen of each other):
+        // pass 1 finds every head's true max, pass 2 redoes the weighted sum with it.
+        if (ovf) overflow_flag = 1;
+        __syncthreads();
+        if (overflow_flag) {
+            // S^T of tile t (both partners), through buffer 0 and the exchange
+            // slots of buffer 1
+            auto full_s = [&](int t) -> f32x16 {
+                issue_tile(t, 0);
+                attn_wait_vmcnt<0>();
+                __syncthreads();
+                const f32x16 mine = qk_half(cfg, 0, no_fill);
+                xch_write(1, mine);
+                __syncthreads();
+                f32x16 s;
 #pragma unroll
-            for (int i = 0; i < 16; ++i)
-                if ((vb >> (16 * (i >> 3) + (i & 7))) & 1u) mt = fmaxf(mt, s0[i] * a.scale_log2);
-            __syncthreads();
-        }
-        mt = fmaxf(mt, __shfl_xor(mt, 32));
-        m = mt;
-        l = 0.0f;
-        le = 0.0f;
+                for (int j = 0; j < 4; ++j) {
+                    const f32x4 o = *xslot(1, wave, j);
 #pragma unroll
-        for (int vt = 0; vt < S::NVT; ++vt) oacc[vt] = f32x16{};
-        for (int t = 0; t < nt_eff; ++t) {
-            issue_tile(t, 0);
-            attn_wait_vmcnt<0>();
-            __syncthreads();
-            bf16x8 pb[2];
-            softmax(qk(0, kNoRow, 0, std::false_type{}, no_fill), t, pb);  // s <= m now, so no weight is clamped
-            pv(0, pb);
-            __syncthreads();
+                    for (int e = 0; e < 4; ++e)
+                        s[4 * j + e] = decltype(cfg)::PX == 0 ? mine[4 * j + e] + o[e] : o[e] + mine[4 * j + e];
+                }
+                __syncthreads();
+                return s;
+            };
+            float mt = -INFINITY;
+            for (int t = 0; t < nt_eff; ++t) {
+                const f32x16 s0 = full_s(t);
+                const uint32_t vb = vbits[t] >> (8 * half);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    if (valid_bit(vb, i)) mt = fmaxf(mt, s0[i] * a.scale_log2);
+            }
+            mt = fmaxf(mt, __shfl_xor(mt, 32));
+            m = mt;
+            l = 0.0f;
+            le = 0.0f;
+#pragma unroll
+            for (int vt = 0; vt < NVT; ++vt) oacc[vt] = f32x16{};
+            for (int t = 0; t < nt_eff; ++t) {
+                SmState st;
+                st.s = full_s(t);
+                sm_begin(st, t, false);
+#pragma unroll
+                for (int step = 0; step < kSmSteps; ++step) sm_step(cfg, st, step);  // s <= m now: no clamping
+                pv(cfg, 0, st);
+                __syncthreads();
+            }
         }
-    }
+    };
+    auto run = [&](auto pxc) {
+        if (precise) tiles(TileCfg<decltype(pxc)::value, true>{});
+        else tiles(TileCfg<decltype(pxc)::value, false>{});
+    };
+    if (px == 0) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
 
+    // both partners hold the same normaliser and weight sums (the same S^T)
     const float lt = l + __shfl_xor(l, 32);
     const float lte = le + __shfl_xor(le, 32);
     if (!hok) return;
     if (a.splits == 1) {
         const float inv = lt > 0.0f ? 1.0f / lt : 0.0f;
-        const int64_t obase = ((int64_t)r * a.num_heads + head) * V + vh * VW;
+        const int64_t obase = ((int64_t)r * a.num_heads + head) * V + px * VW;
 #pragma unroll
-        for (int vt = 0; vt < S::NVT; ++vt)
+        for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
             for (int i = 0; i < 16; i += 4) {
                 const int v = 32 * vt + acc_row(i, half);  // registers i..i+3: columns v..v+3
@@ -554,18 +633,18 @@ __global__ __launch_bounds__(64 * NW, 1) void attend_kernel(const AttnArgs a)
                 else
                     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(a.out) + obase + v) = o;
             }
-        if (a.lse && half == 0 && vh == 0)
+        if (a.lse && half == 0 && px == 0)
             a.lse[(int64_t)r * a.num_heads + head] = lt > 0.0f ? (m + log2f(lte)) * 0.69314718055994531f : -INFINITY;
     } else {
         const int64_t pbase = (((int64_t)r * a.splits + split) * a.num_heads + head);
-        float *po = a.part_o + pbase * V + vh * VW;
+        float *po = a.part_o + pbase * V + px * VW;
 #pragma unroll
-        for (int vt = 0; vt < S::NVT; ++vt)
+        for (int vt = 0; vt < NVT; ++vt)
 #pragma unroll
             for (int i = 0; i < 16; i += 4)
                 *reinterpret_cast<f32x4 *>(po + 32 * vt + acc_row(i, half)) =
                     f32x4{oacc[vt][i], oacc[vt][i + 1], oacc[vt][i + 2], oacc[vt][i + 3]};
-        if (half == 0 && vh == 0) *reinterpret_cast<f32x4 *>(a.part_ml + pbase * 4) = f32x4{m, lt, lte, 0.0f};
+        if (half == 0 && px == 0) *reinterpret_cast<f32x4 *>(a.part_ml + pbase * 4) = f32x4{m, lt, lte, 0.0f};
     }
 }
 

@@ -102,6 +102,11 @@ __device__ __forceinline__ void buf_dma16_to_lds_stream(__amdgpu_buffer_rsrc_t r
 // moving memory operations across it.
 __device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
 
+// The same barrier after this wave's LDS reads and writes have completed
+// (lgkmcnt(0)): LDS data written before it is visible to every wave after it.
+// LDS-DMA copies are counted by vmcnt and waited for separately.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // An LDS address the compiler cannot trace to a __shared__ array: a copy into it
 // carries no alias scope, so the compiler adds no wait for that copy before
 // later reads of other buffers of the same array (ordering is then the

@@ -60,7 +60,7 @@ sa_status check_params(const sa_params *p)
 {
     if (!p) return SA_ERR_NULL;
     if (p->num_heads < 1 || p->qk_dim < 1 || p->v_dim < 1 || p->v_dim > p->qk_dim || p->idx_heads < 1 ||
-        p->idx_dim < 1 || p->block_size < 1 || p->topk < 1 || !std::isfinite(p->softmax_scale) ||
+        p->idx_dim < 1 || p->block_size < 1 || p->topk < 1 || !std::isfinite(p->softmax_scale) || !(p->softmax_scale > 0.0f) ||
         (p->idx_relu != 0 && p->idx_relu != 1) || (p->out_dtype != SA_OUT_F32 && p->out_dtype != SA_OUT_BF16))
         return SA_ERR_SHAPE;
     const bool attn_family = (p->qk_dim == 576 && p->v_dim == 512) || (p->qk_dim == 64 && p->v_dim == 64);
@@ -81,6 +81,26 @@ sa_status check_cache(const sa_params *p, const sa_paged_cache *c, bool need_kv,
     return SA_OK;
 }
 
+// Attention launch shape: blocks of 32 heads (hb per workgroup), partners per
+// block (waves that split the q.k contraction and the value columns) and head
+// groups (workgroups per (row, split)).  The 576/512 family runs 64 heads per
+// workgroup in 8 waves (4 partners), so a wave holds a quarter of its heads'
+// query and of their outputs; the 64/64 family runs up to 128 heads with 2
+// partners.  A block count of 3 runs as 4, with the last block's heads masked.
+struct AttnLaunch {
+    int hb, partners, waves, groups;
+};
+
+AttnLaunch attn_launch(const sa_params *p)
+{
+    AttnLaunch L{};
+    L.hb = p->qk_dim == 576 ? (p->num_heads <= 32 ? 1 : 2) : (p->num_heads <= 32 ? 1 : p->num_heads <= 64 ? 2 : 4);
+    L.partners = 2;
+    L.waves = L.hb * L.partners;
+    L.groups = (p->num_heads + 32 * L.hb - 1) / (32 * L.hb);
+    return L;
+}
+
 // ------------------------------------------------------------------ plans --
 struct DecodePlan {
     int64_t score_stride, mm_stride;  // floats per score row; tiles per min/max row
@@ -96,9 +116,9 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_spli
     DecodePlan d{};
     d.score_stride = round_up(max_ctx > 0 ? max_ctx : 1, 64);
     const int k = p->topk;
-    const int vsplit = p->v_dim > 256 ? 2 : 1;  // value halves per (row, split), as in the attention kernel
+    const int groups = attn_launch(p).groups;  // attention workgroups per (row, split)
     int splits = want_splits > 0 ? want_splits
-                                 : std::max(1, std::min(kMaxDefaultSplits, kTargetAttnBlocks / (batch * vsplit)));
+                                 : std::max(1, std::min(kMaxDefaultSplits, kTargetAttnBlocks / (batch * groups)));
     splits = std::max(1, std::min(splits, (k + 31) / 32));
     splits = std::max(splits, (k + kAttnMaxSplitTokens - 1) / kAttnMaxSplitTokens);
     int tps = (int)round_up((k + splits - 1) / splits, 32);
@@ -396,20 +416,15 @@ void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *id
 
 void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st, StageMarks *mk)
 {
-    // waves of 32 heads; the 576-wide family runs 2 or 4 waves (a 1- or 3-wave
-    // build would need more registers than the pipelined tile loop can spare),
-    // waves past num_heads mask their heads
-    int nw = (p->num_heads + 31) / 32;
-    if (p->qk_dim == 576) nw = nw <= 2 ? 2 : 4;
-    dim3 grid(a.splits * (p->v_dim > 256 ? 2 : 1) * rows), block(64 * nw);
+    const AttnLaunch L = attn_launch(p);
+    dim3 grid(a.splits * rows * L.groups), block(64 * L.waves);
     if (p->qk_dim == 576) {
-        if (nw == 2) hipLaunchKernelGGL((attend_kernel<576, 512, 2>), grid, block, 0, st, a);
-        else hipLaunchKernelGGL((attend_kernel<576, 512, 4>), grid, block, 0, st, a);
+        if (L.hb == 1) hipLaunchKernelGGL((attend_kernel<576, 512, 1>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attend_kernel<576, 512, 2>), grid, block, 0, st, a);
     } else {
-        switch (nw) {
+        switch (L.hb) {
         case 1: hipLaunchKernelGGL((attend_kernel<64, 64, 1>), grid, block, 0, st, a); break;
         case 2: hipLaunchKernelGGL((attend_kernel<64, 64, 2>), grid, block, 0, st, a); break;
-        case 3: hipLaunchKernelGGL((attend_kernel<64, 64, 3>), grid, block, 0, st, a); break;
         default: hipLaunchKernelGGL((attend_kernel<64, 64, 4>), grid, block, 0, st, a); break;
         }
     }

@@ -193,9 +193,18 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def _workspace(nbytes: int, device):
+def _on(stream):
+    """Allocation context of a call: the caller's stream when one is given, so
+    that the caching allocator ties the call's temporaries (workspace and
+    default outputs) to the stream the kernels run on."""
+    import contextlib
+    return _torch().cuda.stream(stream) if stream is not None else contextlib.nullcontext()
+
+
+def _workspace(nbytes: int, device, stream=None):
     torch = _torch()
-    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    with _on(stream):
+        return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
 def decode_workspace_size(p: Params, batch: int, max_ctx: int) -> int:
@@ -212,12 +221,19 @@ def prefill_workspace_size(p: Params, num_rows: int, q_start: int) -> int:
     return n.value
 
 
-def _outputs(p: Params, rows: int, device, want_lse: bool):
+def _index_out(rows: int, k: int, device, stream=None):
     torch = _torch()
-    topk_idx = torch.empty((rows, p.topk), dtype=torch.int32, device=device)
-    out = torch.empty((rows, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
-                      device=device)
-    lse = torch.empty((rows, p.num_heads), dtype=torch.float32, device=device) if want_lse else None
+    with _on(stream):
+        return torch.empty((rows, k), dtype=torch.int32, device=device)
+
+
+def _outputs(p: Params, rows: int, device, want_lse: bool, stream=None):
+    torch = _torch()
+    with _on(stream):
+        topk_idx = torch.empty((rows, p.topk), dtype=torch.int32, device=device)
+        out = torch.empty((rows, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
+                          device=device)
+        lse = torch.empty((rows, p.num_heads), dtype=torch.float32, device=device) if want_lse else None
     return topk_idx, out, lse
 
 
@@ -230,8 +246,8 @@ def sparse_attn_decode(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device, stream)
     _check(lib().sparse_attn_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
                                     idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
                                     _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode")
@@ -251,8 +267,8 @@ def sparse_attn_decode_append(p: Params, cache: PagedCache, max_ctx: int, new_kv
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
     _dev(new_kv, "new_kv", _bf16_types(), (B, p.qk_dim))
     _dev(new_idx_k, "new_idx_k", _bf16_types(), (B, p.idx_dim))
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device, stream)
     _check(lib().sparse_attn_decode_append(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
                                            new_kv.data_ptr(), new_idx_k.data_ptr(), q.data_ptr(), idx_q.data_ptr(),
                                            idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
@@ -269,8 +285,8 @@ def sparse_attn_decode_profiled(p: Params, cache: PagedCache, max_ctx: int, q, i
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device, stream)
     ev = (ctypes.c_void_p * max(1, len(events)))(*[e.handle for e in events])
     n = ctypes.c_int32()
     _check(lib().sparse_attn_decode_profiled(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
@@ -288,8 +304,8 @@ def sparse_attn_prefill_profiled(p: Params, cache: PagedCache, q_start: int, q, 
     _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device, stream)
     ev = (ctypes.c_void_p * max(1, len(events)))(*[e.handle for e in events])
     n = ctypes.c_int32()
     _check(lib().sparse_attn_prefill_profiled(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start,
@@ -302,7 +318,7 @@ def sparse_attn_prefill_profiled(p: Params, cache: PagedCache, q_start: int, q, 
 def _host_i32(a, name, n):
     a = np.ascontiguousarray(np.asarray(a, dtype=np.int32))
     if a.shape != (n,):
-        raise SparseAttnError(f"{name}: expected {n} int32 entries, got shape {a.shape}")
+        raise SparseAttnError(SA_ERR_SHAPE, f"{name}: expected {n} int32 entries, got shape {a.shape}")
     return a
 
 
@@ -328,13 +344,13 @@ def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_start
     cu = _host_i32(cu_seqlens, "cu_seqlens", len(q_starts) + 1)
     qs = _host_i32(q_starts, "q_starts", len(q_starts))
     L = q.shape[0]
+    if int(cu[-1]) != L:
+        raise SparseAttnError(SA_ERR_SHAPE, f"cu_seqlens ends at {int(cu[-1])}, but q has {L} rows")
     _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
-    if int(cu[-1]) != L:
-        raise SparseAttnError(f"cu_seqlens ends at {int(cu[-1])}, but q has {L} rows")
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(prefill_varlen_workspace_size(p, cu, qs), q.device)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(prefill_varlen_workspace_size(p, cu, qs), q.device, stream)
     args = (ctypes.byref(p.c()), ctypes.byref(cache.c()), len(qs), cu.ctypes.data, qs.ctypes.data, q.data_ptr(),
             idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
             ws.numel(), _stream(stream))
@@ -371,8 +387,8 @@ def sparse_attn_decode_blocks(p: Params, cache: PagedCache, max_ctx: int, q, idx
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
-    blk, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(decode_blocks_workspace_size(p, B, max_ctx), q.device)
+    blk, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(decode_blocks_workspace_size(p, B, max_ctx), q.device, stream)
     _check(lib().sparse_attn_decode_blocks(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
                                            idx_q.data_ptr(), idx_w.data_ptr(), blk.data_ptr(), out.data_ptr(),
                                            _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)),
@@ -390,10 +406,8 @@ def sparse_attn_prefill_blocks(p: Params, cache: PagedCache, q_start: int, q_blo
     _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
     groups = (L + max(1, q_block) - 1) // max(1, q_block)
-    blk = torch.empty((groups, p.topk), dtype=torch.int32, device=q.device)
-    out = torch.empty((L, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
-                      device=q.device)
-    lse = torch.empty((L, p.num_heads), dtype=torch.float32, device=q.device) if want_lse else None
+    blk = _index_out(groups, p.topk, q.device, stream)
+    _, out, lse = _outputs(p, L, q.device, want_lse, stream)
     ws = workspace if workspace is not None else _workspace(prefill_blocks_workspace_size(p, L, q_start, q_block),
                                                             q.device)
     _check(lib().sparse_attn_prefill_blocks(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start, q_block,
@@ -423,7 +437,7 @@ def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_spli
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
     ws = workspace if workspace is not None else _workspace(decode_workspace_size_cfg(p, B, max_ctx, attn_splits),
                                                             q.device)
     _check(lib().sparse_attn_decode_cfg(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
@@ -441,8 +455,8 @@ def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, 
     n = ctypes.c_size_t()
     _check(lib().sa_decode_tune_workspace_size(ctypes.byref(p.c()), B, max_ctx, ctypes.byref(n)),
            "sa_decode_tune_workspace_size")
-    ws = _workspace(n.value, q.device)
-    topk_idx, out, lse = _outputs(p, B, q.device, True)
+    ws = _workspace(n.value, q.device, stream)
+    topk_idx, out, lse = _outputs(p, B, q.device, True, stream)
     best = sa_decode_config()
     us = ctypes.c_float()
     _check(lib().sa_decode_tune(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
@@ -500,8 +514,8 @@ def sparse_attn_select_decode(p: Params, cache: PagedCache, max_ctx: int, idx_q,
     _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
     if topk_idx is None:
-        topk_idx = torch.empty((B, p.topk), dtype=torch.int32, device=idx_q.device)
-    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), idx_q.device)
+        topk_idx = _index_out(B, p.topk, idx_q.device, stream)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), idx_q.device, stream)
     _check(lib().sparse_attn_select_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
                                            idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), ws.data_ptr(),
                                            ws.numel(), _stream(stream)), "sparse_attn_select_decode")
@@ -514,10 +528,8 @@ def sparse_attn_attend_decode(p: Params, cache: PagedCache, max_ctx: int, q, top
     B = q.shape[0]
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
     _dev(topk_idx, "topk_idx", (torch.int32,), (B, p.topk))
-    _, out, lse = _outputs(p, 0, q.device, False)
-    out = torch.empty((B, p.num_heads, p.v_dim), dtype=out.dtype, device=q.device)
-    lse = torch.empty((B, p.num_heads), dtype=torch.float32, device=q.device) if want_lse else None
-    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device)
+    _, out, lse = _outputs(p, B, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(decode_workspace_size(p, B, max_ctx), q.device, stream)
     _check(lib().sparse_attn_attend_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
                                            topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
                                            ws.numel(), _stream(stream)), "sparse_attn_attend_decode")
@@ -532,8 +544,8 @@ def sparse_attn_prefill(p: Params, cache: PagedCache, q_start: int, q, idx_q, id
     _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
-    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse)
-    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device)
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, L, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device, stream)
     _check(lib().sparse_attn_prefill(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start, q.data_ptr(),
                                      idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
                                      _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_prefill")
@@ -546,8 +558,8 @@ def sparse_attn_select_prefill(p: Params, cache: PagedCache, q_start: int, idx_q
     L = idx_q.shape[0]
     _dev(idx_q, "idx_q", _bf16_types(), (L, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (L, p.idx_heads))
-    topk_idx = torch.empty((L, p.topk), dtype=torch.int32, device=idx_q.device)
-    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), idx_q.device)
+    topk_idx = _index_out(L, p.topk, idx_q.device, stream)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), idx_q.device, stream)
     _check(lib().sparse_attn_select_prefill(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start,
                                             idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), ws.data_ptr(),
                                             ws.numel(), _stream(stream)), "sparse_attn_select_prefill")
@@ -560,10 +572,8 @@ def sparse_attn_attend_prefill(p: Params, cache: PagedCache, q_start: int, q, to
     L = q.shape[0]
     _dev(q, "q", _bf16_types(), (L, p.num_heads, p.qk_dim))
     _dev(topk_idx, "topk_idx", (torch.int32,), (L, p.topk))
-    out = torch.empty((L, p.num_heads, p.v_dim), dtype=torch.bfloat16 if p.out_bf16 else torch.float32,
-                      device=q.device)
-    lse = torch.empty((L, p.num_heads), dtype=torch.float32, device=q.device) if want_lse else None
-    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device)
+    _, out, lse = _outputs(p, L, q.device, want_lse, stream)
+    ws = workspace if workspace is not None else _workspace(prefill_workspace_size(p, L, q_start), q.device, stream)
     _check(lib().sparse_attn_attend_prefill(ctypes.byref(p.c()), ctypes.byref(cache.c()), L, q_start, q.data_ptr(),
                                             topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
                                             ws.numel(), _stream(stream)), "sparse_attn_attend_prefill")

@@ -80,7 +80,7 @@ typedef struct {
     int32_t idx_dim;        /* D_idx: indexer q/k width (one key vector per token) */
     int32_t block_size;     /* tokens per cache block */
     int32_t topk;           /* k: keys kept per query row */
-    float softmax_scale;    /* logits are softmax_scale * q.k */
+    float softmax_scale;    /* logits are softmax_scale * q.k; finite and > 0 */
     int32_t idx_relu;       /* 1: ReLU on each indexer head's dot product; 0: none */
     int32_t out_dtype;      /* sa_out_dtype of `out` */
 } sa_params;
@@ -157,8 +157,10 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *ca
  * already counts it); its physical slot, block_table[b][pos / bs] * bs +
  * pos % bs, is overwritten in cache->kv and cache->idx_k (the one call that
  * writes through the cache pointers, declared const for the read-only calls).
- * Sequences with context_lens[b] == 0, or whose block-table entry for the
- * position is outside [0, num_blocks), append nothing.  The scores, indices,
+ * Sequences with context_lens[b] == 0 append nothing.  As for every call, the
+ * block-table entries that cover tokens [0, context_lens[b]), this position's
+ * included, must be valid block ids (the cache struct's contract: the scan
+ * reads that block).  The scores, indices,
  * output and lse are those of sparse_attn_decode on the updated cache; no
  * kernel is added: the indexer scan scores each current token with its new
  * key, and the top-k launch, which precedes the attention, writes both rows.

@@ -83,6 +83,10 @@ def test_decode_validation(L):
     assert _decode(L, _params(v_dim=600), c) == sa.SA_ERR_SHAPE
     assert _decode(L, _params(out_dtype=7), c) == sa.SA_ERR_SHAPE
     assert _decode(L, _params(softmax_scale=float("nan")), c) == sa.SA_ERR_SHAPE
+    # a zero or negative scale would make the padding slots' masked logits
+    # meaningless (0 * -inf) and the reference max a minimum: rejected
+    assert _decode(L, _params(softmax_scale=0.0), c) == sa.SA_ERR_SHAPE
+    assert _decode(L, _params(softmax_scale=-0.125), c) == sa.SA_ERR_SHAPE
     assert _decode(L, _params(qk_dim=128, v_dim=128), c) == sa.SA_ERR_UNSUPPORTED
     assert _decode(L, _params(idx_dim=64), c) == sa.SA_ERR_UNSUPPORTED
     assert _decode(L, _params(num_heads=256), c) == sa.SA_ERR_UNSUPPORTED
@@ -204,6 +208,23 @@ def test_prefill_varlen_validation(L):
     assert a.value == b.value > 0
     assert L.sa_prefill_varlen_workspace_size(ctypes.byref(p), 3, None, _i32(0, 5, 200),
                                               ctypes.byref(a)) == sa.SA_ERR_NULL
+
+
+def test_varlen_binding_host_array_errors(L):
+    """The binding checks the host arrays of the multi-sequence prefill before
+    it touches a tensor and raises SparseAttnError with SA_ERR_SHAPE: a
+    cu_seqlens of the wrong length, and one that does not end at the row count
+    of q (the tensors here live on the CPU, so the checks must come first)."""
+    torch = pytest.importorskip("torch")
+    p = sa.Params.from_shape(synth.MLA)
+    q = torch.zeros((5, 1, 1), dtype=torch.bfloat16)
+    for cu, qs in (([0, 5], [0, 0]), ([0, 2, 5, 5], [0, 0]), ([0, 3], [0])):
+        with pytest.raises(sa.SparseAttnError) as e:
+            sa.sparse_attn_prefill_varlen(p, None, cu, qs, q, q, q)
+        assert e.value.status == sa.SA_ERR_SHAPE, (cu, qs)
+    with pytest.raises(sa.SparseAttnError) as e:
+        sa.prefill_varlen_workspace_size(p, [0, 2, 5, 7], [0, 0])
+    assert e.value.status == sa.SA_ERR_SHAPE
 
 
 def test_block_selection_validation(L):

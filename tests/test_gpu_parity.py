@@ -2,11 +2,14 @@
 
 Bar: selected indices bit-exact (the indexer inputs are small integers, so every
 score is exact in fp32 on both sides); attention output within 2e-2 max-abs and
-2e-3 mean-abs error, each query row's error measured relative to the RMS of that
-row's oracle output (a prefill row that keeps one key outputs a V row, RMS ~1,
-one that averages 2048 keys has RMS ~0.05, so one RMS for the whole tensor would
-weigh rows by their scale); lse within 1e-3 absolute.  Full-size workloads run in the same launch configuration as the
-benchmark and compare the rows the oracle can afford, one by one.
+2e-3 mean-abs error relative to the RMS of the oracle's whole output tensor of
+the workload, and, in addition, to the same bar relative to each query row's
+own oracle RMS (a prefill row that keeps one key outputs a V row, RMS ~1, one
+that averages 2048 keys has RMS ~0.05, so each basis is the stricter one for
+some rows); lse within 1e-3 absolute.  Where only some rows are compared, the
+whole-tensor RMS is that of the device output over every row, after checking
+that on the compared rows the device RMS equals the oracle's to 1e-3.
+Full-size workloads run in the same launch configuration as the benchmark.
 """
 import os
 import sys
@@ -64,34 +67,53 @@ def run_gpu(dev, w, out_bf16=False, staged=False):
     return res
 
 
+def device_rms(out_all):
+    """RMS of a device output tensor over every row (float64 accumulation)."""
+    torch = __import__("torch")
+    x = out_all.reshape(out_all.shape[0], -1)
+    ss = 0.0
+    for r0 in range(0, x.shape[0], 1024):
+        ss += float(x[r0:r0 + 1024].double().square().sum())
+    return float(np.sqrt(ss / max(1, x.numel())))
+
+
 def compare(w, res, rows=None, tag=""):
     tk_all, out_all, lse_all = res[:3]
     ref = oracle.run_varlen(w, rows=rows) if w["mode"] == "varlen" else oracle.run(w, rows=rows)
-    rows = ref["rows"]
-    idx = __import__("torch").as_tensor(rows, device=tk_all.device)
+    rows_sel = ref["rows"]
+    idx = __import__("torch").as_tensor(rows_sel, device=tk_all.device)
     tk = tk_all.index_select(0, idx).cpu().numpy()
     out = out_all.index_select(0, idx).float().cpu().numpy().astype(np.float64)
     lse = lse_all.index_select(0, idx).cpu().numpy().astype(np.float64)
     bad = np.nonzero(~np.all(tk == ref["topk"], axis=1))[0]
-    assert len(bad) == 0, f"{tag}: indices differ on rows {rows[bad][:8]}"
-    check_outputs(ref, out, lse, rows, tag)
+    assert len(bad) == 0, f"{tag}: indices differ on rows {rows_sel[bad][:8]}"
+    check_outputs(ref, out, lse, rows_sel, tag, None if rows is None else device_rms(out_all))
     return ref
 
 
-def check_outputs(ref, out, lse, rows, tag):
-    """Outputs (float64 copies of the listed rows) against the oracle's."""
+def check_outputs(ref, out, lse, rows, tag, rms_all=None):
+    """Outputs (float64 copies of the listed rows) against the oracle's.
+    rms_all: the whole-tensor RMS basis when only some rows are listed (the
+    device output's over every row); None when every row is listed."""
     assert np.isfinite(out).all(), f"{tag}: non-finite output"
-    rms_all = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    rms_ref = float(np.sqrt(np.mean(ref["out"] ** 2)))
+    if rms_all is None:
+        rms_all = rms_ref
+    else:
+        rms_dev = float(np.sqrt(np.mean(out ** 2)))
+        assert abs(rms_dev - rms_ref) <= 1e-3 * rms_ref, f"{tag}: device RMS {rms_dev} vs oracle {rms_ref}"
     rms = np.sqrt(np.mean(ref["out"] ** 2, axis=(1, 2), keepdims=True))
     rms = np.where(rms > 0, rms, 1.0)  # empty-context rows: output 0 on both sides
-    err = np.abs(out - ref["out"]) / rms
-    gerr = np.abs(out - ref["out"]) / rms_all
+    diff = np.abs(out - ref["out"])
+    err = diff / rms
+    gerr = diff / (rms_all if rms_all > 0 else 1.0)
     empty = np.isneginf(ref["lse"])
     assert np.array_equal(np.isneginf(lse), empty), f"{tag}: empty-context rows disagree"
     lerr = np.abs(np.where(empty, 0, lse) - np.where(empty, 0, ref["lse"]))
     say(f"  {tag}: rows {len(rows)} out err/row-rms max {err.max():.3e} mean {err.mean():.3e}; "
-        f"err/global-rms max {gerr.max():.3e} mean {gerr.mean():.3e} (rms {rms_all:.3f}); lse err max {lerr.max():.2e}")
-    assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, tag
+        f"err/tensor-rms max {gerr.max():.3e} mean {gerr.mean():.3e} (rms {rms_all:.4f}); lse err max {lerr.max():.2e}")
+    assert gerr.max() <= MAX_REL and gerr.mean() <= MEAN_REL, f"{tag}: whole-tensor RMS bar"
+    assert err.max() <= MAX_REL and err.mean() <= MEAN_REL, f"{tag}: per-row RMS bar"
     assert lerr.max() <= LSE_ABS, tag
 
 
@@ -119,6 +141,7 @@ CASES = {
     # head counts that leave waves (or lanes of a wave) without a head
     "decode_h48": lambda: synth.small_decode("decode_h48", replace(MLA, num_heads=48), [1, 40, 2100, 5000], seed=110),
     "decode_h96": lambda: synth.small_decode("decode_h96", replace(MLA, num_heads=96), [2, 33, 2048, 6000], seed=111),
+    "decode_h20": lambda: synth.small_decode("decode_h20", replace(MLA, num_heads=20), [3, 700, 2048, 4500], seed=116),
     "decode_tiny_h40": lambda: synth.small_decode("decode_tiny_h40", replace(synth.TINY, num_heads=40), [5, 64, 900],
                                                   seed=112),
     # value width 64 with 32 splits per row: the merge's column loop then runs on
@@ -164,6 +187,27 @@ def test_block_relabelling_invariance_gpu(dev):
         assert np.array_equal(x.cpu().numpy(), y.cpu().numpy())
 
 
+def test_side_stream(dev):
+    """The call on a non-default stream: its workspace and default outputs are
+    allocated for that stream, so tensors the caller allocates meanwhile on its
+    current stream never share their memory while the kernels run."""
+    torch, sa = dev
+    spec = CASES["decode_ragged"]()
+    say("[gpu] decode on a side stream")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    res = sa.sparse_attn_decode(p, d["cache"], int(w["context_lens"].max()), d["q"], d["idx_q"], d["idx_w"],
+                                stream=side)
+    junk = [torch.full((1 << 22,), 7.0, device="cuda") for _ in range(8)]
+    side.synchronize()
+    torch.cuda.synchronize()
+    del junk
+    compare(w, res, tag="decode_ragged side stream")
+
+
 def test_bf16_output(dev):
     spec = CASES["decode_ragged"]()
     say("[gpu] bf16 output")
@@ -172,13 +216,25 @@ def test_bf16_output(dev):
 
 
 # ------------------------------------------------------- full-size workloads --
+def _prefill_rows(n=256, seed=171):
+    """Stratified rows of the 32768-row prefill: the first rows (few keys), the
+    rows around the first 2048 (where selection starts), both sides of each
+    8192-row score chunk and of each 4096-row sequence of the multi-sequence
+    workload, the last row, and random rows across the rest."""
+    fixed = {0, 1, 2, 3, 7, 31, 32, 63, 64, 255, 1023, 2045, 2046, 2047, 2048, 2049, 4095, 4096, 8191, 8192,
+             12287, 12288, 16383, 16384, 20479, 20480, 24575, 24576, 28671, 28672, 32766, 32767}
+    rng = np.random.default_rng(seed)
+    rest = [int(x) for x in rng.choice(np.setdiff1d(np.arange(32768), sorted(fixed)), n - len(fixed), replace=False)]
+    return sorted(fixed | set(rest))
+
+
 FULL_ROWS = {
     "tiny_prefill_L256": None,                       # every row
     "decode_b32_ctx8k": None,                        # every row
-    "decode_b64_ctx16k_128k": "ends",                # shortest, longest and a few more
-    "decode_b4_ctx1m": [0, 3],
-    "prefill_L32k": [0, 1, 2046, 2047, 2048, 2049, 4095, 16000, 31999, 32767],
-    "prefill_varlen_8x4k": [0, 1, 2047, 4095, 4096, 8191, 12345, 20480, 28671, 28672, 30000, 32767],
+    "decode_b64_ctx16k_128k": None,                  # every row
+    "decode_b4_ctx1m": None,                         # every row
+    "prefill_L32k": _prefill_rows(),
+    "prefill_varlen_8x4k": _prefill_rows(seed=172),
 }
 
 
@@ -187,11 +243,7 @@ def test_parity_full_size(dev, name):
     spec = synth.WORKLOADS[name]
     say(f"[gpu] full-size parity {name}")
     w = synth.make(spec)
-    rows = FULL_ROWS[name]
-    if rows == "ends":
-        ctx = w["context_lens"]
-        rows = sorted({int(np.argmin(ctx)), int(np.argmax(ctx)), 0, 17, 63})
-    compare(w, run_gpu(dev, w), rows=rows, tag=name)
+    compare(w, run_gpu(dev, w), rows=FULL_ROWS[name], tag=name)
 
 
 def test_parity_scan_score_bursts(dev):
@@ -352,7 +404,7 @@ def compare_blocks(w, res, q_block, rows=None, tag=""):
     idx = torch.as_tensor(ref["rows"], device=out_all.device)
     out = out_all.index_select(0, idx).float().cpu().numpy().astype(np.float64)
     lse = lse_all.index_select(0, idx).cpu().numpy().astype(np.float64)
-    check_outputs(ref, out, lse, ref["rows"], tag)
+    check_outputs(ref, out, lse, ref["rows"], tag, None if rows is None else device_rms(out_all))
 
 
 @pytest.mark.parametrize("name", list(BLOCK_CASES))
