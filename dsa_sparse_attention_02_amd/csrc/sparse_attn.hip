@@ -1,8 +1,9 @@
 // libsparse_attn: C ABI (include/sparse_attn.h) over the gfx950 kernels.
 //
-// Every check runs before the first HIP call; the library never allocates,
-// never synchronises (the tuner aside, which measures) and keeps no mutable
-// global state.  Work is queued on the
+// Every check runs before the first HIP call; the library never allocates and
+// never synchronises (the tuner aside, which measures); its one global state is
+// the allocation-free decode's static scratch array and that array's address on
+// each device.  Work is queued on the
 // caller's stream in this order:
 //   decode : indexer scan -> per-row top-k -> split attention -> split merge
 //   prefill: per chunk of rows { indexer tile scan -> per-row top-k },
@@ -18,6 +19,7 @@
 #include <cmath>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <vector>
 
 #include "../../include/sparse_attn.h"
@@ -1139,6 +1141,49 @@ sa_status sparse_attn_prefill_blocks(const sa_params *p, const sa_paged_cache *c
     prefill_blocks_impl(p, c, num_rows, q_start, q, idx_q, idx_w, block_idx, out, lse, workspace, b, d,
                         (hipStream_t)stream, nullptr);
     return launched();
+}
+
+// ------------------------------------------------- allocation-free decode --
+// The scratch memory of sparse_attn_decode_noalloc: one copy per device,
+// alive until the process ends.  Host code never passes the array's name to a
+// kernel (in host code it is a host-side stand-in): it uses the device address
+// that hipGetSymbolAddress returns, looked up once per device.
+static __device__ __align__(256) uint8_t scratch[SA_NOALLOC_SCRATCH_BYTES];
+
+static std::mutex g_scratch_mu;
+static void *g_scratch_addr[64];  // device address of `scratch`, by device id
+
+// The address of `scratch` on the caller's current device (looked up on the
+// first call for that device, with that device current).
+static sa_status scratch_address(void **addr)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SA_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SA_ERR_HIP;
+        g_scratch_addr[dev] = ptr;
+    }
+    *addr = g_scratch_addr[dev];
+    return SA_OK;
+}
+
+sa_status sparse_attn_decode_noalloc(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
+                                     const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx,
+                                     void *out, float *lse, void *stream)
+{
+    sa_status s = check_decode(p, c, batch, max_ctx, true, true);
+    if (s != SA_OK) return s;
+    if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
+    if (plan_decode(p, batch, max_ctx).total > SA_NOALLOC_SCRATCH_BYTES) return SA_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if ((s = scratch_address(&ws)) != SA_OK) return s;
+    // every kernel of the decode writes the scratch it reads (the many-workgroup
+    // top-k clears its histograms in its first launch), so the previous call's
+    // contents need no clearing
+    return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, ws, SA_NOALLOC_SCRATCH_BYTES,
+                       stream, nullptr);
 }
 
 }  // extern "C"

@@ -28,7 +28,7 @@ EXPORTS = (
     "sa_prefill_varlen_workspace_size", "sparse_attn_prefill_varlen", "sparse_attn_prefill_varlen_profiled",
     "sa_decode_blocks_workspace_size", "sparse_attn_decode_blocks", "sa_prefill_blocks_workspace_size",
     "sparse_attn_prefill_blocks", "sa_decode_workspace_size_cfg", "sparse_attn_decode_cfg",
-    "sa_decode_tune_workspace_size", "sa_decode_tune",
+    "sa_decode_tune_workspace_size", "sa_decode_tune", "sparse_attn_decode_noalloc",
 )
 
 
@@ -97,6 +97,7 @@ def lib():
             "sa_decode_tune_workspace_size": (ctypes.c_int, [pp, i32, i32, ctypes.POINTER(sz)]),
             "sa_decode_tune": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P, i32, P,
                                               ctypes.POINTER(ctypes.c_float)]),
+            "sparse_attn_decode_noalloc": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P]),
         }
         for name, (res, args) in sig.items():
             f = getattr(L, name)
@@ -251,6 +252,24 @@ def sparse_attn_decode(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx
     _check(lib().sparse_attn_decode(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
                                     idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(),
                                     _ptr(lse), ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode")
+    return topk_idx, out, lse
+
+
+def sparse_attn_decode_noalloc(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, want_lse=True,
+                               outputs=None, stream=None):
+    """sparse_attn_decode with the library's static scratch array instead of a
+    workspace (the C call allocates nothing; only default outputs are
+    allocated here).  Calls that overlap on one GPU race."""
+    torch = _torch()
+    B = q.shape[0]
+    _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
+    _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
+    _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
+    topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
+    _check(lib().sparse_attn_decode_noalloc(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx, q.data_ptr(),
+                                            idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(),
+                                            out.data_ptr(), _ptr(lse), _stream(stream)),
+           "sparse_attn_decode_noalloc")
     return topk_idx, out, lse
 
 

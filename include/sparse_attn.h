@@ -25,8 +25,10 @@
  *    packed in the layouts given below.
  *  - Ownership: the caller allocates and frees every buffer, including the
  *    workspace, whose size comes from the matching *_workspace_size call.  The
- *    library never allocates or frees device memory and keeps no mutable global
- *    state; calls on different streams with different workspaces may overlap.
+ *    library never allocates or frees device memory; calls on different
+ *    streams with different workspaces may overlap.  Its only global state
+ *    is the static scratch array of sparse_attn_decode_noalloc (below) and
+ *    that array's device address, looked up once per device.
  *  - Streams: all work is queued on `stream` (a hipStream_t; NULL = the null
  *    stream).  No call synchronises (except sa_decode_tune, which measures);
  *    SA_OK means "queued".
@@ -339,6 +341,31 @@ sa_status sparse_attn_prefill_blocks(const sa_params *p, const sa_paged_cache *c
                                      int32_t q_start, int32_t q_block, const void *q, const void *idx_q,
                                      const float *idx_w, int32_t *block_idx, void *out, float *lse,
                                      void *workspace, size_t workspace_bytes, void *stream);
+
+/* ------------------------------------------------- allocation-free decode --
+ * sparse_attn_decode for callers that cannot allocate device memory at all,
+ * not even a workspace: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The inputs, outputs and their meaning are
+ * those of sparse_attn_decode; the scratch memory (scores, split partials,
+ * top-k state) is a static device array inside the library,
+ * SA_NOALLOC_SCRATCH_BYTES (128 MiB) on every device the library runs on,
+ * held until the process ends.  The call allocates and frees nothing.  Its
+ * first call on a device (the caller's current device) looks the array's
+ * device address up once and keeps it.
+ *  - A batch whose decode workspace (sa_decode_workspace_size) exceeds
+ *    SA_NOALLOC_SCRATCH_BYTES -> SA_ERR_WORKSPACE, before any HIP call.
+ *    (Batch 64 at 128K keys needs about 69 MB, batch 4 at 1M keys about
+ *    41 MB.)
+ *  - All calls on one GPU share the array and it keeps the last call's
+ *    contents: calls that overlap in time on one GPU (other streams, other
+ *    threads) race and give wrong results; serialise them.
+ *  - A failure to look up the array's address -> SA_ERR_HIP.
+ * Other errors as for sparse_attn_decode. */
+#define SA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+sa_status sparse_attn_decode_noalloc(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
+                                     int32_t max_ctx, const void *q, const void *idx_q,
+                                     const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                     void *stream);
 
 #ifdef __cplusplus
 }

@@ -210,6 +210,26 @@ def test_prefill_varlen_validation(L):
                                               ctypes.byref(a)) == sa.SA_ERR_NULL
 
 
+def test_decode_noalloc_validation(L):
+    """The allocation-free decode checks what sparse_attn_decode checks, and
+    rejects a batch whose workspace would exceed its static scratch array with
+    SA_ERR_WORKSPACE, all before any HIP call."""
+    p, c = _params(), _cache()
+    f = L.sparse_attn_decode_noalloc
+    ok = (FAKE,) * 5 + (None, None)
+    assert f(None, ctypes.byref(c), 2, 256, *ok) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(p), None, 2, 256, *ok) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(p), ctypes.byref(c), 2, 256, None, *ok[1:]) == sa.SA_ERR_NULL
+    assert f(ctypes.byref(p), ctypes.byref(c), 0, 256, *ok) == sa.SA_ERR_SHAPE
+    assert f(ctypes.byref(_params(softmax_scale=0.0)), ctypes.byref(c), 2, 256, *ok) == sa.SA_ERR_SHAPE
+    # 2048 rows of 64K keys need far more than 128 MiB of scores
+    big = _cache(max_blocks_per_seq=1024)
+    assert f(ctypes.byref(p), ctypes.byref(big), 2048, 65536, *ok) == sa.SA_ERR_WORKSPACE
+    n = ctypes.c_size_t()
+    assert L.sa_decode_workspace_size(ctypes.byref(p), 2048, 65536, ctypes.byref(n)) == sa.SA_OK
+    assert n.value > (128 << 20)
+
+
 def test_varlen_binding_host_array_errors(L):
     """The binding checks the host arrays of the multi-sequence prefill before
     it touches a tensor and raises SparseAttnError with SA_ERR_SHAPE: a
