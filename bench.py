@@ -10,7 +10,12 @@ resident in HBM.  Secondary lines: prefill query-tokens/s on the L = 32768
 workload, and the CPU oracle timed on the host cores on a bounded sample.
 
 Per-kernel durations come from HIP events that the profiling entry point records
-on the library's stream between its kernels inside the timed region.
+on the library's stream between its kernels, in event-marked steps of their own.
+Order of a run: peak probe, the other decode workloads (batch 32 x 8K, 4 x 1M,
+64 x 128K, each back to back and with a 1 GiB cache flush before every step),
+the two prefill lines, the supplementary decode calls on the headline batch,
+its event-marked and flushed steps, and last the headline: W warm-up steps,
+then K plain steps between two synchronisations.
 """
 import argparse
 import hashlib
@@ -46,10 +51,16 @@ def decode_algorithmic(w):
         sh.idx_heads * (2 * sh.idx_dim + 4)
     total = scan + gather + len(ctx) * per_q + int((4 * kept).sum()) + int((4 * blocks).sum())
     flops = int((2 * ctx * sh.idx_heads * sh.idx_dim).sum() + (2 * kept * sh.num_heads * (sh.qk_dim + sh.v_dim)).sum())
-    # the indexer kernel alone: key rows + score writes + per-row query/weights + block table
-    idx_bytes = int((ctx * (sh.idx_dim * 2 + 4)).sum() + len(ctx) * sh.idx_heads * (2 * sh.idx_dim + 4) +
+    # the indexer scan alone, as the method needs it: the key rows, the row's
+    # indexer query and head weights, and one block-table entry per block (the
+    # fp32 scores the scan writes for the top-k are not counted)
+    idx_bytes = int((ctx * sh.idx_dim * 2).sum() + len(ctx) * sh.idx_heads * (2 * sh.idx_dim + 4) +
                     (4 * blocks).sum())
-    return dict(bytes=total, scan=scan, gather=gather, flops=flops, indexer_bytes=idx_bytes)
+    # the attention alone: the kept latent rows, the queries and the outputs
+    attn_bytes = gather + len(ctx) * sh.num_heads * (sh.qk_dim * 2 + sh.v_dim * 4)
+    attn_flops = int((2 * kept * sh.num_heads * (sh.qk_dim + sh.v_dim)).sum())
+    return dict(bytes=total, scan=scan, gather=gather, flops=flops, indexer_bytes=idx_bytes,
+                attention_bytes=attn_bytes, attention_flops=attn_flops)
 
 
 def source_hash(*names):
@@ -75,8 +86,10 @@ def traffic_from_profiles(kernel_key, launches_per_step):
     return e.get("bytes_per_launch")
 
 
-def run_decode(args, torch, sa, synth):
-    spec = synth.WORKLOADS[args.workload]
+def setup_decode(name, torch, sa, synth):
+    """Generate a decode workload, copy it to the device, and prepare the plain
+    and event-marked calls over it."""
+    spec = synth.WORKLOADS[name]
     log(f"generating {spec.name} (seed {spec.seed})")
     t = time.time()
     w = synth.make(spec)
@@ -87,70 +100,95 @@ def run_decode(args, torch, sa, synth):
     max_ctx = int(w["context_lens"].max())
     ws = torch.empty(sa.decode_workspace_size(p, B, max_ctx), dtype=torch.uint8, device="cuda")
     outs = sa._outputs(p, B, "cuda", True)
-    call = lambda ev: sa.sparse_attn_decode_profiled(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], ev,
-                                                     workspace=ws, outputs=outs)
-    n_marks = call([])[3]
-    kernels = ["indexer", "topk", "attention", "merge"][:n_marks - 1] if max_ctx > p.topk else \
-        ["topk", "attention", "merge"][:n_marks - 1]
+    marked = lambda ev: sa.sparse_attn_decode_profiled(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], ev,
+                                                       workspace=ws, outputs=outs)
     plain = lambda: sa.sparse_attn_decode(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], workspace=ws,
                                           outputs=outs)
-    log(f"warmup {args.warmup} steps ({n_marks - 1} kernels per step: {', '.join(kernels)})")
-    for _ in range(args.warmup):
-        plain()
+    n_marks = marked([])[3]
+    kernels = (["indexer", "topk", "attention", "merge"] if max_ctx > p.topk else
+               ["topk", "attention", "merge"])[:n_marks - 1]
+    return dict(name=name, w=w, d=d, p=p, B=B, max_ctx=max_ctx, ws=ws, outs=outs, plain=plain, marked=marked,
+                n_marks=n_marks, kernels=kernels, alg=decode_algorithmic(w))
+
+
+def time_back_to_back(torch, fn, steps, warmup):
+    """warmup untimed calls, then `steps` calls timed between two synchronisations (ms per call)"""
+    for _ in range(warmup):
+        fn()
     torch.cuda.synchronize()
-    # The timed steps are plain calls: an event recorded between two kernels
-    # holds the next one back, so per-stage times come from separate steps.
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        plain()
+    for _ in range(steps):
+        fn()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms = (t1 - t0) * 1e3 / args.steps
-    # The same step with each sequence's current token appended to the cache
-    # first (sparse_attn_decode_append; the same token every step, so the cache
-    # holds the same values throughout), timed like the plain step right after it.
-    append_ms = None
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def time_stages(torch, sa, c, steps):
+    """Per-kernel durations from HIP events that the profiling entry point
+    records on the library's stream between its kernels; also the step time of
+    these event-marked steps (an event between kernels delays the next one)."""
+    events = [[sa.HipEvent() for _ in range(c["n_marks"])] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        c["marked"](events[s])
+    torch.cuda.synchronize()
+    ms_marked = (time.perf_counter() - t0) * 1e3 / steps
+    per_kernel = {k: [ev[i].elapsed_ms(ev[i + 1]) for ev in events] for i, k in enumerate(c["kernels"])}
+    return {k: statistics.mean(v) for k, v in per_kernel.items()}, ms_marked
+
+
+def time_flushed(torch, sa, c, steps):
+    """Steps with a 1 GiB write before each (the 256 MB MALL and the L2 hold
+    none of the step's data), each timed alone between events; median ms."""
+    flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
+    times = []
+    for _ in range(steps):
+        flush.fill_(1.0)
+        ev = [sa.HipEvent() for _ in range(c["n_marks"])]
+        c["marked"](ev)
+        torch.cuda.synchronize()
+        times.append(ev[0].elapsed_ms(ev[-1]))
+    del flush
+    return statistics.median(times), min(times)
+
+
+def decode_line(c, ms):
+    """tokens/s and algorithmic HBM rate of a decode step of ms milliseconds"""
+    B, alg = c["B"], c["alg"]
+    return {"ms_per_step": round(ms, 4), "tokens_per_s": round(B / (ms / 1e3), 1),
+            "hbm_gbps": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
+            "hbm_frac": round(alg["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "algorithmic_bytes_per_step": alg["bytes"]}
+
+
+def supplementary_decode(args, torch, sa, synth, c):
+    """On the headline batch: the call that appends each sequence's current
+    token first, the run-time tuned call, and block-granular selection."""
+    p, d, w, B, max_ctx, ws, outs = c["p"], c["d"], c["w"], c["B"], c["max_ctx"], c["ws"], c["outs"]
+    res = {}
     if args.append_steps > 0:
         nk_np, ni_np = synth.new_tokens(w)
         nk = torch.from_numpy(nk_np).view(torch.bfloat16).cuda()
         ni = torch.from_numpy(ni_np).view(torch.bfloat16).cuda()
+        # (the same token every step, so the cache keeps its values)
         app = lambda: sa.sparse_attn_decode_append(p, d["cache"], max_ctx, nk, ni, d["q"], d["idx_q"], d["idx_w"],
                                                    workspace=ws, outputs=outs)
-        for _ in range(args.warmup):
-            app()
-        torch.cuda.synchronize()
-        ta = time.perf_counter()
-        for _ in range(args.append_steps):
-            app()
-        torch.cuda.synchronize()
-        append_ms = (time.perf_counter() - ta) * 1e3 / args.append_steps
-        tb = time.perf_counter()
-        for _ in range(args.steps):
-            plain()
-        torch.cuda.synchronize()
-        again = (time.perf_counter() - tb) * 1e3 / args.steps
-        log(f"decode with append: {append_ms:.3f} ms/step (plain step again after it: {again:.3f} ms)")
-    # Run-time tuning of the attention split count on this batch, then the
-    # configured call timed like the plain one.
-    tuned = None
+        ms_app = time_back_to_back(torch, app, args.append_steps, 20)
+        ms_plain = time_back_to_back(torch, c["plain"], args.append_steps, 0)
+        log(f"decode with append: {ms_app:.3f} ms/step (plain step right after it: {ms_plain:.3f} ms)")
+        res["decode_append"] = {"ms_per_step": round(ms_app, 4), "tokens_per_s": round(B / (ms_app / 1e3), 1),
+                                "added_us": round((ms_app - ms_plain) * 1e3, 2)}
     if args.tune:
         splits, tune_us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=10)
         wst = torch.empty(sa.decode_workspace_size_cfg(p, B, max_ctx, splits), dtype=torch.uint8, device="cuda")
         cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"],
                                                 workspace=wst, outputs=outs)
-        for _ in range(args.warmup):
-            cfg()
-        torch.cuda.synchronize()
-        tc = time.perf_counter()
-        for _ in range(args.steps):
-            cfg()
-        torch.cuda.synchronize()
-        tuned = dict(attn_splits=splits, ms=(time.perf_counter() - tc) * 1e3 / args.steps, tune_us=tune_us)
-        log(f"tuned: {splits} attention splits per row, {tuned['ms']:.3f} ms/step (tuner's own mean {tune_us:.1f} us)")
+        ms = time_back_to_back(torch, cfg, 20, 20)
+        log(f"tuned: {splits} attention splits per row, {ms:.3f} ms/step (tuner's own mean {tune_us:.1f} us)")
+        res["decode_tuned"] = {"attn_splits": splits, "ms_per_step": round(ms, 4),
+                               "tokens_per_s": round(B / (ms / 1e3), 1)}
         del wst
-    # Block-granular selection over the same batch: k / block_size whole cache
-    # blocks per row (the same number of attended token slots), timed the same way.
-    blocks_ms = None
     if args.blocks_steps > 0:
         from dataclasses import replace
         sh = w["shape"]
@@ -159,70 +197,41 @@ def run_decode(args, torch, sa, synth):
         outb = sa._outputs(pb, B, "cuda", True)
         blk = lambda: sa.sparse_attn_decode_blocks(pb, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"],
                                                    workspace=wsb, outputs=outb)
-        for _ in range(args.warmup):
-            blk()
-        torch.cuda.synchronize()
-        tb = time.perf_counter()
-        for _ in range(args.blocks_steps):
-            blk()
-        torch.cuda.synchronize()
-        blocks_ms = (time.perf_counter() - tb) * 1e3 / args.blocks_steps
-        log(f"decode with block selection ({pb.topk} blocks of {sh.block_size}): {blocks_ms:.3f} ms/step")
+        ms = time_back_to_back(torch, blk, args.blocks_steps, 20)
+        log(f"decode with block selection ({pb.topk} blocks of {sh.block_size}): {ms:.3f} ms/step")
+        res["decode_blocks"] = {"ms_per_step": round(ms, 4), "tokens_per_s": round(B / (ms / 1e3), 1),
+                                "kept_blocks": pb.topk, "block_size": sh.block_size}
         del wsb, outb
-    events = [[sa.HipEvent() for _ in range(n_marks)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for s in range(args.steps):
-        call(events[s])
-    torch.cuda.synchronize()
-    ms_marked = (time.perf_counter() - t2) * 1e3 / args.steps
-    log(f"steps with an event after every kernel: {ms_marked:.3f} ms/step")
-    per_kernel = {k: [] for k in kernels}
-    for ev in events:
-        for i, k in enumerate(kernels):
-            per_kernel[k].append(ev[i].elapsed_ms(ev[i + 1]))
-    stages = {k: statistics.mean(v) for k, v in per_kernel.items()}
-    log(f"timed {args.steps} steps: {ms:.3f} ms/step; stages " +
-        ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in stages.items()))
-
-    # the same step with a 1 GiB write between steps (HBM-cold caches), events only
-    cold = []
-    if args.flush_steps > 0:
-        flush = torch.empty(1 << 28, dtype=torch.float32, device="cuda")
-        for _ in range(args.flush_steps):
-            flush.fill_(1.0)
-            ev = [sa.HipEvent() for _ in range(n_marks)]
-            call(ev)
-            torch.cuda.synchronize()
-            cold.append(ev[0].elapsed_ms(ev[-1]))
-        del flush
-    alg = decode_algorithmic(w)
-    return w, dict(ms=ms, stages=stages, cold_ms=statistics.median(cold) if cold else None, alg=alg,
-                   per_kernel=per_kernel, append_ms=append_ms, ms_marked=ms_marked, blocks_ms=blocks_ms,
-                   tuned=tuned)
-
-
-def run_other_decodes(args, torch, sa, synth, names):
-    """The other decode configurations, timed like the main one (fewer steps, no flush)."""
-    res = {}
-    for name in names:
-        sub = argparse.Namespace(**vars(args))
-        sub.workload, sub.steps, sub.warmup, sub.flush_steps, sub.append_steps = name, 20, 20, 0, 0
-        sub.blocks_steps = 0
-        w, dec = run_decode(sub, torch, sa, synth)
-        B = len(w["context_lens"])
-        res[name] = {"ms_per_step": round(dec["ms"], 4), "tokens_per_s": round(B / (dec["ms"] / 1e3), 1),
-                     "hbm_gbps": round(dec["alg"]["bytes"] / (dec["ms"] / 1e3) / 1e9, 1),
-                     "hbm_frac": round(dec["alg"]["bytes"] / (dec["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
-                     "algorithmic_bytes_per_step": dec["alg"]["bytes"],
-                     "stages_us": {k: round(v * 1e3, 2) for k, v in dec["stages"].items()}}
-        if dec["tuned"]:
-            res[name]["tuned"] = {"attn_splits": dec["tuned"]["attn_splits"],
-                                  "ms_per_step": round(dec["tuned"]["ms"], 4),
-                                  "tokens_per_s": round(B / (dec["tuned"]["ms"] / 1e3), 1)}
-        del w, dec
-        torch.cuda.empty_cache()
     return res
+
+
+def run_other_decode(args, torch, sa, synth, name):
+    """Another decode configuration: back-to-back steps, MALL-flushed steps
+    (median) and per-kernel stages; supplementary lines, not the metric."""
+    c = setup_decode(name, torch, sa, synth)
+    ms = time_back_to_back(torch, c["plain"], 20, 50)
+    stages, _ = time_stages(torch, sa, c, 10)
+    cold, cold_min = time_flushed(torch, sa, c, 10)
+    line = decode_line(c, ms)
+    line["flushed"] = {"median_ms": round(cold, 4), "min_ms": round(cold_min, 4),
+                       "tokens_per_s": round(c["B"] / (cold / 1e3), 1),
+                       "hbm_frac": round(c["alg"]["bytes"] / (cold / 1e3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    line["stages_us"] = {k: round(v * 1e3, 2) for k, v in stages.items()}
+    log(f"{name}: {ms:.4f} ms/step back to back, {cold:.4f} ms flushed (median); stages " +
+        ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in stages.items()))
+    if args.tune:
+        p, d = c["p"], c["d"]
+        splits, _ = sa.decode_tune(p, d["cache"], c["max_ctx"], d["q"], d["idx_q"], d["idx_w"], reps=10)
+        wst = torch.empty(sa.decode_workspace_size_cfg(p, c["B"], c["max_ctx"], splits), dtype=torch.uint8,
+                          device="cuda")
+        cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], c["max_ctx"], splits, d["q"], d["idx_q"],
+                                                d["idx_w"], workspace=wst, outputs=c["outs"])
+        mt = time_back_to_back(torch, cfg, 20, 20)
+        line["tuned"] = {"attn_splits": splits, "ms_per_step": round(mt, 4),
+                         "tokens_per_s": round(c["B"] / (mt / 1e3), 1)}
+    del c
+    torch.cuda.empty_cache()
+    return line
 
 
 def prefill_pieces(w):
@@ -311,6 +320,35 @@ def run_prefill(args, torch, sa, synth, name="prefill_L32k"):
     return res
 
 
+def measured_peaks():
+    """The peak probe (dsa_sparse_attention_02_amd/peak_probe, built with the
+    library): streamed HBM read and copy rates, bf16 MFMA throughput and LDS
+    read bandwidth of this GPU, or None when the probe is missing."""
+    import subprocess
+    exe = os.path.join(ROOT, "dsa_sparse_attention_02_amd", "peak_probe")
+    if not os.path.exists(exe):
+        log("peak probe not built; no measured peaks")
+        return None
+    r = subprocess.run([exe], capture_output=True, text=True, timeout=120)
+    if r.returncode != 0:
+        log(f"peak probe failed: {r.stderr.strip()[-200:]}")
+        return None
+    return json.loads(r.stdout.strip().splitlines()[-1])
+
+
+def cpu_model():
+    """The host CPU's model name (as lscpu reports it, from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(args, w):
     """The oracle as it stands, on the host's cores, over a bounded sample of the
     same batch: rows longest first, passes repeated until the time budget is spent."""
@@ -330,6 +368,7 @@ def cpu_baseline(args, w):
     el = time.perf_counter() - t0
     rows = sorted(distinct)
     return {"value": round(done / el, 3), "unit": "tokens/s", "cores": oracle.max_threads(), "kind": "oracle",
+            "cpu": cpu_model(), "logical_cpus": os.cpu_count(),
             "sample": f"{done} decode-row evaluations over {len(rows)} of {len(ctx)} rows of {args.workload} "
                       f"(longest first, ctx {int(ctx[rows].min())}-{int(ctx[rows].max())}, repeated to fill the "
                       f"budget); {el:.1f}s: indexer {stage[0]:.1f}s, sort {stage[1]:.1f}s, attention {stage[2]:.1f}s"}
@@ -397,7 +436,7 @@ def main():
                     help="untimed steps first; tens of milliseconds of work can leave the clocks below their "
                          "loaded level, so the default warms up for about 0.1 s")
     ap.add_argument("--workload", default="decode_b64_ctx16k_128k")
-    ap.add_argument("--flush-steps", type=int, default=5, help="extra steps timed after a 1 GiB cache flush")
+    ap.add_argument("--flush-steps", type=int, default=10, help="extra steps timed after a 1 GiB cache flush")
     ap.add_argument("--prefill-steps", type=int, default=2)
     ap.add_argument("--append-steps", type=int, default=20,
                     help="steps of the decode call that also appends each sequence's current token to the "
@@ -409,10 +448,10 @@ def main():
                     help="skip the run-time tuning of the attention split count (sa_decode_tune)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--other-workloads", default="none",
-                    help="comma-separated decode workloads also timed, e.g. decode_b32_ctx8k,decode_b4_ctx1m "
-                         "(supplementary, not the metric; off by default so that kernel traces of the default "
-                         "command hold the headline workload only)")
+    ap.add_argument("--no-peaks", action="store_true", help="skip the HBM / MFMA / LDS peak probe")
+    ap.add_argument("--other-workloads", default="decode_b32_ctx8k,decode_b4_ctx1m,decode_b64_ctx128k_full",
+                    help="comma-separated decode workloads also timed (supplementary lines, not the metric; "
+                         "'none' for the headline workload only)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM byte counters)")
@@ -457,57 +496,71 @@ def main():
         log("copy calibration: 3 elementwise copies of 1 GiB")
         del src, dst
 
-    w, dec = run_decode(args, torch, sa, synth)
-    sh = w["shape"]
-    B = len(w["context_lens"])
-    value = B / (dec["ms"] / 1e3)
-    alg = dec["alg"]
-    t_idx = dec["stages"].get("indexer")
+    peaks = None
+    if not args.no_peaks:
+        peaks = measured_peaks()
+        log(f"measured peaks: {peaks}")
+    # The supplementary measurements run first, so that the GPU clocks have
+    # long reached their loaded level when the headline steps are timed.
+    c = setup_decode(args.workload, torch, sa, synth)
+    w, sh, B, alg = c["w"], c["w"]["shape"], c["B"], c["alg"]
+    others = [x for x in args.other_workloads.split(",") if x and x != "none" and x != args.workload]
+    other_lines = {name: run_other_decode(args, torch, sa, synth, name) for name in others}
+    prefill_lines = {}
+    if not args.no_prefill:
+        prefill_lines["prefill"] = run_prefill(args, torch, sa, synth)
+        prefill_lines["prefill_varlen"] = run_prefill(args, torch, sa, synth, "prefill_varlen_8x4k")
+    supp = supplementary_decode(args, torch, sa, synth, c)
+    stages, ms_marked = time_stages(torch, sa, c, args.steps)
+    log(f"steps with an event after every kernel: {ms_marked:.3f} ms/step; stages " +
+        ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in stages.items()))
+    cold = time_flushed(torch, sa, c, args.flush_steps) if args.flush_steps > 0 else None
+
+    # the headline: W warm-up steps, then exactly K plain steps between two synchronisations
+    log(f"warmup {args.warmup} steps ({len(c['kernels'])} kernels per step: {', '.join(c['kernels'])})")
+    ms = time_back_to_back(torch, c["plain"], args.steps, args.warmup)
+    log(f"timed {args.steps} steps: {ms:.4f} ms/step")
+    value = B / (ms / 1e3)
+    t_idx = stages.get("indexer")
     roof = None
     if t_idx:
         achieved = alg["indexer_bytes"] / (t_idx / 1e3) / 1e9
         traffic = traffic_from_profiles(TRAFFIC_KERNEL + "/" + args.workload, 1)
         roof = {"bound": "hbm", "kernel": TRAFFIC_KERNEL, "achieved": round(achieved, 1),
                 "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": traffic, "avg_ms": round(t_idx, 5)}
+                "traffic": traffic, "avg_ms": round(t_idx, 5), "algorithmic_bytes": alg["indexer_bytes"]}
     line = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(dec["ms"], 4), "higher_is_better": True, "scaling": "weak",
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": args.workload, "batch": B, "context": "uniform[16384,131072]" if
                    args.workload == "decode_b64_ctx16k_128k" else int(w["context_lens"].max()),
                    "topk": sh.topk, "heads": sh.num_heads, "qk_dim": sh.qk_dim, "v_dim": sh.v_dim,
                    "indexer": f"{sh.idx_heads}x{sh.idx_dim}", "block_size": sh.block_size, "out": "fp32",
                    "parallelism": "single GPU"},
-        "hbm_gbps": round(alg["bytes"] / (dec["ms"] / 1e3) / 1e9, 1),
-        "hbm_frac": round(alg["bytes"] / (dec["ms"] / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+        "hbm_gbps": round(alg["bytes"] / (ms / 1e3) / 1e9, 1),
+        "hbm_frac": round(alg["bytes"] / (ms / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
         "algorithmic_bytes_per_step": alg["bytes"],
-        "stages_us": {k: round(v * 1e3, 2) for k, v in dec["stages"].items()},
-        "ms_per_step_with_stage_events": round(dec["ms_marked"], 4),
-        "cold_cache_ms_per_step": round(dec["cold_ms"], 4) if dec["cold_ms"] else None,
+        "stages_us": {k: round(v * 1e3, 2) for k, v in stages.items()},
+        "ms_per_step_with_stage_events": round(ms_marked, 4),
+        "cold_cache_ms_per_step": round(cold[0], 4) if cold else None,
         "roofline": roof,
     }
-    if dec.get("append_ms"):
-        # supplementary: the same step appending each sequence's current token first
-        line["decode_append"] = {"ms_per_step": round(dec["append_ms"], 4),
-                                 "tokens_per_s": round(B / (dec["append_ms"] / 1e3), 1),
-                                 "added_us": round((dec["append_ms"] - dec["ms"]) * 1e3, 2)}
-    if dec.get("tuned"):
-        # supplementary: the split count picked by sa_decode_tune on this batch
-        t = dec["tuned"]
-        line["decode_tuned"] = {"attn_splits": t["attn_splits"], "ms_per_step": round(t["ms"], 4),
-                                "tokens_per_s": round(B / (t["ms"] / 1e3), 1)}
-    if dec.get("blocks_ms"):
-        # supplementary: block-granular selection over the same batch
-        line["decode_blocks"] = {"ms_per_step": round(dec["blocks_ms"], 4),
-                                 "tokens_per_s": round(B / (dec["blocks_ms"] / 1e3), 1),
-                                 "kept_blocks": sh.topk // sh.block_size, "block_size": sh.block_size}
-    if not args.no_prefill:
-        line["prefill"] = run_prefill(args, torch, sa, synth)
-        line["prefill_varlen"] = run_prefill(args, torch, sa, synth, "prefill_varlen_8x4k")
-    others = [x for x in args.other_workloads.split(",") if x and x != "none" and x != args.workload]
-    if others:
-        line["other_workloads"] = run_other_decodes(args, torch, sa, synth, others)
+    t_att = stages.get("attention")
+    if t_att:
+        # the attention kernel against both of its bounds (its merge is a separate kernel)
+        line["attention_roofline"] = {
+            "kernel": "attend_kernel<576, 512, 2>", "avg_ms": round(t_att, 5),
+            "hbm_gbps": round(alg["attention_bytes"] / (t_att / 1e3) / 1e9, 1),
+            "hbm_frac": round(alg["attention_bytes"] / (t_att / 1e3) / 1e9 / HBM_PEAK_GBPS, 4),
+            "mfma_tflops": round(alg["attention_flops"] / (t_att / 1e3) / 1e12, 1),
+            "mfma_frac": round(alg["attention_flops"] / (t_att / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4)}
+    if peaks:
+        line["measured_peaks"] = peaks
+    line.update(supp)
+    line.update(prefill_lines)
+    if other_lines:
+        line["other_workloads"] = other_lines
     if not args.no_cpu_baseline:
         log(f"cpu baseline: oracle on up to {args.cpu_seconds:.0f}s of rows")
         line["cpu_baseline"] = cpu_baseline(args, w)

@@ -38,5 +38,22 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+PROBE = os.path.join(HERE, "peak_probe")
+
+
+def build_probe() -> str:
+    """The peak-probe executable the benchmark runs for its roofline figures."""
+    tmp = PROBE + ".tmp"
+    cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", os.path.join(CSRC, "peak_probe.hip"), "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError("hipcc failed to build peak_probe")
+    os.replace(tmp, PROBE)
+    return PROBE
+
+
 if __name__ == "__main__":
     print(build(verbose="-v" in sys.argv))
+    print(build_probe())

@@ -100,6 +100,10 @@ WORKLOADS = {
                                    ctx_uniform=(16384, 131072), seed=1003),
     # long-context decode, batch 4, each context 1,048,576.
     "decode_b4_ctx1m": Spec("decode_b4_ctx1m", "decode", MLA, batch=4, ctx=[1 << 20] * 4, seed=1004),
+    # decode, batch 64, every context 131072: the mixed-length batch at its
+    # longest context (a labelled supplementary of the 128K metric)
+    "decode_b64_ctx128k_full": Spec("decode_b64_ctx128k_full", "decode", MLA, batch=64, ctx=[1 << 17] * 64,
+                                    seed=1006),
     # chunked prefill of 8 sequences in one call: 4096 new rows each after cached
     # prefixes of 0, 4096, ..., 28672 tokens (the same 32768 rows and causal
     # pairs as the single 32K prefill, spread over 8 block-table rows).

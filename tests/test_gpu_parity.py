@@ -148,6 +148,18 @@ CASES = {
     # 16 lanes of a wave while the split weights sit in lanes 0..31
     "decode_v64_splits": lambda: synth.small_decode("decode_v64_splits", V64, [3000, 2500, 4000, 2049, 5000, 2100],
                                                     seed=115),
+    # long rows in a small batch, ragged ends (16K to 128K keys, one of 8192 + 1)
+    "decode_long_rows": lambda: synth.small_decode("decode_long_rows", V64,
+                                                   [16_384, 131_072, 40_001, 2048, 2049, 1, 0, 24_607, 8193], seed=117),
+    "decode_long_int1": lambda: synth.small_decode("decode_long_int1", V64, [70_000, 16_385, 64, 65, 33_333],
+                                                   seed=118, idx_int_max=1),
+    # every score zero: the threshold bin holds the whole row, more than the
+    # candidate list takes, so each row goes the radix path and keeps its
+    # lowest positions
+    "decode_long_all_ties": lambda: synth.small_decode("decode_long_all_ties", V64, [70_000, 16_385, 64, 65, 33_333],
+                                                       seed=119, topk=64, idx_int_max=0),
+    "decode_all_ties": lambda: synth.small_decode("decode_all_ties", V64, [100, 5000, 9000, 3], seed=120, topk=64,
+                                                  idx_int_max=0),
 }
 
 
@@ -269,6 +281,8 @@ APPEND_CASES = {
     "append_decode_b32_ctx8k": lambda: synth.WORKLOADS["decode_b32_ctx8k"],
     # longer than 262144 keys: the many-workgroup top-k stores the new rows
     "append_long_mb": lambda: synth.small_decode("append_long", V64, [300_001, 262_145, 1, 0], seed=124),
+    # long rows in a small batch
+    "append_long_rows": lambda: synth.small_decode("append_long_rows", V64, [40_000, 17_000, 5, 0], seed=125),
 }
 
 
