@@ -30,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0          # MI355X HBM3E
+TOPK_PATHS = {0: "default", 1: "threshold", 2: "onepass_u2", 3: "onepass_u4"}
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16
 METRIC = "decode tokens/s + HBM GB/s at 128K ctx, top-k=2048; prefill query-tokens/s"
 
@@ -180,13 +181,15 @@ def supplementary_decode(args, torch, sa, synth, c):
         res["decode_append"] = {"ms_per_step": round(ms_app, 4), "tokens_per_s": round(B / (ms_app / 1e3), 1),
                                 "added_us": round((ms_app - ms_plain) * 1e3, 2)}
     if args.tune:
-        splits, tune_us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=10)
-        wst = torch.empty(sa.decode_workspace_size_cfg(p, B, max_ctx, splits), dtype=torch.uint8, device="cuda")
+        splits, path, tune_us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=10)
+        wst = torch.empty(sa.decode_workspace_size_cfg(p, B, max_ctx, splits, path), dtype=torch.uint8,
+                          device="cuda")
         cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"],
-                                                workspace=wst, outputs=outs)
+                                                topk_path=path, workspace=wst, outputs=outs)
         ms = time_back_to_back(torch, cfg, 20, 20)
-        log(f"tuned: {splits} attention splits per row, {ms:.3f} ms/step (tuner's own mean {tune_us:.1f} us)")
-        res["decode_tuned"] = {"attn_splits": splits, "ms_per_step": round(ms, 4),
+        log(f"tuned: {splits} attention splits per row, top-k path {TOPK_PATHS[path]}, {ms:.3f} ms/step "
+            f"(tuner's own mean {tune_us:.1f} us)")
+        res["decode_tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "ms_per_step": round(ms, 4),
                                "tokens_per_s": round(B / (ms / 1e3), 1)}
         del wst
     if args.blocks_steps > 0:
@@ -221,13 +224,13 @@ def run_other_decode(args, torch, sa, synth, name):
         ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in stages.items()))
     if args.tune:
         p, d = c["p"], c["d"]
-        splits, _ = sa.decode_tune(p, d["cache"], c["max_ctx"], d["q"], d["idx_q"], d["idx_w"], reps=10)
-        wst = torch.empty(sa.decode_workspace_size_cfg(p, c["B"], c["max_ctx"], splits), dtype=torch.uint8,
+        splits, path, _ = sa.decode_tune(p, d["cache"], c["max_ctx"], d["q"], d["idx_q"], d["idx_w"], reps=10)
+        wst = torch.empty(sa.decode_workspace_size_cfg(p, c["B"], c["max_ctx"], splits, path), dtype=torch.uint8,
                           device="cuda")
         cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], c["max_ctx"], splits, d["q"], d["idx_q"],
-                                                d["idx_w"], workspace=wst, outputs=c["outs"])
+                                                d["idx_w"], topk_path=path, workspace=wst, outputs=c["outs"])
         mt = time_back_to_back(torch, cfg, 20, 20)
-        line["tuned"] = {"attn_splits": splits, "ms_per_step": round(mt, 4),
+        line["tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "ms_per_step": round(mt, 4),
                          "tokens_per_s": round(c["B"] / (mt / 1e3), 1)}
     del c
     torch.cuda.empty_cache()
@@ -445,7 +448,7 @@ def main():
                     help="steps of block-granular decode (sparse_attn_decode_blocks, k / block_size blocks per "
                          "row) over the same batch")
     ap.add_argument("--no-tune", dest="tune", action="store_false",
-                    help="skip the run-time tuning of the attention split count (sa_decode_tune)")
+                    help="skip the run-time tuning of the attention split count and top-k path (sa_decode_tune)")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the HBM / MFMA / LDS peak probe")

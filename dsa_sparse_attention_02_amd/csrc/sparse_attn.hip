@@ -16,6 +16,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -38,6 +39,10 @@ constexpr int kTargetAttnBlocks = 256;        // one attention workgroup per CU 
 // costs more than the extra workgroups gain (batches of 1, 2 and 4 at long
 // contexts ran 3-8% faster at 22 splits than at 32 or 64).
 constexpr int kMaxDefaultSplits = 24;
+#ifndef SA_TOPK_ONEPASS_MIN_PER_K
+#define SA_TOPK_ONEPASS_MIN_PER_K 8
+#endif
+constexpr int kOnePassMinPerK = SA_TOPK_ONEPASS_MIN_PER_K;  // decode rows of >= this many keys per kept key: one-pass top-k
 constexpr int kCUs = 256;                     // compute units of an MI355X
 #ifndef SA_SCAN_BLOCKS_PER_CU
 #define SA_SCAN_BLOCKS_PER_CU 1
@@ -109,13 +114,15 @@ struct DecodePlan {
     int splits, tokens_per_split, scan_blocks;
     size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
+    int topk_path;  // SA_TOPK_*: which decode rows take the one-pass top-k, and its unroll
 };
 
 // want_splits > 0 asks for that many attention splits per row (clamped to
 // what k allows); 0 takes one attention workgroup per CU over the batch
-DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_splits = 0)
+DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_splits = 0, int topk_path = 0)
 {
     DecodePlan d{};
+    d.topk_path = topk_path;
     d.score_stride = round_up(max_ctx > 0 ? max_ctx : 1, 64);
     const int k = p->topk;
     const int groups = attn_launch(p).groups;  // attention workgroups per (row, split)
@@ -162,6 +169,7 @@ struct PrefillPlan {
     int attn_chunk_rows;     // rows per attention launch when splits > 1
     size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
+    int topk_path;  // SA_TOPK_*: which decode rows take the one-pass top-k, and its unroll
 };
 
 // num_rows: query rows of the call; max_ctx: the most keys any row sees;
@@ -519,8 +527,16 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
         hipLaunchKernelGGL(topk_mb_emit_kernel, grid, dim3(kTopkThreads), 0, st, scores, d.score_stride, cl, p->topk,
                            mst, counts, d.mb_chunks, topk_idx);
     } else {
-        hipLaunchKernelGGL(topk_rows_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, 0, c->context_lens, SeqMap{}, p->topk, topk_idx, ap);
+        // rows of at least onepass_min keys take the one-pass top-k
+        const int k = p->topk;
+        const int onepass_min = d.topk_path == SA_TOPK_THRESHOLD ? INT_MAX
+                                : d.topk_path == SA_TOPK_DEFAULT ? kOnePassMinPerK * k : 0;
+        if (d.topk_path == SA_TOPK_ONEPASS_U4)
+            hipLaunchKernelGGL(topk_decode_kernel<4>, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
+                               mm, d.mm_stride, c->context_lens, k, onepass_min, topk_idx, ap);
+        else
+            hipLaunchKernelGGL(topk_decode_kernel<2>, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
+                               mm, d.mm_stride, c->context_lens, k, onepass_min, topk_idx, ap);
     }
     if (mk) mk->mark();
 }
@@ -794,12 +810,13 @@ sa_status sparse_attn_attend_decode(const sa_params *p, const sa_paged_cache *c,
 static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_t batch, int32_t max_ctx,
                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
                              float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk,
-                             const void *new_kv = nullptr, const void *new_idx_k = nullptr, int want_splits = 0)
+                             const void *new_kv = nullptr, const void *new_idx_k = nullptr, int want_splits = 0,
+                             int topk_path = 0)
 {
     sa_status s = check_decode(p, c, batch, max_ctx, true, true);
     if (s != SA_OK) return s;
     if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
-    const DecodePlan d = plan_decode(p, batch, max_ctx, want_splits);
+    const DecodePlan d = plan_decode(p, batch, max_ctx, want_splits, topk_path);
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     clear_hip_error();
@@ -976,6 +993,8 @@ sa_status sparse_attn_prefill_profiled(const sa_params *p, const sa_paged_cache 
 static sa_status check_cfg(const sa_decode_config *cfg)
 {
     if (cfg && (cfg->attn_splits < 0 || cfg->attn_splits > 1024)) return SA_ERR_SHAPE;
+    if (cfg && (cfg->topk_path < SA_TOPK_DEFAULT || cfg->topk_path > SA_TOPK_ONEPASS_U4)) return SA_ERR_SHAPE;
+    if (cfg && (cfg->reserved[0] != 0 || cfg->reserved[1] != 0)) return SA_ERR_SHAPE;
     return SA_OK;
 }
 
@@ -999,7 +1018,7 @@ sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *c, in
     const sa_status s = check_cfg(cfg);
     if (s != SA_OK) return s;
     return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
-                       nullptr, nullptr, nullptr, cfg ? cfg->attn_splits : 0);
+                       nullptr, nullptr, nullptr, cfg ? cfg->attn_splits : 0, cfg ? cfg->topk_path : 0);
 }
 
 // The split counts the tuner tries: every count the plan can realise (k is
@@ -1044,26 +1063,40 @@ sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *c, int32_t ba
         if (e0) (void)hipEventDestroy(e0);
         return SA_ERR_HIP;
     }
-    float best_t = INFINITY;
-    int best_sp = 0;
-    s = SA_OK;
-    for (int sp : tune_candidates(p, batch, max_ctx)) {
-        // one untimed call, then reps timed back to back
-        for (int i = 0; i <= reps && s == SA_OK; ++i) {
-            if (i == 1 && hipEventRecord(e0, st) != hipSuccess) s = SA_ERR_HIP;
-            if (s == SA_OK)
-                s = decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace,
-                                workspace_bytes, stream, nullptr, nullptr, nullptr, sp);
+    // one untimed call, then reps timed back to back; microseconds per call
+    auto time_cfg = [&](int sp, int path, float &us) -> sa_status {
+        sa_status r = SA_OK;
+        for (int i = 0; i <= reps && r == SA_OK; ++i) {
+            if (i == 1 && hipEventRecord(e0, st) != hipSuccess) r = SA_ERR_HIP;
+            if (r == SA_OK)
+                r = decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                                workspace_bytes, stream, nullptr, nullptr, nullptr, sp, path);
         }
         float ms = 0.0f;
-        if (s == SA_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+        if (r == SA_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
                            hipEventElapsedTime(&ms, e0, e1) != hipSuccess))
-            s = SA_ERR_HIP;
-        if (s != SA_OK) break;
-        const float us = ms * 1000.0f / reps;
+            r = SA_ERR_HIP;
+        us = ms * 1000.0f / reps;
+        return r;
+    };
+    // the split count under the default top-k, then the top-k path under that count
+    float best_t = INFINITY;
+    int best_sp = 0, best_path = SA_TOPK_DEFAULT;
+    s = SA_OK;
+    for (int sp : tune_candidates(p, batch, max_ctx)) {
+        float us = 0.0f;
+        if ((s = time_cfg(sp, SA_TOPK_DEFAULT, us)) != SA_OK) break;
         if (us < best_t) {
             best_t = us;
             best_sp = sp;
+        }
+    }
+    for (int path = SA_TOPK_THRESHOLD; path <= SA_TOPK_ONEPASS_U4 && s == SA_OK; ++path) {
+        float us = 0.0f;
+        if ((s = time_cfg(best_sp, path, us)) != SA_OK) break;
+        if (us < best_t) {
+            best_t = us;
+            best_path = path;
         }
     }
     (void)hipEventDestroy(e0);
@@ -1071,6 +1104,7 @@ sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *c, int32_t ba
     if (s != SA_OK) return s;
     *best = sa_decode_config{};
     best->attn_splits = best_sp;
+    best->topk_path = best_path;
     if (best_us) *best_us = best_t;
     return SA_OK;
 }

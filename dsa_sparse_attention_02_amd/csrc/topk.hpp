@@ -202,8 +202,18 @@ __device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int3
     const int w0 = tid * per, w1 = min(words, w0 + per);
     uint32_t cnt = 0;
     for (int w = w0; w < w1; ++w) cnt += __popc(sh.bitmap[w]);
-    uint32_t tot;
-    uint32_t pos = block_inclusive_scan(cnt, sh.wsum, &tot) - cnt;
+    // exclusive block scan of cnt with one barrier (wsum is not used after this)
+    const int lane = tid & 63, wave = tid >> 6;
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t x = __shfl_up(incl, d);
+        if (lane >= d) incl += x;
+    }
+    if (lane == 63) sh.wsum[wave] = incl;
+    __syncthreads();
+    uint32_t pos = incl - cnt;
+    for (int w = 0; w < wave; ++w) pos += sh.wsum[w];
     for (int w = w0; w < w1; ++w) {
         uint32_t bits = sh.bitmap[w];
         while (bits) {
@@ -215,43 +225,13 @@ __device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int3
     }
 }
 
-// Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
-// else n = p + 1 for a prefill row at position p, found through the piece map
-// (rows counted from the launch's first row).  tile_mm holds
-// score ranges (min, max) at row stride mm_stride: one per 32-key tile
-// (mm_per_row == 0) or mm_per_row entries covering the whole row.
-__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
-    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
-    int mm_per_row, const int32_t *__restrict__ ctx_lens, const SeqMap rows_map, int k, int32_t *__restrict__ out,
-    const AppendArgs ap)
+// The row's score range [lo, hi] from the (min, max) of its nmm tiles, in every
+// thread.
+__device__ __forceinline__ void row_range(TopkShared &sh, const f32x2 *__restrict__ mm, int nmm, float &lo, float &hi)
 {
-    __shared__ TopkShared sh;
-    const int r = blockIdx.x;
-    append_rows(ap, r, threadIdx.x, kTopkThreads);  // (decode row r = sequence r; before the attention reads it)
-    int n;
-    if (ctx_lens) {
-        n = ctx_lens[r];
-    } else {
-        const int pc = map_piece(rows_map, r);
-        n = rows_map.pos0[pc] + (r - rows_map.row0[pc]) + 1;
-    }
-    int32_t *o = out + (int64_t)r * k;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    if (n <= k) {
-        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
-        return;
-    }
-    const float *sr = scores + (int64_t)r * score_stride;
-    if (n > kBitmapKeys) {
-        topk_radix_row(sh, sr, n, k, o);
-        return;
-    }
-    const int n4 = n & ~3;
-
-    // 1. score range of the row
-    float lo = INFINITY, hi = -INFINITY;
-    const f32x2 *mm = tile_mm + (int64_t)r * mm_stride;
-    const int nmm = mm_per_row ? mm_per_row : (n + 31) / 32;
+    lo = INFINITY;
+    hi = -INFINITY;
     for (int t = tid; t < nmm; t += kTopkThreads) {
         const f32x2 v = mm[t];
         lo = fminf(lo, v[0]);
@@ -266,7 +246,6 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
         sh.red[0][wv] = lo;
         sh.red[1][wv] = hi;
     }
-    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
     __syncthreads();
     lo = sh.red[0][0];
     hi = sh.red[1][0];
@@ -274,13 +253,88 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
         lo = fminf(lo, sh.red[0][w]);
         hi = fmaxf(hi, sh.red[1][w]);
     }
-    const float span = hi - lo;
-    const float scale = (span > 0.0f && span < INFINITY) ? (float)kBins / span : 0.0f;
-    // monotone non-decreasing in the score (all steps are monotone in fp32)
-    auto bin_of = [&](float x) -> uint32_t {
-        const float f = fminf(fmaxf((x - lo) * scale, 0.0f), (float)(kBins - 1));
-        return (uint32_t)f;
-    };
+    __syncthreads();  // red is reused
+}
+
+// kBins equal-width bins over [lo, hi]: monotone non-decreasing in the score
+// (every step is monotone in fp32); a zero or non-finite span puts every score
+// in bin 0.
+struct ScoreBins {
+    float lo, scale;
+    __device__ __forceinline__ ScoreBins(float lo_, float hi_)
+    {
+        lo = lo_;
+        const float span = hi_ - lo_;
+        scale = (span > 0.0f && span < INFINITY) ? (float)kBins / span : 0.0f;
+    }
+    __device__ __forceinline__ uint32_t operator()(float x) const
+    {
+        return (uint32_t)fminf(fmaxf((x - lo) * scale, 0.0f), (float)(kBins - 1));
+    }
+};
+
+// (order-preserving key, position) as one 64-bit word: larger means kept first
+__device__ __forceinline__ uint64_t cand_word(float x, int i)
+{
+    return ((uint64_t)score_key(x) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+}
+
+// 4. The need best of the m candidates in sh.cand, by (key, -position)
+// descending, join the bitmap; 5. the bitmap's positions are written in order.
+// Up to 64 candidates: wave 0 ranks each against all (lane i holds candidate
+// i); more: a bitonic sort over the block.
+__device__ void resolve_emit(TopkShared &sh, int m, uint32_t need, int words, int k, int32_t *__restrict__ o)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (m <= 64) {  // block-uniform
+        if (wv == 0) {
+            const uint64_t mine = lane < m ? sh.cand[lane] : 0;
+            int rank = 0;  // candidates ahead of mine (keys are distinct: positions differ)
+            for (int j = 0; j < m; ++j) rank += __shfl(mine, j) > mine;
+            if (lane < m && rank < (int)need) {
+                const int pos = (int)(0xFFFFFFFFu - (uint32_t)mine);
+                atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
+            }
+        }
+        __syncthreads();
+        topk_emit(sh, words, k, o, tid);
+        return;
+    }
+    int P = 1;
+    while (P < m) P <<= 1;
+    for (int i = m + tid; i < P; i += kTopkThreads) sh.cand[i] = 0;
+    __syncthreads();
+    for (int size = 2; size <= P; size <<= 1)
+        for (int j = size >> 1; j > 0; j >>= 1) {
+            for (int i = tid; i < P / 2; i += kTopkThreads) {
+                const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b = a | j;
+                const uint64_t x = sh.cand[a], y = sh.cand[b];
+                const bool desc = (a & size) == 0;  // the final pass (size == P) sorts descending
+                if (desc ? (x < y) : (x > y)) {
+                    sh.cand[a] = y;
+                    sh.cand[b] = x;
+                }
+            }
+            __syncthreads();
+        }
+    for (int i = tid; i < (int)need; i += kTopkThreads) {
+        const int pos = (int)(0xFFFFFFFFu - (uint32_t)sh.cand[i]);
+        atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
+    }
+    __syncthreads();
+    topk_emit(sh, words, k, o, tid);
+}
+
+// Steps 2-5 of the threshold path for a row of n keys (k < n <= kBitmapKeys)
+// whose score range is [lo, hi].
+__device__ void threshold_row(TopkShared &sh, const float *__restrict__ sr, int n, int k, int32_t *__restrict__ o,
+                              float lo, float hi)
+{
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n4 = n & ~3;
+    const ScoreBins bin_of(lo, hi);
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
 
     // 2. histogram of the bins (four 16-byte loads in flight per thread)
     constexpr int U = 4;
@@ -328,8 +382,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
                 const uint32_t rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
                 const uint32_t slot = base + rank;
-                if (slot < (uint32_t)kCandCap)
-                    sh.cand[slot] = ((uint64_t)score_key(x) << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)i);
+                if (slot < (uint32_t)kCandCap) sh.cand[slot] = cand_word(x, i);
             }
         }
     };
@@ -359,48 +412,335 @@ __global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
             }
         }
     __syncthreads();
+    resolve_emit(sh, (int)m, need, words, k, o);
+}
 
-    // 4. the need best candidates, by (key, -position) descending.  Up to 64 of
-    // them: wave 0 ranks each against all (lane i holds candidate i); more: a
-    // bitonic sort over the block.
-    if (m <= 64) {  // block-uniform
-        if (wv == 0) {
-            const uint64_t mine = lane < (int)m ? sh.cand[lane] : 0;
-            int rank = 0;  // candidates ahead of mine (keys are distinct: positions differ)
-            for (int j = 0; j < (int)m; ++j) rank += __shfl(mine, j) > mine;
-            if (lane < (int)m && rank < (int)need) {
-                const int pos = (int)(0xFFFFFFFFu - (uint32_t)mine);
-                atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
-            }
-        }
-        __syncthreads();
-        topk_emit(sh, words, k, o, tid);
+// Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
+// else n = p + 1 for a prefill row at position p, found through the piece map
+// (rows counted from the launch's first row).  tile_mm holds
+// score ranges (min, max) at row stride mm_stride: one per 32-key tile
+// (mm_per_row == 0) or mm_per_row entries covering the whole row.
+__global__ __launch_bounds__(kTopkThreads) void topk_rows_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
+    int mm_per_row, const int32_t *__restrict__ ctx_lens, const SeqMap rows_map, int k, int32_t *__restrict__ out,
+    const AppendArgs ap)
+{
+    __shared__ TopkShared sh;
+    const int r = blockIdx.x;
+    append_rows(ap, r, threadIdx.x, kTopkThreads);  // (decode row r = sequence r; before the attention reads it)
+    int n;
+    if (ctx_lens) {
+        n = ctx_lens[r];
+    } else {
+        const int pc = map_piece(rows_map, r);
+        n = rows_map.pos0[pc] + (r - rows_map.row0[pc]) + 1;
+    }
+    int32_t *o = out + (int64_t)r * k;
+    const int tid = threadIdx.x;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
         return;
     }
-    int P = 1;
-    while (P < (int)m) P <<= 1;
-    for (int i = (int)m + tid; i < P; i += kTopkThreads) sh.cand[i] = 0;
-    __syncthreads();
-    for (int size = 2; size <= P; size <<= 1)
-        for (int j = size >> 1; j > 0; j >>= 1) {
-            for (int i = tid; i < P / 2; i += kTopkThreads) {
-                const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b = a | j;
-                const uint64_t x = sh.cand[a], y = sh.cand[b];
-                const bool desc = (a & size) == 0;  // the final pass (size == P) sorts descending
-                if (desc ? (x < y) : (x > y)) {
-                    sh.cand[a] = y;
-                    sh.cand[b] = x;
-                }
-            }
-            __syncthreads();
+    const float *sr = scores + (int64_t)r * score_stride;
+    if (n > kBitmapKeys) {
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+    // 1. score range of the row
+    float lo, hi;
+    row_range(sh, tile_mm + (int64_t)r * mm_stride, mm_per_row ? mm_per_row : (n + 31) / 32, lo, hi);
+    threshold_row(sh, sr, n, k, o, lo, hi);
+}
+
+// ------------------------------------------------- one pass for decode rows --
+// Decode rows take one workgroup each, so a batch of long rows keeps one
+// workgroup per row busy through both passes of the threshold path; there the
+// per-key work (a histogram atomic per key, then a ballot per key) and the
+// latency of each dependent step set the time.  This path reads each row once
+// and does per-key work only on a small candidate set:
+//  a. Estimate: the row's tile ranges and the keys of every 16th 32-key tile
+//     (1/16 of the row) are loaded together; the sample is histogrammed into
+//     the row's 2048 bins, and the bound T_f is set at the lower edge of the
+//     bin above which the sample holds about 1.25 k/16 + 16 keys.
+//  b. Gather: one pass over the row (GR 4 KB rounds per wave in flight)
+//     writes the position of every key >= T_f to LDS (kCompCap at most).
+//  c. If at least k and at most kCompCap keys were gathered, the top k of the
+//     row are the top k of the gathered set (its k-th best key is >= T_f, so
+//     every kept key was gathered): their scores are read back, and bins over
+//     [T_f, hi], a suffix scan, a bitmap of the keys above the threshold bin
+//     and a resolution of that bin's candidates give them, as in the threshold
+//     path.  Otherwise (a sample that misjudged the row) the row takes the
+//     threshold path from its scores.
+// On MI355X a workgroup reads a row's scores at about 25 bytes per clock
+// however many loads it keeps in flight, so this path gains on long rows with
+// a small k / n (one pass instead of two) and loses on short ones (its fixed
+// steps); which rows take it is a run-time choice (onepass_min).
+// Either way the kept set is the exact top-k with the lowest-position
+// tie-break; the sample only decides how much work finds it.
+constexpr int kCompCap = 8192;  // positions gathered in LDS
+
+constexpr int kSampleGap = 512;   // keys from one sample tile to the next
+
+struct TopkGatherShared {
+    TopkShared sh;
+    int32_t cp[kCompCap];
+    uint32_t ngather, ncand;
+};
+
+// pick_bin over kBins bins by wave 0 alone (lane l sums the 32 bins
+// [kBins - 32 (l + 1), kBins - 32 l), a wave scan runs from the top bins down),
+// then one barrier.  need <= the histogram's total.
+__device__ __forceinline__ void pick_bin_wave(TopkShared &sh, uint32_t need, uint32_t &bin, uint32_t &above,
+                                              uint32_t &count)
+{
+    static_assert(kBins == 64 * 32, "32 bins per lane");
+    const int tid = threadIdx.x, lane = tid & 63;
+    if (tid < 64) {
+        const int base = kBins - 32 * (lane + 1);
+        uint32_t c[32];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(&sh.hist[base + 4 * q]);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) c[4 * q + e] = x[e];
         }
-    for (int i = tid; i < (int)need; i += kTopkThreads) {
-        const int pos = (int)(0xFFFFFFFFu - (uint32_t)sh.cand[i]);
-        atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
+        uint32_t sum = 0;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) sum += c[e];
+        uint32_t incl = sum;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const uint32_t x = __shfl_up(incl, d);
+            if (lane >= d) incl += x;
+        }
+        if (lane == 0) {
+            sh.pick[0] = 0;
+            sh.pick[1] = 0;
+            sh.pick[2] = 0;
+        }
+        uint32_t ab = incl - sum;
+        if (ab < need && incl >= need) {  // (one lane)
+            bool found = false;
+#pragma unroll
+            for (int e = 31; e >= 0; --e) {
+                if (!found && ab + c[e] >= need) {
+                    sh.pick[0] = (uint32_t)(base + e);
+                    sh.pick[1] = ab;
+                    sh.pick[2] = c[e];
+                    found = true;
+                }
+                ab += c[e];
+            }
+        }
     }
     __syncthreads();
+    bin = sh.pick[0];
+    above = sh.pick[1];
+    count = sh.pick[2];
+}
 
-    topk_emit(sh, words, k, o, tid);
+// Rows of fewer than onepass_min keys take the threshold path.  GR: gather
+// rounds whose loads are in flight together per wave (the loop's unroll).
+template <int GR>
+__global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
+    const int32_t *__restrict__ ctx_lens, int k, int onepass_min, int32_t *__restrict__ out, const AppendArgs ap)
+{
+    __shared__ TopkGatherShared g;
+    TopkShared &sh = g.sh;
+    const int r = blockIdx.x;
+    append_rows(ap, r, threadIdx.x, kTopkThreads);  // (row r = sequence r; before the attention reads it)
+    const int n = ctx_lens[r];
+    int32_t *o = out + (int64_t)r * k;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (n <= k) {
+        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const float *sr = scores + (int64_t)r * score_stride;
+    if (n > kBitmapKeys) {
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+    const f32x2 *mm = tile_mm + (int64_t)r * mm_stride;
+    const int nmm = (n + 31) / 32;
+    if (n < onepass_min || n <= 2 * k || 2 * k > kCompCap) {  // (also where the gathered set would be large)
+        float lo, hi;
+        row_range(sh, mm, nmm, lo, hi);
+        threshold_row(sh, sr, n, k, o, lo, hi);
+        return;
+    }
+
+    // a. range and sample.  Sample tile j holds keys [512 j, 512 j + 32);
+    // thread t takes 4 of them in tile (t >> 3) + 128 q, q < 4 (512 tiles cover
+    // kBitmapKeys).  The first four tile ranges and the sample pieces of every
+    // thread load together.  (A score row is allocated to a multiple of 64
+    // keys, n64 here, so a 16-byte piece that starts below n is read whole;
+    // keys at n and beyond are never counted.)
+    const int wvu = __builtin_amdgcn_readfirstlane(wv);  // (wave-uniform, in a scalar register)
+    const int n64 = (n + 63) & ~63;
+    static_assert(4 * (kTopkThreads / 8) * kSampleGap >= kBitmapKeys, "one batch of sample loads");
+    const int ns = (n + kSampleGap - 1) / kSampleGap;
+    const int sx = 4 * (tid & 7);
+    f32x2 mv[4];
+    f32x4 sv[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int t = tid + kTopkThreads * q;
+        mv[q] = t < nmm ? mm[t] : f32x2{INFINITY, -INFINITY};
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {  // (tiles past the last are read as the last one, and not counted)
+        const int j = min((tid >> 3) + (kTopkThreads / 8) * q, ns - 1);
+        sv[q] = *reinterpret_cast<const f32x4 *>(sr + kSampleGap * j + sx);
+    }
+    float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        lo = fminf(lo, mv[q][0]);
+        hi = fmaxf(hi, mv[q][1]);
+    }
+    for (int t = tid + 4 * kTopkThreads; t < nmm; t += kTopkThreads) {  // (rows over 131072 keys)
+        const f32x2 v = mm[t];
+        lo = fminf(lo, v[0]);
+        hi = fmaxf(hi, v[1]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d));
+        hi = fmaxf(hi, __shfl_xor(hi, d));
+    }
+    if (lane == 0) {
+        sh.red[0][wv] = lo;
+        sh.red[1][wv] = hi;
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    if (tid == 0) {
+        g.ngather = 0;
+        g.ncand = 0;
+    }
+    __syncthreads();
+    lo = sh.red[0][0];
+    hi = sh.red[1][0];
+    for (int w = 1; w < kTopkWaves; ++w) {
+        lo = fminf(lo, sh.red[0][w]);
+        hi = fmaxf(hi, sh.red[1][w]);
+    }
+    const ScoreBins bin_of(lo, hi);
+    auto sample_count = [&](const f32x4 &v, int j) {
+        if (j < ns) {
+            const int i0 = kSampleGap * j + sx;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (i0 + e < n) atomicAdd(&sh.hist[bin_of(v[e])], 1u);
+        }
+    };
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sample_count(sv[q], (tid >> 3) + (kTopkThreads / 8) * q);
+    __syncthreads();
+    // keys in the sample: 32 per sample tile, the last one cut at n
+    const int nsamp = 32 * (ns - 1) + min(32, n - kSampleGap * (ns - 1));
+    const uint32_t want = (uint32_t)min(nsamp, (int)ceilf(1.25f * (float)k * (float)nsamp / (float)n) + 16);
+    uint32_t b, above, cnt;
+    pick_bin_wave(sh, want, b, above, cnt);
+    const float tf = bin_of.scale > 0.0f ? lo + (float)b / bin_of.scale : lo;
+
+    // b. gather the positions of the keys >= T_f.  Round c covers keys
+    // [1024 c, 1024 c + 1024): lane l the 16-byte pieces at 4 l + 256 u
+    // (u < 4).  A wave scan of the lanes' counts (five ballots) places them;
+    // one LDS atomic per round reserves the wave's slots.  GR rounds' loads are
+    // in flight per wave.
+    const int nch = (n + 1023) / 1024;
+    auto load = [&](f32x4 (&v)[4], int c) {  // (pieces past the row's last one re-read it: never gathered)
+        const int i0 = 1024 * c + 4 * lane;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4 *>(sr + min(i0 + 256 * u, n64 - 4));
+    };
+    auto gather_round = [&](const f32x4 (&v)[4], int c, auto full) {
+        const int i0 = 1024 * c + 4 * lane;
+        uint32_t bits = 0;  // bit 4 u + e: key i0 + 256 u + e is gathered
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                bits |= (v[u][e] >= tf && (decltype(full)::value || i0 + 256 * u + e < n)) ? 1u << (4 * u + e) : 0u;
+        const uint32_t cnt = (uint32_t)__popc(bits);  // <= 16: five bits
+        uint32_t pre = 0, tot = 0;
+#pragma unroll
+        for (int bt = 0; bt < 5; ++bt) {
+            const uint64_t mb = __ballot((cnt >> bt) & 1u);
+            pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u)) << bt;
+            tot += (uint32_t)__popcll(mb) << bt;
+        }
+        if (tot == 0) return;  // (wave-uniform)
+        uint32_t base = 0;
+        if (lane == 0) base = atomicAdd(&g.ngather, tot);
+        uint32_t slot = (uint32_t)__builtin_amdgcn_readfirstlane((int)base) + pre;
+        while (bits) {
+            const int j = __builtin_ctz(bits);
+            bits &= bits - 1;
+            if (slot < (uint32_t)kCompCap) g.cp[slot] = i0 + 256 * (j >> 2) + (j & 3);
+            ++slot;
+        }
+    };
+    for (int c = wvu; c < nch; c += GR * kTopkWaves) {
+        f32x4 v[GR][4];
+#pragma unroll
+        for (int q = 0; q < GR; ++q)  // (a round past the last re-reads the last one, and is not gathered)
+            load(v[q], min(c + q * kTopkWaves, nch - 1));
+#pragma unroll
+        for (int q = 0; q < GR; ++q) {
+            const int cq = c + q * kTopkWaves;
+            if (cq >= nch) break;  // (wave-uniform)
+            if (1024 * cq + 1024 <= n) gather_round(v[q], cq, std::true_type{});
+            else gather_round(v[q], cq, std::false_type{});
+        }
+    }
+    __syncthreads();
+    const int mc = (int)g.ngather;
+    if (mc < k || mc > kCompCap) {  // (block-uniform) the sample misjudged the row
+        threshold_row(sh, sr, n, k, o, lo, hi);
+        return;
+    }
+
+    // c. the top k of the gathered keys
+    constexpr int G = kCompCap / kTopkThreads;
+    float xv[G];
+    int pv[G];
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        const int i = tid + kTopkThreads * q;
+        pv[q] = i < mc ? g.cp[i] : 0;
+        xv[q] = i < mc ? sr[pv[q]] : 0.0f;
+    }
+    const ScoreBins bin2(tf > lo ? tf : lo, hi);
+    const int words = (n + 31) / 32;
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    for (int i = tid; i < words; i += kTopkThreads) sh.bitmap[i] = 0;
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < G; ++q)
+        if (tid + kTopkThreads * q < mc) atomicAdd(&sh.hist[bin2(xv[q])], 1u);
+    __syncthreads();
+    uint32_t tbin, m;
+    pick_bin_wave(sh, (uint32_t)k, tbin, above, m);
+    if (m > (uint32_t)kCandCap) {  // block-uniform
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+#pragma unroll
+    for (int q = 0; q < G; ++q) {
+        if (tid + kTopkThreads * q >= mc) continue;
+        const uint32_t bi = bin2(xv[q]);
+        if (bi > tbin) {
+            atomicOr(&sh.bitmap[pv[q] >> 5], 1u << (pv[q] & 31));
+        } else if (bi == tbin) {
+            const uint32_t slot = atomicAdd(&g.ncand, 1u);  // < m: the histogram counted them
+            if (slot < (uint32_t)kCandCap) sh.cand[slot] = cand_word(xv[q], pv[q]);
+        }
+    }
+    __syncthreads();
+    resolve_emit(sh, (int)m, (uint32_t)k - above, words, k, o);
 }
 
 // ------------------------------------------------- many workgroups per row --

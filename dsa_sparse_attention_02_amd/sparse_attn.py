@@ -33,7 +33,10 @@ EXPORTS = (
 
 
 class sa_decode_config(ctypes.Structure):
-    _fields_ = [("attn_splits", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+    _fields_ = [("attn_splits", ctypes.c_int32), ("topk_path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+
+
+SA_TOPK_DEFAULT, SA_TOPK_THRESHOLD, SA_TOPK_ONEPASS_U2, SA_TOPK_ONEPASS_U4 = 0, 1, 2, 3
 
 
 class sa_params(ctypes.Structure):
@@ -436,39 +439,42 @@ def sparse_attn_prefill_blocks(p: Params, cache: PagedCache, q_start: int, q_blo
     return blk, out, lse
 
 
-def _cfg(attn_splits: int):
-    return sa_decode_config(attn_splits=attn_splits)
+def _cfg(attn_splits: int, topk_path: int = SA_TOPK_DEFAULT):
+    return sa_decode_config(attn_splits=attn_splits, topk_path=topk_path)
 
 
-def decode_workspace_size_cfg(p: Params, batch: int, max_ctx: int, attn_splits: int = 0) -> int:
+def decode_workspace_size_cfg(p: Params, batch: int, max_ctx: int, attn_splits: int = 0,
+                              topk_path: int = SA_TOPK_DEFAULT) -> int:
     n = ctypes.c_size_t()
     _check(lib().sa_decode_workspace_size_cfg(ctypes.byref(p.c()), batch, max_ctx,
-                                              ctypes.byref(_cfg(attn_splits)), ctypes.byref(n)),
+                                              ctypes.byref(_cfg(attn_splits, topk_path)), ctypes.byref(n)),
            "sa_decode_workspace_size_cfg")
     return n.value
 
 
 def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_splits: int, q, idx_q, idx_w, *,
-                           want_lse=True, workspace=None, outputs=None, stream=None):
-    """sparse_attn_decode with attn_splits attention splits per row (0 = default)."""
+                           topk_path=SA_TOPK_DEFAULT, want_lse=True, workspace=None, outputs=None, stream=None):
+    """sparse_attn_decode with attn_splits attention splits per row (0 = default)
+    and a top-k path (SA_TOPK_*)."""
     torch = _torch()
     B = q.shape[0]
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
     _dev(idx_q, "idx_q", _bf16_types(), (B, p.idx_heads, p.idx_dim))
     _dev(idx_w, "idx_w", (torch.float32,), (B, p.idx_heads))
     topk_idx, out, lse = outputs if outputs is not None else _outputs(p, B, q.device, want_lse, stream)
-    ws = workspace if workspace is not None else _workspace(decode_workspace_size_cfg(p, B, max_ctx, attn_splits),
-                                                            q.device)
+    ws = workspace if workspace is not None else _workspace(
+        decode_workspace_size_cfg(p, B, max_ctx, attn_splits, topk_path), q.device)
     _check(lib().sparse_attn_decode_cfg(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
-                                        ctypes.byref(_cfg(attn_splits)), q.data_ptr(), idx_q.data_ptr(),
+                                        ctypes.byref(_cfg(attn_splits, topk_path)), q.data_ptr(), idx_q.data_ptr(),
                                         idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
                                         ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode_cfg")
     return topk_idx, out, lse
 
 
 def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, reps=10, stream=None):
-    """Run-time tuning of the decode split count on these inputs (waits for
-    the stream).  Returns (attn_splits, microseconds per call)."""
+    """Run-time tuning of the decode split count and top-k path on these
+    inputs (waits for the stream).  Returns (attn_splits, topk_path,
+    microseconds per call)."""
     torch = _torch()
     B = q.shape[0]
     n = ctypes.c_size_t()
@@ -482,7 +488,7 @@ def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, 
                                 idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
                                 ws.data_ptr(), ws.numel(), _stream(stream), reps, ctypes.byref(best),
                                 ctypes.byref(us)), "sa_decode_tune")
-    return best.attn_splits, us.value
+    return best.attn_splits, best.topk_path, us.value
 
 
 class HipEvent:

@@ -265,23 +265,40 @@ sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged
 /* ----------------------------------------------------- run-time tuning --
  * Kernel tuning at run time (the page on the compute software stack names
  * auto-tuning of block sizes and unrolling at run time as the next step for
- * sparse attention operators).  The tunable here is the number of splits of
- * each decode row's k keys across attention workgroups (merged afterwards):
- * the default takes one attention workgroup per compute unit over the batch;
- * the best count also depends on the context lengths and the cache's
+ * sparse attention operators).  Two tunables:
+ *   attn_splits: the number of splits of each decode row's k keys across
+ *                attention workgroups (merged afterwards).  0 = the library's
+ *                choice (one attention workgroup per compute unit over the
+ *                batch); otherwise requested splits per row, clamped to what k
+ *                allows (32-token multiples of at most 2048 tokens per split).
+ *                Results do not depend on it beyond floating-point rounding
+ *                order.
+ *   topk_path:   the decode top-k's algorithm and unroll for rows of at most
+ *                262144 keys: SA_TOPK_DEFAULT (rows of at least 8 k keys take
+ *                the one-pass path below, the rest the two-pass threshold
+ *                path), SA_TOPK_THRESHOLD (every row two-pass: a histogram
+ *                pass, then a marking pass), SA_TOPK_ONEPASS_U2 / _U4 (every
+ *                row longer than 2 k one-pass: a 1/16 sample sets a bound, one
+ *                pass gathers the keys above it, the top k of those are
+ *                selected; 2 or 4 rounds of 4 KB loads in flight per wave, two
+ *                compiled variants of the gather loop).  The kept indices are
+ *                the same, bit for bit, on every path.
+ * The best choice depends on the context lengths, the batch and the cache's
  * placement, which only a run on the caller's data measures.
- *   attn_splits: 0 = the library's choice; otherwise requested splits per row,
- *                clamped to what k allows (32-token multiples of at most 2048
- *                tokens per split); results do not depend on it beyond
- *                floating-point rounding order
  */
+#define SA_TOPK_DEFAULT 0
+#define SA_TOPK_THRESHOLD 1
+#define SA_TOPK_ONEPASS_U2 2
+#define SA_TOPK_ONEPASS_U4 3
 typedef struct {
     int32_t attn_splits;
-    int32_t reserved[3];   /* zero */
+    int32_t topk_path;     /* SA_TOPK_* */
+    int32_t reserved[2];   /* zero */
 } sa_decode_config;
 
 /* sparse_attn_decode with a configuration (NULL = defaults).  SA_ERR_SHAPE
- * for attn_splits outside [0, 1024]; otherwise as sparse_attn_decode. */
+ * for attn_splits outside [0, 1024], topk_path outside the SA_TOPK_* values or
+ * nonzero reserved fields; otherwise as sparse_attn_decode. */
 sa_status sa_decode_workspace_size_cfg(const sa_params *p, int32_t batch, int32_t max_ctx,
                                        const sa_decode_config *cfg, size_t *bytes /* host, out */);
 sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *cache, int32_t batch,
@@ -289,9 +306,10 @@ sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *cache
                                  const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
                                  float *lse, void *workspace, size_t workspace_bytes, void *stream);
 /* Times sparse_attn_decode_cfg on the given inputs for every split count the
- * plan can realise (up to 64): one untimed call, then `reps` (1..1000) calls
- * between two HIP events on `stream`, per count; writes the fastest into
- * *best (and its mean microseconds per call into *best_us when non-NULL).
+ * plan can realise (up to 64) under the default top-k, then every top-k path
+ * under the fastest count: one untimed call, then `reps` (1..1000) calls
+ * between two HIP events on `stream`, per configuration; writes the fastest
+ * into *best (and its mean microseconds per call into *best_us when non-NULL).
  * Unlike every other call it creates two HIP events, waits for the stream
  * and leaves the outputs of the last call tried.  The workspace must hold
  * sa_decode_tune_workspace_size bytes (the largest of the candidates). */

@@ -289,12 +289,22 @@ def test_decode_cfg_and_tune_validation(L):
 
     assert cfg_call(sa.sa_decode_config(attn_splits=-1)) == sa.SA_ERR_SHAPE
     assert cfg_call(sa.sa_decode_config(attn_splits=2000)) == sa.SA_ERR_SHAPE
+    assert cfg_call(sa.sa_decode_config(topk_path=-1)) == sa.SA_ERR_SHAPE
+    assert cfg_call(sa.sa_decode_config(topk_path=sa.SA_TOPK_ONEPASS_U4 + 1)) == sa.SA_ERR_SHAPE
+    bad = sa.sa_decode_config()
+    bad.reserved[1] = 3
+    assert cfg_call(bad) == sa.SA_ERR_SHAPE
+    assert cfg_call(sa.sa_decode_config(topk_path=sa.SA_TOPK_ONEPASS_U4), ws=16) == sa.SA_ERR_WORKSPACE
     assert cfg_call(None, ws=16) == sa.SA_ERR_WORKSPACE
     assert cfg_call(sa.sa_decode_config(attn_splits=7), ws=16) == sa.SA_ERR_WORKSPACE
     a, b = ctypes.c_size_t(), ctypes.c_size_t()
     assert L.sa_decode_workspace_size_cfg(ctypes.byref(p), 2, 256, None, ctypes.byref(a)) == sa.SA_OK
     assert L.sa_decode_workspace_size(ctypes.byref(p), 2, 256, ctypes.byref(b)) == sa.SA_OK
     assert a.value == b.value
+    for path in (sa.SA_TOPK_THRESHOLD, sa.SA_TOPK_ONEPASS_U2, sa.SA_TOPK_ONEPASS_U4):  # (the same workspace)
+        cfg = sa.sa_decode_config(topk_path=path)
+        assert L.sa_decode_workspace_size_cfg(ctypes.byref(p), 2, 256, ctypes.byref(cfg), ctypes.byref(b)) == sa.SA_OK
+        assert b.value == a.value
     assert L.sa_decode_tune_workspace_size(ctypes.byref(p), 2, 256, ctypes.byref(b)) == sa.SA_OK
     assert b.value >= a.value
     best, us = sa.sa_decode_config(), ctypes.c_float()

@@ -472,12 +472,53 @@ def test_decode_tune_then_run(dev):
     d = sa.to_device(w)
     p = sa.Params.from_shape(w["shape"])
     max_ctx = int(w["context_lens"].max())
-    splits, us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=3)
-    say(f"  tuned: {splits} splits, {us:.1f} us per call")
+    splits, path, us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=3)
+    say(f"  tuned: {splits} splits, top-k path {path}, {us:.1f} us per call")
     assert 1 <= splits <= 64 and us > 0
-    res = sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"])
+    assert path in (sa.SA_TOPK_DEFAULT, sa.SA_TOPK_THRESHOLD, sa.SA_TOPK_ONEPASS_U2, sa.SA_TOPK_ONEPASS_U4)
+    res = sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"], topk_path=path)
     torch.cuda.synchronize()
-    compare(w, res, tag=f"decode_ragged tuned splits={splits}")
+    compare(w, res, tag=f"decode_ragged tuned splits={splits} topk_path={path}")
+
+
+TOPK_PATH_CASES = ["decode_ragged", "decode_k1", "decode_k64_ties", "decode_k3000_splits", "decode_tiny_shape",
+                   "decode_k256_bound", "decode_long_rows", "decode_long_int1", "decode_long_all_ties",
+                   "decode_all_ties"]
+
+
+@pytest.mark.parametrize("path", [1, 2, 3])
+@pytest.mark.parametrize("case", TOPK_PATH_CASES)
+def test_decode_topk_paths(dev, case, path):
+    """Every compiled top-k variant the tuner chooses among (the two-pass
+    threshold path for every row; the one-pass path for every row longer than
+    2 k, with 2 or 4 gather rounds in flight) keeps exactly the oracle's
+    indices, on ragged, tied and long rows."""
+    torch, sa = dev
+    spec = CASES[case]()
+    say(f"[gpu] {case} with top-k path {path}")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    res = sa.sparse_attn_decode_cfg(p, d["cache"], int(w["context_lens"].max()), 0, d["q"], d["idx_q"],
+                                    d["idx_w"], topk_path=path)
+    torch.cuda.synchronize()
+    compare(w, res, tag=f"{case} topk_path={path}")
+
+
+@pytest.mark.parametrize("path", [1, 2, 3])
+def test_decode_topk_paths_full_size(dev, path):
+    """The top-k variants on the mixed-length batch of 64 rows (16K to 128K
+    keys): every row against the oracle (indices bit-exact, outputs to the
+    bar)."""
+    torch, sa = dev
+    w = synth.make(synth.WORKLOADS["decode_b64_ctx16k_128k"])
+    say(f"[gpu] decode_b64_ctx16k_128k with top-k path {path}")
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    res = sa.sparse_attn_decode_cfg(p, d["cache"], int(w["context_lens"].max()), 0, d["q"], d["idx_q"],
+                                    d["idx_w"], topk_path=path)
+    torch.cuda.synchronize()
+    compare(w, res, tag=f"decode_b64_ctx16k_128k topk_path={path}")
 
 
 def test_block_selection_prefill_chunks(dev):
