@@ -169,7 +169,6 @@ struct PrefillPlan {
     int attn_chunk_rows;     // rows per attention launch when splits > 1
     size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
-    int topk_path;  // SA_TOPK_*: which decode rows take the one-pass top-k, and its unroll
 };
 
 // num_rows: query rows of the call; max_ctx: the most keys any row sees;
