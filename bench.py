@@ -319,7 +319,17 @@ def run_prefill(args, torch, sa, synth, name="prefill_L32k"):
                attention_tflops=round(attn_flops / (tot["attention"] / 1e3) / 1e12, 1))
     res["indexer_mfma_frac"] = round(res["indexer_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
     res["attention_mfma_frac"] = round(res["attention_tflops"] / MFMA_BF16_PEAK_TFLOPS, 4)
-    log(f"{spec.name}: {ms:.2f} ms/step, stages {res['stages_ms']}")
+    # the same rows in plain calls under both schedules: every chunk's select,
+    # then the attention (serial), or select and attention pipelined by chunk
+    cu, qs = (w["cu_seqlens"], w["q_starts"]) if w["mode"] == "varlen" else ([0, L], [w["q_start"]])
+    wsv = torch.empty(sa.prefill_varlen_workspace_size(p, cu, qs), dtype=torch.uint8, device="cuda")
+    sched = {}
+    for sname, code in (("serial", sa.SA_PREFILL_SERIAL), ("pipelined", sa.SA_PREFILL_PIPELINED)):
+        f = lambda code=code: sa.sparse_attn_prefill_varlen(p, d["cache"], cu, qs, d["q"], d["idx_q"], d["idx_w"],
+                                                            workspace=wsv, outputs=outs, pipeline=code)
+        sched[sname] = round(time_back_to_back(torch, f, steps, 1), 3)
+    res["schedules_ms_per_step"] = sched
+    log(f"{spec.name}: {ms:.2f} ms/step, stages {res['stages_ms']}; plain calls {sched}")
     return res
 
 

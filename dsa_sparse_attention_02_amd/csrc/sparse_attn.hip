@@ -552,41 +552,51 @@ void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const
     attend(p, a, batch, st, mk);
 }
 
-void select_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *idx_q,
-                    const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d, hipStream_t st,
-                    StageMarks *mk)
+// Scan (where some row has more than k keys) and top-k of the rows from r0 on,
+// as many as one score chunk holds; returns the end of the chunk.
+int select_prefill_chunk(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, size_t &from, int r0,
+                         const void *idx_q, const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d,
+                         hipStream_t st, StageMarks *mk)
 {
     float *scores = (float *)((char *)ws + d.off_scores);
     f32x2 *mm = (f32x2 *)((char *)ws + d.off_mm);
     std::vector<Piece> parts;
-    size_t from = 0;
-    for (int r0 = 0, r1; r0 < rows.total; r0 = r1) {
-        r1 = cut_rows(rows, from, r0, std::min(rows.total, r0 + d.chunk_rows), parts);
-        // rows whose whole context fits in k need no scores
-        bool scan = false;
-        for (const Piece &pc : parts) scan |= (int64_t)pc.pos0 + pc.n > p->topk;
-        if (scan) {
-            SeqMap bm;
-            const int nb = blocks_map(parts, r0, &bm);
-            idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
-                        idx_w + (int64_t)r0 * p->idx_heads, bm, nb, scores, d.score_stride, mm, d.mm_stride, st);
-            if (mk) mk->mark();
-        }
-        hipLaunchKernelGGL(topk_rows_kernel, dim3(r1 - r0), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, 1, (const int32_t *)nullptr, rows_map(parts, r0), p->topk,
-                           topk_idx + (int64_t)r0 * p->topk, no_append());
+    const int r1 = cut_rows(rows, from, r0, std::min(rows.total, r0 + d.chunk_rows), parts);
+    // rows whose whole context fits in k need no scores
+    bool scan = false;
+    for (const Piece &pc : parts) scan |= (int64_t)pc.pos0 + pc.n > p->topk;
+    if (scan) {
+        SeqMap bm;
+        const int nb = blocks_map(parts, r0, &bm);
+        idx_prefill(p, c, (const uint16_t *)idx_q + (int64_t)r0 * p->idx_heads * p->idx_dim,
+                    idx_w + (int64_t)r0 * p->idx_heads, bm, nb, scores, d.score_stride, mm, d.mm_stride, st);
         if (mk) mk->mark();
     }
+    hipLaunchKernelGGL(topk_rows_kernel, dim3(r1 - r0), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
+                       d.mm_stride, 1, (const int32_t *)nullptr, rows_map(parts, r0), p->topk,
+                       topk_idx + (int64_t)r0 * p->topk, no_append());
+    if (mk) mk->mark();
+    return r1;
 }
 
-void attend_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *q,
-                    const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d, hipStream_t st,
+void select_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *idx_q,
+                    const float *idx_w, int32_t *topk_idx, void *ws, const PrefillPlan &d, hipStream_t st,
                     StageMarks *mk)
+{
+    size_t from = 0;
+    for (int r0 = 0; r0 < rows.total;)
+        r0 = select_prefill_chunk(p, c, rows, from, r0, idx_q, idx_w, topk_idx, ws, d, st, mk);
+}
+
+// attention of rows [ra, rb)
+void attend_prefill_rows(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, int ra, int rb,
+                         const void *q, const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d,
+                         hipStream_t st, StageMarks *mk)
 {
     std::vector<Piece> parts;
     size_t from = 0;
-    for (int r0 = 0, r1; r0 < rows.total; r0 = r1) {
-        r1 = cut_rows(rows, from, r0, std::min(rows.total, r0 + d.attn_chunk_rows), parts);
+    for (int r0 = ra, r1; r0 < rb; r0 = r1) {
+        r1 = cut_rows(rows, from, r0, std::min(rb, r0 + d.attn_chunk_rows), parts);
         AttnArgs a = attn_args(p, c, (const uint16_t *)q + (int64_t)r0 * p->num_heads * p->qk_dim,
                                topk_idx + (int64_t)r0 * p->topk,
                                (char *)out + (int64_t)r0 * p->num_heads * p->v_dim * (p->out_dtype ? 2 : 4),
@@ -599,6 +609,86 @@ void attend_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRo
         a.part_ml = (float *)((char *)ws + d.off_part_ml);
         attend(p, a, r1 - r0, st, mk);
     }
+}
+
+void attend_prefill(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *q,
+                    const int32_t *topk_idx, void *out, float *lse, void *ws, const PrefillPlan &d, hipStream_t st,
+                    StageMarks *mk)
+{
+    attend_prefill_rows(p, c, rows, 0, rows.total, q, topk_idx, out, lse, ws, d, st, mk);
+}
+
+// The library's second stream on the current device (default priority,
+// non-blocking), created on first use and kept until the process ends.
+constexpr int kMaxDevices = 64;
+static std::mutex g_side_mu;
+static hipStream_t g_side[kMaxDevices];
+
+static hipStream_t side_stream()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    if (!g_side[dev] && hipStreamCreateWithFlags(&g_side[dev], hipStreamNonBlocking) != hipSuccess)
+        g_side[dev] = nullptr;
+    return g_side[dev];
+}
+
+// Index selection and attention pipelined by chunks of rows ("Day-0
+// Adaptation for LLMs: Implementing Sparse Attention and Low-Precision
+// Weights", section III item 3): the scan and top-k of chunk i + 1 run on the
+// caller's stream while the attention of chunk i runs on the library's second
+// stream, which waits for chunk i's top-k through an event; the caller's
+// stream waits for the second stream's last launch at the end, so the call is
+// ordered on the caller's stream as a serial one would be.  Returns false
+// (having launched nothing) where it cannot run: one chunk, a stream under
+// graph capture, or no second stream or events.
+static bool prefill_pipelined(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows, const void *q,
+                              const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                              void *ws, const PrefillPlan &d, hipStream_t st)
+{
+    if (d.chunk_rows >= rows.total) return false;
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone) return false;
+    hipStream_t side = side_stream();
+    if (!side) return false;
+    std::vector<int> ends;  // the chunks, as select_prefill_chunk cuts them
+    {
+        std::vector<Piece> parts;
+        size_t from = 0;
+        for (int r0 = 0; r0 < rows.total;) {
+            r0 = cut_rows(rows, from, r0, std::min(rows.total, r0 + d.chunk_rows), parts);
+            ends.push_back(r0);
+        }
+    }
+    const int nchunks = (int)ends.size();
+    std::vector<hipEvent_t> ev;
+    auto drop = [&]() {
+        for (hipEvent_t e : ev) (void)hipEventDestroy(e);  // (released once complete)
+    };
+    for (int i = 0; i < nchunks + 2; ++i) {
+        hipEvent_t e = nullptr;
+        if (hipEventCreateWithFlags(&e, hipEventDisableTiming) != hipSuccess) {
+            drop();
+            clear_hip_error();
+            return false;
+        }
+        ev.push_back(e);
+    }
+    int ne = 0;
+    (void)hipEventRecord(ev[ne], st);  // the side stream starts after the caller's earlier work
+    (void)hipStreamWaitEvent(side, ev[ne++], 0);
+    size_t from = 0;
+    for (int i = 0, r0 = 0; i < nchunks; r0 = ends[i++]) {
+        const int r1 = select_prefill_chunk(p, c, rows, from, r0, idx_q, idx_w, topk_idx, ws, d, st, nullptr);
+        (void)hipEventRecord(ev[ne], st);
+        (void)hipStreamWaitEvent(side, ev[ne++], 0);
+        attend_prefill_rows(p, c, rows, r0, r1, q, topk_idx, out, lse, ws, d, side, nullptr);
+    }
+    (void)hipEventRecord(ev[ne], side);
+    (void)hipStreamWaitEvent(st, ev[ne], 0);
+    drop();
+    return true;
 }
 
 // ------------------------------------------------ block-granular selection --
@@ -895,7 +985,7 @@ sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *c
 static sa_status prefill_rows_impl(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows,
                                    const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx,
                                    void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
-                                   StageMarks *mk)
+                                   StageMarks *mk, bool pipeline = false)
 {
     if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
     const PrefillPlan d = plan_prefill(p, rows.total, rows.max_ctx);
@@ -907,6 +997,8 @@ static sa_status prefill_rows_impl(const sa_params *p, const sa_paged_cache *c, 
         mk->stream = st;
         mk->mark();
     }
+    if (pipeline && !mk && prefill_pipelined(p, c, rows, q, idx_q, idx_w, topk_idx, out, lse, workspace, d, st))
+        return launched();
     select_prefill(p, c, rows, idx_q, idx_w, topk_idx, workspace, d, st, mk);
     attend_prefill(p, c, rows, q, topk_idx, out, lse, workspace, d, st, mk);
     return launched();
@@ -925,7 +1017,8 @@ static sa_status prefill_impl(const sa_params *p, const sa_paged_cache *c, int32
 static sa_status prefill_varlen_impl(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
                                      const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
                                      const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out, float *lse,
-                                     void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk)
+                                     void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk,
+                                     bool pipeline = false)
 {
     sa_status s = check_params(p);
     if (s != SA_OK) return s;
@@ -936,7 +1029,20 @@ static sa_status prefill_varlen_impl(const sa_params *p, const sa_paged_cache *c
         SA_OK)
         return s;
     return prefill_rows_impl(p, c, rows, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
-                             mk);
+                             mk, pipeline);
+}
+
+sa_status sparse_attn_prefill_varlen_cfg(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
+                                         const int32_t *cu_seqlens, const int32_t *q_starts,
+                                         const sa_prefill_config *cfg, const void *q, const void *idx_q,
+                                         const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (cfg && ((cfg->pipeline != SA_PREFILL_SERIAL && cfg->pipeline != SA_PREFILL_PIPELINED) ||
+                cfg->reserved[0] != 0 || cfg->reserved[1] != 0 || cfg->reserved[2] != 0))
+        return SA_ERR_SHAPE;
+    return prefill_varlen_impl(p, c, num_seqs, cu_seqlens, q_starts, q, idx_q, idx_w, topk_idx, out, lse, workspace,
+                               workspace_bytes, stream, nullptr, cfg && cfg->pipeline == SA_PREFILL_PIPELINED);
 }
 
 sa_status sparse_attn_prefill_varlen(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
@@ -1184,14 +1290,14 @@ sa_status sparse_attn_prefill_blocks(const sa_params *p, const sa_paged_cache *c
 static __device__ __align__(256) uint8_t scratch[SA_NOALLOC_SCRATCH_BYTES];
 
 static std::mutex g_scratch_mu;
-static void *g_scratch_addr[64];  // device address of `scratch`, by device id
+static void *g_scratch_addr[kMaxDevices];  // device address of `scratch`, by device id
 
 // The address of `scratch` on the caller's current device (looked up on the
 // first call for that device, with that device current).
 static sa_status scratch_address(void **addr)
 {
     int dev = -1;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return SA_ERR_HIP;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SA_ERR_HIP;
     std::lock_guard<std::mutex> lock(g_scratch_mu);
     if (!g_scratch_addr[dev]) {
         void *ptr = nullptr;

@@ -119,7 +119,8 @@ __device__ __forceinline__ void pick_bin(TopkShared &sh, int nbins, uint32_t nee
 
 // Radix path for one row: exact threshold key by three histogram passes, then
 // ordered compaction with the lowest-position tie-break.
-__device__ void topk_radix_row(TopkShared &sh, const float *__restrict__ sr, int n, int k, int32_t *__restrict__ o)
+__device__ __forceinline__ void topk_radix_row(TopkShared &sh, const float *__restrict__ sr, int n, int k,
+                                               int32_t *__restrict__ o)
 {
     const int tid = threadIdx.x;
     const int n4 = n & ~3;
@@ -283,7 +284,8 @@ __device__ __forceinline__ uint64_t cand_word(float x, int i)
 // descending, join the bitmap; 5. the bitmap's positions are written in order.
 // Up to 64 candidates: wave 0 ranks each against all (lane i holds candidate
 // i); more: a bitonic sort over the block.
-__device__ void resolve_emit(TopkShared &sh, int m, uint32_t need, int words, int k, int32_t *__restrict__ o)
+__device__ __forceinline__ void resolve_emit(TopkShared &sh, int m, uint32_t need, int words, int k,
+                                             int32_t *__restrict__ o)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (m <= 64) {  // block-uniform
@@ -327,8 +329,8 @@ __device__ void resolve_emit(TopkShared &sh, int m, uint32_t need, int words, in
 
 // Steps 2-5 of the threshold path for a row of n keys (k < n <= kBitmapKeys)
 // whose score range is [lo, hi].
-__device__ void threshold_row(TopkShared &sh, const float *__restrict__ sr, int n, int k, int32_t *__restrict__ o,
-                              float lo, float hi)
+__device__ __forceinline__ void threshold_row(TopkShared &sh, const float *__restrict__ sr, int n, int k,
+                                              int32_t *__restrict__ o, float lo, float hi)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n4 = n & ~3;

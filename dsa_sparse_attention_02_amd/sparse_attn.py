@@ -29,6 +29,7 @@ EXPORTS = (
     "sa_decode_blocks_workspace_size", "sparse_attn_decode_blocks", "sa_prefill_blocks_workspace_size",
     "sparse_attn_prefill_blocks", "sa_decode_workspace_size_cfg", "sparse_attn_decode_cfg",
     "sa_decode_tune_workspace_size", "sa_decode_tune", "sparse_attn_decode_noalloc",
+    "sparse_attn_prefill_varlen_cfg",
 )
 
 
@@ -37,6 +38,13 @@ class sa_decode_config(ctypes.Structure):
 
 
 SA_TOPK_DEFAULT, SA_TOPK_THRESHOLD, SA_TOPK_ONEPASS_U2, SA_TOPK_ONEPASS_U4 = 0, 1, 2, 3
+
+
+class sa_prefill_config(ctypes.Structure):
+    _fields_ = [("pipeline", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+
+
+SA_PREFILL_SERIAL, SA_PREFILL_PIPELINED = 0, 1
 
 
 class sa_params(ctypes.Structure):
@@ -91,6 +99,7 @@ def lib():
             "sparse_attn_prefill_varlen": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, sz, P]),
             "sparse_attn_prefill_varlen_profiled": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, sz, P,
                                                                    P, i32, ctypes.POINTER(i32)]),
+            "sparse_attn_prefill_varlen_cfg": (ctypes.c_int, [pp, pc, i32, P, P, P, P, P, P, P, P, P, P, sz, P]),
             "sa_decode_blocks_workspace_size": (ctypes.c_int, [pp, i32, i32, ctypes.POINTER(sz)]),
             "sparse_attn_decode_blocks": (ctypes.c_int, [pp, pc, i32, i32, P, P, P, P, P, P, P, sz, P]),
             "sa_prefill_blocks_workspace_size": (ctypes.c_int, [pp, i32, i32, i32, ctypes.POINTER(sz)]),
@@ -355,12 +364,14 @@ def prefill_varlen_workspace_size(p: Params, cu_seqlens, q_starts) -> int:
 
 
 def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_starts, q, idx_q, idx_w, *,
-                               want_lse=True, workspace=None, outputs=None, stream=None, events=None):
+                               want_lse=True, workspace=None, outputs=None, stream=None, events=None,
+                               pipeline=None):
     """Prefill of several sequences in one call: sequence s owns packed rows
     cu_seqlens[s] .. cu_seqlens[s+1]-1 (host int32 arrays), its row i at
     position q_starts[s] + i, block-table row s.  With `events`, the profiling
     entry point records them around the kernels and the mark count is returned
-    as a fourth value."""
+    as a fourth value.  With `pipeline` (SA_PREFILL_*), the configured entry
+    point runs that schedule."""
     torch = _torch()
     q_starts = np.asarray(q_starts)
     cu = _host_i32(cu_seqlens, "cu_seqlens", len(q_starts) + 1)
@@ -376,6 +387,13 @@ def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_start
     args = (ctypes.byref(p.c()), ctypes.byref(cache.c()), len(qs), cu.ctypes.data, qs.ctypes.data, q.data_ptr(),
             idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
             ws.numel(), _stream(stream))
+    if pipeline is not None:
+        if events is not None:
+            raise SparseAttnError(SA_ERR_SHAPE, "pipeline and events are exclusive")
+        cfg = sa_prefill_config(pipeline=pipeline)
+        _check(lib().sparse_attn_prefill_varlen_cfg(*args[:5], ctypes.byref(cfg), *args[5:]),
+               "sparse_attn_prefill_varlen_cfg")
+        return topk_idx, out, lse
     if events is None:
         _check(lib().sparse_attn_prefill_varlen(*args), "sparse_attn_prefill_varlen")
         return topk_idx, out, lse

@@ -253,6 +253,37 @@ sa_status sparse_attn_prefill_varlen(const sa_params *p, const sa_paged_cache *c
                                      const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
                                      const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
                                      float *lse, void *workspace, size_t workspace_bytes, void *stream);
+/* Varlen prefill with a schedule choice (NULL = defaults).
+ *   pipeline: SA_PREFILL_SERIAL (the default): every score chunk's scan and
+ *             top-k, then the attention of all rows, on `stream`.
+ *             SA_PREFILL_PIPELINED: the select and attention stages pipelined
+ *             by chunk (section III item 3 of the page on implementing sparse
+ *             attention and low-precision weights): the scan and top-k of
+ *             chunk i + 1 run on `stream` while the attention of chunk i runs
+ *             on a second stream that the library creates on first use (one
+ *             per device, default priority, kept until the process ends); it
+ *             waits for chunk i's top-k and for `stream`'s earlier work
+ *             through events, and `stream` waits for its last launch, so the
+ *             call is ordered on `stream` like any other.  It applies when the
+ *             rows take more than one score chunk and `stream` is not being
+ *             captured into a graph (otherwise the serial schedule runs).
+ *             The results are the serial schedule's, bit for bit.  On MI355X
+ *             it gains nothing at the shapes measured: an attention workgroup
+ *             holds a compute unit's LDS, so the stages alternate on each unit
+ *             rather than share it.
+ * SA_ERR_SHAPE for another pipeline value or nonzero reserved fields;
+ * otherwise as sparse_attn_prefill_varlen (same workspace). */
+#define SA_PREFILL_SERIAL 0
+#define SA_PREFILL_PIPELINED 1
+typedef struct {
+    int32_t pipeline;
+    int32_t reserved[3];   /* zero */
+} sa_prefill_config;
+sa_status sparse_attn_prefill_varlen_cfg(const sa_params *p, const sa_paged_cache *cache, int32_t num_seqs,
+                                         const int32_t *cu_seqlens, const int32_t *q_starts,
+                                         const sa_prefill_config *cfg, const void *q, const void *idx_q,
+                                         const float *idx_w, int32_t *topk_idx, void *out, float *lse,
+                                         void *workspace, size_t workspace_bytes, void *stream);
 /* Profiling variant (marks as for sparse_attn_prefill_profiled). */
 sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged_cache *cache,
                                               int32_t num_seqs, const int32_t *cu_seqlens,

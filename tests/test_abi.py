@@ -276,6 +276,27 @@ def test_block_selection_validation(L):
     assert L.sa_prefill_blocks_workspace_size(ctypes.byref(p), 100, 0, 3, ctypes.byref(n)) == sa.SA_ERR_UNSUPPORTED
 
 
+def test_prefill_varlen_cfg_validation(L):
+    """The configured varlen prefill checks its schedule before any HIP call."""
+    p, c = _params(), _cache()
+    F = FAKE
+    cu = (ctypes.c_int32 * 2)(0, 4)
+    qs = (ctypes.c_int32 * 1)(0)
+
+    def call(cfg, ws=1 << 40):
+        return L.sparse_attn_prefill_varlen_cfg(ctypes.byref(p), ctypes.byref(c), 1, cu, qs,
+                                                ctypes.byref(cfg) if cfg is not None else None, F, F, F, F, F,
+                                                None, F, ws, None)
+
+    assert call(sa.sa_prefill_config(pipeline=2)) == sa.SA_ERR_SHAPE
+    assert call(sa.sa_prefill_config(pipeline=-1)) == sa.SA_ERR_SHAPE
+    bad = sa.sa_prefill_config()
+    bad.reserved[2] = 1
+    assert call(bad) == sa.SA_ERR_SHAPE
+    assert call(sa.sa_prefill_config(pipeline=sa.SA_PREFILL_PIPELINED), ws=16) == sa.SA_ERR_WORKSPACE
+    assert call(None, ws=16) == sa.SA_ERR_WORKSPACE
+
+
 def test_decode_cfg_and_tune_validation(L):
     """The configured decode and the tuner check the configuration, the
     repetition count and the workspace before any HIP call."""

@@ -185,6 +185,31 @@ def test_staged_equals_fused_and_deterministic(dev, name):
         assert np.array_equal(x[2].cpu().numpy(), y[2].cpu().numpy())
 
 
+def test_prefill_pipelined_equals_serial(dev):
+    """prefill_L32k selects in four chunks of 8192 rows, so the pipelined
+    schedule runs the attention of chunk i on the library's second stream while
+    chunk i + 1 is scanned.  Called on a non-default caller stream, it gives the
+    serial schedule's indices, outputs and lse bit for bit, and so does a
+    repeat."""
+    torch, sa = dev
+    w = synth.make(synth.WORKLOADS["prefill_L32k"])
+    say("[gpu] prefill_L32k pipelined against serial")
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    cu, qs = [0, w["rows"]], [w["q_start"]]
+    side = torch.cuda.Stream()
+    with torch.cuda.stream(side):
+        a = sa.sparse_attn_prefill_varlen(p, d["cache"], cu, qs, d["q"], d["idx_q"], d["idx_w"], stream=side,
+                                          pipeline=sa.SA_PREFILL_PIPELINED)
+        b = sa.sparse_attn_prefill_varlen(p, d["cache"], cu, qs, d["q"], d["idx_q"], d["idx_w"], stream=side,
+                                          pipeline=sa.SA_PREFILL_PIPELINED)
+        c = sa.sparse_attn_prefill(p, d["cache"], w["q_start"], d["q"], d["idx_q"], d["idx_w"], stream=side)
+    side.synchronize()
+    for x, y in ((a, b), (a, c)):
+        for i in range(3):
+            assert torch.equal(x[i], y[i]), f"output {i} differs"
+
+
 def test_block_relabelling_invariance_gpu(dev):
     spec = CASES["decode_ragged"]()
     say("[gpu] block relabelling invariance")
