@@ -16,22 +16,24 @@
 // the next tile's gather is in flight while the current one is computed (same
 // item: prefetch of the next KV block during attention).
 //
-// gfx950 mapping.  One workgroup = one (row, split) over all heads: 2 * HB waves,
-// two per 32-head block.  The two waves of a head block ("partners" x = 0, 1)
-// split both contractions: for q.k, partner x holds the query of its 32 heads
-// over half of the QK dims (QK = 576: 72 registers) and computes a partial S^T
-// over that half; for P.V it owns half of the V value columns (V = 512: 32 x
-// 256 fp32 accumulators, 128 registers).  The partners add their partial S^T
-// through LDS, so no logit is computed twice, and with 8 waves two run on each
-// SIMD (256 registers each), hiding each other's LDS and MFMA latencies.  Per
+// gfx950 mapping.  One workgroup = one (row, split, head group of 32 * HB
+// heads): 2 * HB waves, two per 32-head block.  The two waves of a head block
+// ("partners" x = 0, 1) split both contractions: for q.k, partner x holds the
+// query of its 32 heads over half of the QK dims (QK = 576: 72 registers) and
+// computes a partial S^T over that half; for P.V it owns half of the V value
+// columns (V = 512: 32 x 256 fp32 accumulators, 128 registers).  The partners
+// add their partial S^T through LDS (the main rows of a spent tile buffer), so
+// no logit is computed twice.  With 128 heads, HB = 2: two workgroups of 4 waves
+// per (row, split), one wave per SIMD (the tile ring takes 158 KB of LDS).  Per
 // tile of 32 kept tokens:
 //   * the 32 latent rows are copied HBM -> LDS by buffer-form LDS-DMA, one
 //     resource per token row: a 64-lane copy of its first 1 KiB and an 8-lane
 //     copy of its 128-byte tail; the main rows' 16-byte pieces are XOR-swizzled
 //     by token (through the copy's per-lane source offsets) so that MFMA
-//     operand reads do not collide on LDS banks; a ring of 3 tile buffers keeps
-//     the next tile's copies in flight while one tile's values and the
-//     following tile's keys are read;
+//     operand reads do not collide on LDS banks; a ring of 4 tile buffers keeps
+//     two tiles' copies in flight while one tile's values and the next tile's
+//     keys are read, and the copies of tile t + 3 are issued between the q.k
+//     MFMAs of tile t + 1, beside the softmax of tile t;
 //   * partial S^T[token][head] = K . Q^T on 32x32x16 bf16 MFMAs (K from LDS,
 //     Q^T from registers, contraction over the partner's QK half in 16-wide
 //     steps), exchanged through LDS and summed;
