@@ -39,6 +39,10 @@ constexpr int kTargetAttnBlocks = 256;        // one attention workgroup per CU 
 // costs more than the extra workgroups gain (batches of 1, 2 and 4 at long
 // contexts ran 3-8% faster at 22 splits than at 32 or 64).
 constexpr int kMaxDefaultSplits = 24;
+#ifndef SA_COMBINE_HEADS
+#define SA_COMBINE_HEADS 8
+#endif
+constexpr int kCombineHeads = SA_COMBINE_HEADS;  // heads per 512-thread merge workgroup (64 or 128 threads each)
 #ifndef SA_TOPK_ONEPASS_MIN_PER_K
 #define SA_TOPK_ONEPASS_MIN_PER_K 8
 #endif
@@ -440,9 +444,10 @@ void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st, StageMarks
     if (mk) mk->mark();
     if (a.splits > 1) {
         dim3 cg(p->num_heads, rows);
-        if (p->v_dim == 512 && a.splits <= 64 && p->num_heads % 4 == 0)  // 4 heads per workgroup
-            hipLaunchKernelGGL((combine_kernel<512, 4>), dim3(p->num_heads / 4, rows), dim3(512), 0, st, a.part_o,
-                               a.part_ml, a.splits, p->num_heads, a.out, a.out_bf16, a.lse);
+        if (p->v_dim == 512 && a.splits <= 64 && p->num_heads % kCombineHeads == 0)  // kCombineHeads per workgroup
+            hipLaunchKernelGGL((combine_kernel<512, kCombineHeads>), dim3(p->num_heads / kCombineHeads, rows),
+                               dim3(512), 0, st, a.part_o, a.part_ml, a.splits, p->num_heads, a.out, a.out_bf16,
+                               a.lse);
         else if (p->v_dim == 512)
             hipLaunchKernelGGL((combine_kernel<512, 1>), cg, dim3(128), 0, st, a.part_o, a.part_ml, a.splits,
                                p->num_heads, a.out, a.out_bf16, a.lse);

@@ -210,6 +210,28 @@ def test_prefill_pipelined_equals_serial(dev):
             assert torch.equal(x[i], y[i]), f"output {i} differs"
 
 
+def test_prefill_pipelined_split_attention(dev):
+    """The pipelined schedule with k = 3000 (two attention splits per row and a
+    merge per attention launch, the partials' workspace reused launch after
+    launch on the second stream) over 9000 rows after 23000 cached tokens:
+    two score chunks, bit-equal to the serial schedule."""
+    torch, sa = dev
+    spec = synth.small_prefill("prefill_pipe_k3000", MLA, rows=9000, q_start=23000, seed=131, topk=3000)
+    say("[gpu] prefill 9000 rows, k = 3000, pipelined against serial")
+    w = synth.make(spec)
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    cu, qs = [0, w["rows"]], [w["q_start"]]
+    a = sa.sparse_attn_prefill_varlen(p, d["cache"], cu, qs, d["q"], d["idx_q"], d["idx_w"],
+                                      pipeline=sa.SA_PREFILL_PIPELINED)
+    b = sa.sparse_attn_prefill_varlen(p, d["cache"], cu, qs, d["q"], d["idx_q"], d["idx_w"],
+                                      pipeline=sa.SA_PREFILL_SERIAL)
+    torch.cuda.synchronize()
+    for i in range(3):
+        assert torch.equal(a[i], b[i]), f"output {i} differs"
+    compare(w, b, rows=[0, 1, 4095, 4096, 8191, 8192, 8999], tag="prefill_pipe_k3000")
+
+
 def test_block_relabelling_invariance_gpu(dev):
     spec = CASES["decode_ragged"]()
     say("[gpu] block relabelling invariance")
