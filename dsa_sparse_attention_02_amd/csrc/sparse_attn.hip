@@ -158,10 +158,15 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_spli
     }
     // many-workgroup top-k state: per row a MbRowState, 3 digit histograms and
     // two counts per chunk
+    // (or, for k <= kLongCap / 2 and rows of at most kMaxLongChunks chunks, the
+    // three-launch path's per-row state, per-chunk counts and key segments)
     d.off_mb = off;
     d.mb_chunks = max_ctx > kBitmapKeys ? (max_ctx + kMbChunk - 1) / kMbChunk : 0;
-    if (d.mb_chunks > 0)
-        off = align_up(off + (size_t)batch * (sizeof(MbRowState) + 3 * kMbBins * 4 + (size_t)d.mb_chunks * 8), kAlign);
+    if (d.mb_chunks > 0) {
+        const size_t mb = (size_t)batch * (sizeof(MbRowState) + 3 * kMbBins * 4 + (size_t)d.mb_chunks * 8);
+        const size_t lp = (size_t)batch * (sizeof(LongRowState) + (size_t)d.mb_chunks * (8 + (size_t)kLongSeg * 8));
+        off = align_up(off + std::max(mb, lp), kAlign);
+    }
     d.total = std::max(off, kAlign);
     return d;
 }
@@ -513,7 +518,19 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
         idx_decode(p, c, batch, idx_q, idx_w, scores, d.score_stride, mm, d.mm_stride, d.scan_blocks, ap, st);
         if (mk) mk->mark();
     }
-    if (d.mb_chunks > 0) {
+    if (d.mb_chunks > 0 && 2 * p->topk <= kLongCap && d.mb_chunks <= kMaxLongChunks) {
+        LongRowState *lst = (LongRowState *)((char *)ws + d.off_mb);
+        uint64_t *seg = (uint64_t *)(lst + batch);  // (16-byte states keep these aligned)
+        uint2 *seg_info = (uint2 *)(seg + (size_t)batch * d.mb_chunks * kLongSeg);
+        const int32_t *cl = c->context_lens;
+        hipLaunchKernelGGL(topk_long_bound_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
+                           d.mm_stride, cl, p->topk, topk_idx, lst, ap);
+        hipLaunchKernelGGL(topk_long_gather_kernel, dim3(d.mb_chunks, batch), dim3(kTopkThreads), 0, st, scores,
+                           d.score_stride, cl, p->topk, (const LongRowState *)lst, seg, seg_info);
+        hipLaunchKernelGGL(topk_long_select_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
+                           cl, p->topk, d.mb_chunks, (const LongRowState *)lst, (const uint64_t *)seg,
+                           (const uint2 *)seg_info, topk_idx);
+    } else if (d.mb_chunks > 0) {
         MbRowState *mst = (MbRowState *)((char *)ws + d.off_mb);
         uint32_t *hist = (uint32_t *)(mst + batch);
         uint32_t *counts = hist + (size_t)batch * 3 * kMbBins;

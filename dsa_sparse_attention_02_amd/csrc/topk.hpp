@@ -951,4 +951,306 @@ __global__ __launch_bounds__(kTopkThreads) void topk_mb_emit_kernel(
     }
 }
 
+// ---------------------------------------------- one pass for very long rows --
+// Rows over kBitmapKeys keys (with 2 k <= kLongCap) in three launches instead
+// of the many-workgroup radix select's nine:
+//  1. per row (topk_long_bound_kernel): a sample of one 32-key tile in every
+//     kLongGap keys (1/64 of the row) is histogrammed over its own range, and
+//     the bound T_f is set where about 1.25 k/64 + 16 sample keys lie above it;
+//  2. per 16384-key chunk (topk_long_gather_kernel): the chunk's keys >= T_f
+//     are written, as (order-preserving key, position) words in ascending
+//     position order, to the chunk's own segment of kLongSeg words, with their
+//     count and largest key;
+//  3. per row (topk_long_select_kernel): if the segments hold at least k and
+//     at most kLongCap keys (none overflowing), the top k of the row are the
+//     top k of those keys (the k-th best key of the row is >= T_f).  They are
+//     read into LDS in position order, binned over [T_f, max], the threshold
+//     bin found by a suffix scan and its keys ranked exactly (score, then the
+//     lower position); the kept keys, flagged in order, are compacted into the
+//     output, which is then ascending without a sort.  Otherwise the row takes
+//     the radix path of one workgroup (exact; slow on such rows, and only
+//     where the sample misjudged the row or scores tie massively).
+// The segments take 8 bytes per key of the row: twice the scores' space.
+constexpr int kLongCap = 8192;  // gathered keys a row may select from
+constexpr int kMaxLongChunks = 1024;  // 16384-key chunks a row may have (16M keys)
+constexpr int kLongGap = 2048;  // keys from one sample tile to the next
+constexpr int kLongSeg = kLongCap;  // gathered keys a chunk may hold (more than this: more than kLongCap)
+
+struct LongRowState {
+    float tf;  // the bound
+    uint32_t pad[3];
+};
+
+// inverse of score_key
+__device__ __forceinline__ float key_score(uint32_t key)
+{
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_long_bound_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
+    const int32_t *__restrict__ ctx_lens, int k, int32_t *__restrict__ out, LongRowState *__restrict__ state,
+    const AppendArgs ap)
+{
+    __shared__ TopkShared sh;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    append_rows(ap, r, tid, kTopkThreads);  // (row r = sequence r; before the attention reads it)
+    const int n = ctx_lens[r];
+    if (n <= k) {  // (block-uniform) the whole row
+        int32_t *o = out + (int64_t)r * k;
+        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
+        return;
+    }
+    const float *sr = scores + (int64_t)r * score_stride;
+    const f32x2 *mm = tile_mm + (int64_t)r * mm_stride;
+    // sample tile j: keys [kLongGap j, kLongGap j + 32), tile entry kLongGap j / 32
+    // of the ranges; thread t reads 4 keys of tile (t >> 3) + 128 q.  (A score
+    // row is allocated to a multiple of 64 keys, so a 16-byte piece of a tile
+    // that starts below n is read whole; keys at n and beyond are never counted.)
+    const int ns = (n + kLongGap - 1) / kLongGap;
+    const int sx = 4 * (tid & 7);
+    float lo = INFINITY, hi = -INFINITY;
+    for (int j = tid; j < ns; j += kTopkThreads) {
+        const f32x2 v = mm[(int64_t)j * (kLongGap / 32)];
+        lo = fminf(lo, v[0]);
+        hi = fmaxf(hi, v[1]);
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        lo = fminf(lo, __shfl_xor(lo, d));
+        hi = fmaxf(hi, __shfl_xor(hi, d));
+    }
+    if (lane == 0) {
+        sh.red[0][wv] = lo;
+        sh.red[1][wv] = hi;
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    __syncthreads();
+    lo = sh.red[0][0];
+    hi = sh.red[1][0];
+    for (int w = 1; w < kTopkWaves; ++w) {
+        lo = fminf(lo, sh.red[0][w]);
+        hi = fmaxf(hi, sh.red[1][w]);
+    }
+    const ScoreBins bin_of(lo, hi);
+    for (int j0 = tid >> 3; j0 < ns; j0 += 4 * (kTopkThreads / 8)) {
+        f32x4 v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q)  // (tiles past the last are read as the last one, and not counted)
+            v[q] = *reinterpret_cast<const f32x4 *>(sr + (int64_t)kLongGap * min(j0 + 128 * q, ns - 1) + sx);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int j = j0 + 128 * q, i0 = kLongGap * j + sx;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                if (j < ns && i0 + e < n) atomicAdd(&sh.hist[bin_of(v[q][e])], 1u);
+        }
+    }
+    __syncthreads();
+    const int nsamp = 32 * (ns - 1) + min(32, n - kLongGap * (ns - 1));
+    const uint32_t want = (uint32_t)min(nsamp, (int)ceilf(1.25f * (float)k * (float)nsamp / (float)n) + 16);
+    uint32_t b, above, cnt;
+    pick_bin_wave(sh, want, b, above, cnt);
+    if (tid == 0) state[r] = LongRowState{bin_of.scale > 0.0f ? lo + (float)b / bin_of.scale : lo, {0u, 0u, 0u}};
+}
+
+// Chunk c of row r: keys [16384 c, 16384 c + 16384); wave w takes keys
+// [1024 w, 1024 w + 1024) of it, lane l the 16 consecutive keys 16 l ..
+// (four 16-byte loads), so lane order, then wave order, is position order.
+// seg: [rows][chunks][kLongSeg] words; seg_info: [rows][chunks] (count, largest key).
+__global__ __launch_bounds__(kTopkThreads) void topk_long_gather_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens, int k,
+    const LongRowState *__restrict__ state, uint64_t *__restrict__ seg, uint2 *__restrict__ seg_info)
+{
+    __shared__ uint32_t wtot[kTopkWaves], wmax[kTopkWaves];
+    const int r = blockIdx.y, n = ctx_lens[r], tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int c0 = blockIdx.x * kMbChunk;
+    if (n <= k || c0 >= n) return;  // (block-uniform)
+    static_assert(kMbChunk == 1024 * kTopkWaves, "one 1024-key round per wave");
+    const float tf = state[r].tf;
+    const float *sr = scores + (int64_t)r * score_stride;
+    const int n64 = (n + 63) & ~63;
+    const int i0 = c0 + 1024 * wv + 16 * lane;
+    f32x4 v[4];  // (pieces past the row's allocation re-read its last one: never gathered)
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4 *>(sr + min(i0 + 4 * u, n64 - 4));
+    uint32_t bits = 0, kmax = 0;  // gathered keys (bit j: key i0 + j); the largest one's order-preserving key
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const bool c = v[u][e] >= tf && i0 + 4 * u + e < n;
+            bits |= c ? 1u << (4 * u + e) : 0u;
+            kmax = c ? max(kmax, score_key(v[u][e])) : kmax;
+        }
+    const uint32_t cnt = (uint32_t)__popc(bits);  // <= 16: five bits
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int bt = 0; bt < 5; ++bt) {
+        const uint64_t mb = __ballot((cnt >> bt) & 1u);
+        pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u)) << bt;
+        tot += (uint32_t)__popcll(mb) << bt;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
+    if (lane == 0) {
+        wtot[wv] = tot;
+        wmax[wv] = kmax;
+    }
+    __syncthreads();
+    uint32_t slot = pre;
+    for (int w = 0; w < wv; ++w) slot += wtot[w];
+    uint64_t *sg = seg + ((int64_t)r * gridDim.x + blockIdx.x) * kLongSeg;
+    while (bits) {
+        const int j = __builtin_ctz(bits);
+        bits &= bits - 1;
+        const int ju = j >> 2, je = j & 3;  // key j of the lane's 16, picked from registers
+        float xu[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) xu[u] = je == 0 ? v[u][0] : je == 1 ? v[u][1] : je == 2 ? v[u][2] : v[u][3];
+        const float x = ju == 0 ? xu[0] : ju == 1 ? xu[1] : ju == 2 ? xu[2] : xu[3];
+        if (slot < (uint32_t)kLongSeg) sg[slot] = cand_word(x, i0 + j);
+        ++slot;
+    }
+    if (tid == 0) {
+        uint32_t all = 0, mx = 0;
+        for (int w = 0; w < kTopkWaves; ++w) {
+            all += wtot[w];
+            mx = max(mx, wmax[w]);
+        }
+        seg_info[(int64_t)r * gridDim.x + blockIdx.x] = uint2{all, mx};
+    }
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
+    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens, int k, int chunks,
+    const LongRowState *__restrict__ state, const uint64_t *__restrict__ seg, const uint2 *__restrict__ seg_info,
+    int32_t *__restrict__ out)
+{
+    __shared__ TopkShared sh;
+    __shared__ uint64_t cl[kLongCap];            // the gathered keys, in position order
+    __shared__ uint32_t keep[kLongCap / 32];     // flags of the kept ones
+    __shared__ uint32_t cstart[kMaxLongChunks];  // each chunk's first slot in cl
+    __shared__ uint32_t info[2], ncand;
+    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int n = ctx_lens[r];
+    if (n <= k) return;  // (written by the bound kernel)
+    const float *sr = scores + (int64_t)r * score_stride;
+    int32_t *o = out + (int64_t)r * k;
+    const int nch = (n + kMbChunk - 1) / kMbChunk;  // chunks of this row (<= chunks)
+    // chunk counts, their prefix and the largest key
+    if (wv == 0) {
+        uint32_t run = 0, mx = 0;
+        for (int c0 = 0; c0 < nch; c0 += 64) {
+            const int c = c0 + lane;
+            const uint2 ci = c < nch ? seg_info[(int64_t)r * chunks + c] : uint2{0u, 0u};
+            uint32_t incl = ci.x;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t x = __shfl_up(incl, d);
+                if (lane >= d) incl += x;
+            }
+            if (c < nch) cstart[c] = run + incl - ci.x;
+            run += __shfl(incl, 63);
+            mx = max(mx, ci.y);
+        }
+#pragma unroll
+        for (int d = 32; d >= 1; d >>= 1) mx = max(mx, (uint32_t)__shfl_xor((int)mx, d));
+        if (lane == 0) {
+            info[0] = run;
+            info[1] = mx;
+            ncand = 0;
+        }
+    }
+    for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
+    for (int i = tid; i < kLongCap / 32; i += kTopkThreads) keep[i] = 0;
+    __syncthreads();
+    const int mc = (int)info[0];
+    if (mc < k || mc > kLongCap) {  // (block-uniform) the sample misjudged the row (no segment overflowed)
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+    // the segments, in chunk order, into cl
+    for (int c = wv; c < nch; c += kTopkWaves) {  // (wave-uniform)
+        const uint32_t s0 = cstart[c], cnt = (c + 1 < nch ? cstart[c + 1] : (uint32_t)mc) - s0;
+        const uint64_t *sg = seg + ((int64_t)r * chunks + c) * kLongSeg;
+        for (uint32_t i = lane; i < cnt; i += 64) cl[s0 + i] = sg[i];
+    }
+    __syncthreads();
+    const float tf = state[r].tf;
+    const ScoreBins bin2(tf, key_score(info[1]));
+    for (int i = tid; i < mc; i += kTopkThreads) atomicAdd(&sh.hist[bin2(key_score((uint32_t)(cl[i] >> 32)))], 1u);
+    __syncthreads();
+    uint32_t tbin, above, m;
+    pick_bin_wave(sh, (uint32_t)k, tbin, above, m);
+    if (m > (uint32_t)kCandCap) {  // (block-uniform) massive ties in the threshold bin
+        topk_radix_row(sh, sr, n, k, o);
+        return;
+    }
+    // flag the keys above the threshold bin; list the threshold bin's
+    for (int i = tid; i < mc; i += kTopkThreads) {
+        const uint64_t w = cl[i];
+        const uint32_t bi = bin2(key_score((uint32_t)(w >> 32)));
+        if (bi > tbin) atomicOr(&keep[i >> 5], 1u << (i & 31));
+        else if (bi == tbin) sh.cand[atomicAdd(&ncand, 1u)] = w;  // (< m)
+    }
+    __syncthreads();
+    // the need-th best word of the threshold bin (words are distinct: positions differ)
+    const uint32_t need = (uint32_t)k - above;
+    if (m <= 64) {  // (block-uniform) wave 0 ranks each candidate against all
+        if (wv == 0) {
+            const uint64_t mine = lane < (int)m ? sh.cand[lane] : 0;
+            int rank = 0;
+            for (int j = 0; j < (int)m; ++j) rank += __shfl(mine, j) > mine;
+            if (lane < (int)m && rank == (int)need - 1) sh.cand[kCandCap - 1] = mine;  // (slot past m <= 64)
+        }
+    } else {
+        int P = 1;
+        while (P < (int)m) P <<= 1;
+        for (int i = (int)m + tid; i < P; i += kTopkThreads) sh.cand[i] = 0;
+        __syncthreads();
+        for (int size = 2; size <= P; size <<= 1)
+            for (int j = size >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < P / 2; i += kTopkThreads) {
+                    const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b2 = a | j;
+                    const uint64_t x = sh.cand[a], y = sh.cand[b2];
+                    if (((a & size) == 0) ? (x < y) : (x > y)) {  // descending
+                        sh.cand[a] = y;
+                        sh.cand[b2] = x;
+                    }
+                }
+                __syncthreads();
+            }
+    }
+    __syncthreads();
+    const uint64_t tstar = m <= 64 ? sh.cand[kCandCap - 1] : sh.cand[need - 1];
+    for (int i = tid; i < mc; i += kTopkThreads) {
+        const uint64_t w = cl[i];
+        if (bin2(key_score((uint32_t)(w >> 32))) == tbin && w >= tstar) atomicOr(&keep[i >> 5], 1u << (i & 31));
+    }
+    __syncthreads();
+    // ordered compaction of the kept keys: thread t < mc / 32 takes flag word t (keys 32 t ..)
+    static_assert(kLongCap / 32 <= kTopkThreads, "one flag word per thread");
+    const int words = (mc + 31) / 32;
+    uint32_t wbits = tid < words ? keep[tid] : 0u;
+    const uint32_t cnt = (uint32_t)__popc(wbits);
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const uint32_t x = __shfl_up(incl, d);
+        if (lane >= d) incl += x;
+    }
+    if (lane == 63) sh.wsum[wv] = incl;
+    __syncthreads();
+    uint32_t pos = incl - cnt;
+    for (int w = 0; w < wv; ++w) pos += sh.wsum[w];
+    while (wbits) {
+        const int b = __builtin_ctz(wbits);
+        wbits &= wbits - 1;
+        if (pos < (uint32_t)k) o[pos] = (int)(0xFFFFFFFFu - (uint32_t)cl[32 * tid + b]);
+        ++pos;
+    }
+}
+
 }  // namespace sa

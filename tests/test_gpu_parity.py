@@ -160,6 +160,21 @@ CASES = {
                                                        seed=119, topk=64, idx_int_max=0),
     "decode_all_ties": lambda: synth.small_decode("decode_all_ties", V64, [100, 5000, 9000, 3], seed=120, topk=64,
                                                   idx_int_max=0),
+    # rows over 262144 keys: the three-launch path (sampled bound, gathered
+    # positions, exact selection and an ascending sort of the kept positions),
+    # with shorter rows of the same batch on it too; k not a power of two
+    "decode_very_long": lambda: synth.small_decode("decode_very_long", V64, [300_000, 262_145, 70_001, 5, 0],
+                                                   seed=126),
+    "decode_very_long_k3000": lambda: synth.small_decode("decode_very_long_k3000", V64, [300_001, 5000], seed=127,
+                                                         topk=3000),
+    # every score zero on rows over 262144 keys: the gathered list overflows and
+    # each row takes the one-workgroup radix path
+    "decode_very_long_all_ties": lambda: synth.small_decode("decode_very_long_all_ties", V64,
+                                                            [300_000, 262_145, 70_000, 5], seed=128, topk=64,
+                                                            idx_int_max=0),
+    # k over 4096: the many-workgroup radix select
+    "decode_very_long_k5000": lambda: synth.small_decode("decode_very_long_k5000", V64, [270_000, 6000], seed=129,
+                                                         topk=5000),
 }
 
 
