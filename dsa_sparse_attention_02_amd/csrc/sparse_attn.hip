@@ -523,10 +523,8 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
         uint64_t *seg = (uint64_t *)(lst + batch);  // (16-byte states keep these aligned)
         uint2 *seg_info = (uint2 *)(seg + (size_t)batch * d.mb_chunks * kLongSeg);
         const int32_t *cl = c->context_lens;
-        hipLaunchKernelGGL(topk_long_bound_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride, mm,
-                           d.mm_stride, cl, p->topk, topk_idx, lst, ap);
         hipLaunchKernelGGL(topk_long_gather_kernel, dim3(d.mb_chunks, batch), dim3(kTopkThreads), 0, st, scores,
-                           d.score_stride, cl, p->topk, (const LongRowState *)lst, seg, seg_info);
+                           d.score_stride, mm, d.mm_stride, cl, p->topk, topk_idx, lst, seg, seg_info, ap);
         hipLaunchKernelGGL(topk_long_select_kernel, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
                            cl, p->topk, d.mb_chunks, (const LongRowState *)lst, (const uint64_t *)seg,
                            (const uint2 *)seg_info, topk_idx);

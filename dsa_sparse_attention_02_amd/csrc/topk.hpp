@@ -492,7 +492,8 @@ struct TopkGatherShared {
 // pick_bin over kBins bins by wave 0 alone (lane l sums the 32 bins
 // [kBins - 32 (l + 1), kBins - 32 l), a wave scan runs from the top bins down),
 // then one barrier.  need <= the histogram's total.
-__device__ __forceinline__ void pick_bin_wave(TopkShared &sh, uint32_t need, uint32_t &bin, uint32_t &above,
+template <class Shared>  // (TopkShared, or any with hist[kBins] and pick[3])
+__device__ __forceinline__ void pick_bin_wave(Shared &sh, uint32_t need, uint32_t &bin, uint32_t &above,
                                               uint32_t &count)
 {
     static_assert(kBins == 64 * 32, "32 bins per lane");
@@ -952,33 +953,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_mb_emit_kernel(
 }
 
 // ---------------------------------------------- one pass for very long rows --
-// Rows over kBitmapKeys keys (with 2 k <= kLongCap) in three launches instead
-// of the many-workgroup radix select's nine:
-//  1. per row (topk_long_bound_kernel): a sample of one 32-key tile in every
-//     kLongGap keys (1/64 of the row) is histogrammed over its own range, and
-//     the bound T_f is set where about 1.25 k/64 + 16 sample keys lie above it;
-//  2. per 16384-key chunk (topk_long_gather_kernel): the chunk's keys >= T_f
-//     are written, as (order-preserving key, position) words in ascending
-//     position order, to the chunk's own segment of kLongSeg words, with their
-//     count and largest key;
-//  3. per row (topk_long_select_kernel): if the segments hold at least k and
-//     at most kLongCap keys (none overflowing), the top k of the row are the
-//     top k of those keys (the k-th best key of the row is >= T_f).  They are
-//     read into LDS in position order, binned over [T_f, max], the threshold
-//     bin found by a suffix scan and its keys ranked exactly (score, then the
-//     lower position); the kept keys, flagged in order, are compacted into the
-//     output, which is then ascending without a sort.  Otherwise the row takes
-//     the radix path of one workgroup (exact; slow on such rows, and only
-//     where the sample misjudged the row or scores tie massively).
+// Rows over kBitmapKeys keys (with 2 k <= kLongCap, up to kMaxLongChunks
+// chunks) in two launches instead of the many-workgroup radix select's nine:
+//  1. per 16384-key chunk (topk_long_gather_kernel): the bound T_f of the row
+//     is set from a sample, one 32-key tile in every kLongGap keys (1/64 of the
+//     row), histogrammed over its own range, where about 1.25 k/64 + 16 sample
+//     keys lie above it.  Every chunk of the row computes the same bound from
+//     the same sample (chunk 0 stores it); its own keys are read meanwhile.
+//     The chunk's keys >= T_f are then written, as (order-preserving key,
+//     position) words in ascending position order, to the chunk's own segment
+//     of kLongSeg words, with their count and largest key;
+//  2. per row (topk_long_select_kernel): if the segments hold at least k and
+//     at most kLongCap keys, the top k of the row are the top k of those keys
+//     (the k-th best key of the row is >= T_f).  Each thread takes 8
+//     consecutive ones of them into registers; they are binned over [T_f, max],
+//     the threshold bin found by a suffix scan and its keys ranked exactly
+//     (score, then the lower position); the kept keys are compacted in order
+//     into the output, which is thus ascending without a sort.  Otherwise the
+//     row takes the radix path of one workgroup (exact; slow on such rows, and
+//     only where the sample misjudged the row or scores tie massively).
 // The segments take 8 bytes per key of the row: twice the scores' space.
-constexpr int kLongCap = 8192;  // gathered keys a row may select from
+constexpr int kLongCap = 8192;        // gathered keys a row may select from
 constexpr int kMaxLongChunks = 1024;  // 16384-key chunks a row may have (16M keys)
-constexpr int kLongGap = 2048;  // keys from one sample tile to the next
-constexpr int kLongSeg = kLongCap;  // gathered keys a chunk may hold (more than this: more than kLongCap)
+constexpr int kLongGap = 2048;        // keys from one sample tile to the next
+constexpr int kLongSeg = kLongCap;    // gathered keys a chunk may hold (more than this: more than kLongCap)
+constexpr int kLongPerThread = kLongCap / kTopkThreads;  // gathered keys per selecting thread
 
 struct LongRowState {
     float tf;  // the bound
     uint32_t pad[3];
+};
+
+struct LongGatherShared {
+    uint32_t hist[kBins];
+    uint32_t pick[4];
+    float red[2][kTopkWaves];
+    uint32_t wtot[kTopkWaves], wmax[kTopkWaves];
 };
 
 // inverse of score_key
@@ -987,33 +997,29 @@ __device__ __forceinline__ float key_score(uint32_t key)
     return __uint_as_float((key & 0x80000000u) ? (key & 0x7FFFFFFFu) : ~key);
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_long_bound_kernel(
-    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
-    const int32_t *__restrict__ ctx_lens, int k, int32_t *__restrict__ out, LongRowState *__restrict__ state,
-    const AppendArgs ap)
+// The bound T_f of a row of n > k keys (every thread gets it).  Sample tile j:
+// keys [kLongGap j, kLongGap j + 32), tile entry kLongGap j / 32 of the ranges;
+// thread t reads 4 keys of tile (t >> 3) + 128 q.  (A score row is allocated
+// to a multiple of 64 keys, so a 16-byte piece of a tile that starts below n
+// is read whole; keys at n and beyond are never counted.)
+__device__ __forceinline__ float long_row_bound(LongGatherShared &sh, const float *__restrict__ sr,
+                                                const f32x2 *__restrict__ mm, int n, int k)
 {
-    __shared__ TopkShared sh;
-    const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    append_rows(ap, r, tid, kTopkThreads);  // (row r = sequence r; before the attention reads it)
-    const int n = ctx_lens[r];
-    if (n <= k) {  // (block-uniform) the whole row
-        int32_t *o = out + (int64_t)r * k;
-        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
-        return;
-    }
-    const float *sr = scores + (int64_t)r * score_stride;
-    const f32x2 *mm = tile_mm + (int64_t)r * mm_stride;
-    // sample tile j: keys [kLongGap j, kLongGap j + 32), tile entry kLongGap j / 32
-    // of the ranges; thread t reads 4 keys of tile (t >> 3) + 128 q.  (A score
-    // row is allocated to a multiple of 64 keys, so a 16-byte piece of a tile
-    // that starts below n is read whole; keys at n and beyond are never counted.)
+    static_assert(kTopkThreads == 1024, "128 sample tiles per 4-load round");
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int ns = (n + kLongGap - 1) / kLongGap;
-    const int sx = 4 * (tid & 7);
+    const int sx = 4 * (tid & 7), j0 = tid >> 3;
+    // the first round's samples are read before the range is known (rows of up
+    // to 512 tiles take one round; tiles past the last are read as the last one,
+    // and not counted)
+    f32x4 v[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4 *>(sr + (int64_t)kLongGap * min(j0 + 128 * q, ns - 1) + sx);
     float lo = INFINITY, hi = -INFINITY;
     for (int j = tid; j < ns; j += kTopkThreads) {
-        const f32x2 v = mm[(int64_t)j * (kLongGap / 32)];
-        lo = fminf(lo, v[0]);
-        hi = fmaxf(hi, v[1]);
+        const f32x2 m = mm[(int64_t)j * (kLongGap / 32)];
+        lo = fminf(lo, m[0]);
+        hi = fmaxf(hi, m[1]);
     }
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) {
@@ -1033,48 +1039,61 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_bound_kernel(
         hi = fmaxf(hi, sh.red[1][w]);
     }
     const ScoreBins bin_of(lo, hi);
-    for (int j0 = tid >> 3; j0 < ns; j0 += 4 * (kTopkThreads / 8)) {
-        f32x4 v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q)  // (tiles past the last are read as the last one, and not counted)
-            v[q] = *reinterpret_cast<const f32x4 *>(sr + (int64_t)kLongGap * min(j0 + 128 * q, ns - 1) + sx);
+    for (int jr = j0;;) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-            const int j = j0 + 128 * q, i0 = kLongGap * j + sx;
+            const int j = jr + 128 * q, i0 = kLongGap * j + sx;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 if (j < ns && i0 + e < n) atomicAdd(&sh.hist[bin_of(v[q][e])], 1u);
         }
+        jr += 512;
+        if (jr >= ns) break;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = *reinterpret_cast<const f32x4 *>(sr + (int64_t)kLongGap * min(jr + 128 * q, ns - 1) + sx);
     }
     __syncthreads();
     const int nsamp = 32 * (ns - 1) + min(32, n - kLongGap * (ns - 1));
     const uint32_t want = (uint32_t)min(nsamp, (int)ceilf(1.25f * (float)k * (float)nsamp / (float)n) + 16);
     uint32_t b, above, cnt;
     pick_bin_wave(sh, want, b, above, cnt);
-    if (tid == 0) state[r] = LongRowState{bin_of.scale > 0.0f ? lo + (float)b / bin_of.scale : lo, {0u, 0u, 0u}};
+    return bin_of.scale > 0.0f ? lo + (float)b / bin_of.scale : lo;
 }
 
 // Chunk c of row r: keys [16384 c, 16384 c + 16384); wave w takes keys
 // [1024 w, 1024 w + 1024) of it, lane l the 16 consecutive keys 16 l ..
 // (four 16-byte loads), so lane order, then wave order, is position order.
 // seg: [rows][chunks][kLongSeg] words; seg_info: [rows][chunks] (count, largest key).
+// Chunk 0 of each row also writes the row's new cache entries (before the
+// attention reads them) and the whole row's positions when it has <= k keys.
 __global__ __launch_bounds__(kTopkThreads) void topk_long_gather_kernel(
-    const float *__restrict__ scores, int64_t score_stride, const int32_t *__restrict__ ctx_lens, int k,
-    const LongRowState *__restrict__ state, uint64_t *__restrict__ seg, uint2 *__restrict__ seg_info)
+    const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
+    const int32_t *__restrict__ ctx_lens, int k, int32_t *__restrict__ out, LongRowState *__restrict__ state,
+    uint64_t *__restrict__ seg, uint2 *__restrict__ seg_info, const AppendArgs ap)
 {
-    __shared__ uint32_t wtot[kTopkWaves], wmax[kTopkWaves];
-    const int r = blockIdx.y, n = ctx_lens[r], tid = threadIdx.x, lane = tid & 63;
+    __shared__ LongGatherShared sh;
+    const int r = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
     const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (blockIdx.x == 0) append_rows(ap, r, tid, kTopkThreads);
+    const int n = ctx_lens[r];
     const int c0 = blockIdx.x * kMbChunk;
-    if (n <= k || c0 >= n) return;  // (block-uniform)
+    if (n <= k) {  // (block-uniform) the whole row
+        if (blockIdx.x == 0) {
+            int32_t *o = out + (int64_t)r * k;
+            for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
+        }
+        return;
+    }
+    if (c0 >= n) return;  // (block-uniform)
     static_assert(kMbChunk == 1024 * kTopkWaves, "one 1024-key round per wave");
-    const float tf = state[r].tf;
     const float *sr = scores + (int64_t)r * score_stride;
     const int n64 = (n + 63) & ~63;
     const int i0 = c0 + 1024 * wv + 16 * lane;
     f32x4 v[4];  // (pieces past the row's allocation re-read its last one: never gathered)
 #pragma unroll
     for (int u = 0; u < 4; ++u) v[u] = *reinterpret_cast<const f32x4 *>(sr + min(i0 + 4 * u, n64 - 4));
+    const float tf = long_row_bound(sh, sr, tile_mm + (int64_t)r * mm_stride, n, k);
+    if (blockIdx.x == 0 && tid == 0) state[r] = LongRowState{tf, {0u, 0u, 0u}};
     uint32_t bits = 0, kmax = 0;  // gathered keys (bit j: key i0 + j); the largest one's order-preserving key
 #pragma unroll
     for (int u = 0; u < 4; ++u)
@@ -1095,12 +1114,12 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_gather_kernel(
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d));
     if (lane == 0) {
-        wtot[wv] = tot;
-        wmax[wv] = kmax;
+        sh.wtot[wv] = tot;
+        sh.wmax[wv] = kmax;
     }
     __syncthreads();
     uint32_t slot = pre;
-    for (int w = 0; w < wv; ++w) slot += wtot[w];
+    for (int w = 0; w < wv; ++w) slot += sh.wtot[w];
     uint64_t *sg = seg + ((int64_t)r * gridDim.x + blockIdx.x) * kLongSeg;
     while (bits) {
         const int j = __builtin_ctz(bits);
@@ -1116,8 +1135,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_gather_kernel(
     if (tid == 0) {
         uint32_t all = 0, mx = 0;
         for (int w = 0; w < kTopkWaves; ++w) {
-            all += wtot[w];
-            mx = max(mx, wmax[w]);
+            all += sh.wtot[w];
+            mx = max(mx, sh.wmax[w]);
         }
         seg_info[(int64_t)r * gridDim.x + blockIdx.x] = uint2{all, mx};
     }
@@ -1129,13 +1148,15 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
     int32_t *__restrict__ out)
 {
     __shared__ TopkShared sh;
-    __shared__ uint64_t cl[kLongCap];            // the gathered keys, in position order
-    __shared__ uint32_t keep[kLongCap / 32];     // flags of the kept ones
-    __shared__ uint32_t cstart[kMaxLongChunks];  // each chunk's first slot in cl
+    __shared__ uint32_t cstart[kMaxLongChunks];  // each chunk's first gathered key
     __shared__ uint32_t info[2], ncand;
     const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    // (the bound and the first chunk counts are read with n; rows of n <= k
+    // have neither, and return)
+    const float tf = state[r].tf;
+    const uint2 ci0 = wv == 0 ? seg_info[(int64_t)r * chunks + min(lane, chunks - 1)] : uint2{0u, 0u};
     const int n = ctx_lens[r];
-    if (n <= k) return;  // (written by the bound kernel)
+    if (n <= k) return;  // (written by the gathering launch)
     const float *sr = scores + (int64_t)r * score_stride;
     int32_t *o = out + (int64_t)r * k;
     const int nch = (n + kMbChunk - 1) / kMbChunk;  // chunks of this row (<= chunks)
@@ -1144,7 +1165,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
         uint32_t run = 0, mx = 0;
         for (int c0 = 0; c0 < nch; c0 += 64) {
             const int c = c0 + lane;
-            const uint2 ci = c < nch ? seg_info[(int64_t)r * chunks + c] : uint2{0u, 0u};
+            uint2 ci = c0 == 0 ? ci0 : seg_info[(int64_t)r * chunks + min(c, chunks - 1)];
+            if (c >= nch) ci = uint2{0u, 0u};
             uint32_t incl = ci.x;
 #pragma unroll
             for (int d = 1; d < 64; d <<= 1) {
@@ -1164,23 +1186,42 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
         }
     }
     for (int i = tid; i < kBins; i += kTopkThreads) sh.hist[i] = 0;
-    for (int i = tid; i < kLongCap / 32; i += kTopkThreads) keep[i] = 0;
     __syncthreads();
     const int mc = (int)info[0];
     if (mc < k || mc > kLongCap) {  // (block-uniform) the sample misjudged the row (no segment overflowed)
         topk_radix_row(sh, sr, n, k, o);
         return;
     }
-    // the segments, in chunk order, into cl
-    for (int c = wv; c < nch; c += kTopkWaves) {  // (wave-uniform)
-        const uint32_t s0 = cstart[c], cnt = (c + 1 < nch ? cstart[c + 1] : (uint32_t)mc) - s0;
-        const uint64_t *sg = seg + ((int64_t)r * chunks + c) * kLongSeg;
-        for (uint32_t i = lane; i < cnt; i += 64) cl[s0 + i] = sg[i];
+    // gathered keys [8 t, 8 t + 8) of the row, in position order, to thread t:
+    // the chunk holding key 8 t by a binary search of the chunk starts, then on
+    static_assert(kLongPerThread == 8, "8 gathered keys per thread");
+    const int s0 = kLongPerThread * tid;
+    int c = 0;
+    if (s0 < mc) {
+        int hi = nch;  // the last chunk starting at or below s0 is in [c, hi)
+        while (hi - c > 1) {
+            const int mid = (c + hi) >> 1;
+            if (cstart[mid] <= (uint32_t)s0) c = mid;
+            else hi = mid;
+        }
     }
-    __syncthreads();
-    const float tf = state[r].tf;
+    uint64_t w[kLongPerThread];
+#pragma unroll
+    for (int e = 0; e < kLongPerThread; ++e) {
+        const int s = s0 + e;
+        w[e] = 0;
+        if (s < mc) {
+            while (c + 1 < nch && cstart[c + 1] <= (uint32_t)s) ++c;
+            w[e] = seg[((int64_t)r * chunks + c) * kLongSeg + (s - (int)cstart[c])];
+        }
+    }
     const ScoreBins bin2(tf, key_score(info[1]));
-    for (int i = tid; i < mc; i += kTopkThreads) atomicAdd(&sh.hist[bin2(key_score((uint32_t)(cl[i] >> 32)))], 1u);
+    uint32_t bi[kLongPerThread];
+#pragma unroll
+    for (int e = 0; e < kLongPerThread; ++e) {
+        bi[e] = bin2(key_score((uint32_t)(w[e] >> 32)));
+        if (s0 + e < mc) atomicAdd(&sh.hist[bi[e]], 1u);
+    }
     __syncthreads();
     uint32_t tbin, above, m;
     pick_bin_wave(sh, (uint32_t)k, tbin, above, m);
@@ -1188,24 +1229,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
         topk_radix_row(sh, sr, n, k, o);
         return;
     }
-    // flag the keys above the threshold bin; list the threshold bin's
-    for (int i = tid; i < mc; i += kTopkThreads) {
-        const uint64_t w = cl[i];
-        const uint32_t bi = bin2(key_score((uint32_t)(w >> 32)));
-        if (bi > tbin) atomicOr(&keep[i >> 5], 1u << (i & 31));
-        else if (bi == tbin) sh.cand[atomicAdd(&ncand, 1u)] = w;  // (< m)
-    }
+    // the threshold bin's keys, then the need-th best of them (words are
+    // distinct: positions differ)
+#pragma unroll
+    for (int e = 0; e < kLongPerThread; ++e)
+        if (s0 + e < mc && bi[e] == tbin) sh.cand[atomicAdd(&ncand, 1u)] = w[e];  // (< m)
     __syncthreads();
-    // the need-th best word of the threshold bin (words are distinct: positions differ)
     const uint32_t need = (uint32_t)k - above;
     if (m <= 64) {  // (block-uniform) wave 0 ranks each candidate against all
         if (wv == 0) {
             const uint64_t mine = lane < (int)m ? sh.cand[lane] : 0;
             int rank = 0;
             for (int j = 0; j < (int)m; ++j) rank += __shfl(mine, j) > mine;
-            if (lane < (int)m && rank == (int)need - 1) sh.cand[kCandCap - 1] = mine;  // (slot past m <= 64)
+            if (lane < (int)m && rank == (int)need - 1) sh.cand[kCandCap - 1] = mine;  // (a slot past m <= 64)
         }
-    } else {
+    } else {  // bitonic sort, descending, of the m (<= kCandCap) candidates padded to a power of two
         int P = 1;
         while (P < (int)m) P <<= 1;
         for (int i = (int)m + tid; i < P; i += kTopkThreads) sh.cand[i] = 0;
@@ -1215,7 +1253,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
                 for (int i = tid; i < P / 2; i += kTopkThreads) {
                     const int a = ((i & ~(j - 1)) << 1) | (i & (j - 1)), b2 = a | j;
                     const uint64_t x = sh.cand[a], y = sh.cand[b2];
-                    if (((a & size) == 0) ? (x < y) : (x > y)) {  // descending
+                    if (((a & size) == 0) ? (x < y) : (x > y)) {
                         sh.cand[a] = y;
                         sh.cand[b2] = x;
                     }
@@ -1225,32 +1263,29 @@ __global__ __launch_bounds__(kTopkThreads) void topk_long_select_kernel(
     }
     __syncthreads();
     const uint64_t tstar = m <= 64 ? sh.cand[kCandCap - 1] : sh.cand[need - 1];
-    for (int i = tid; i < mc; i += kTopkThreads) {
-        const uint64_t w = cl[i];
-        if (bin2(key_score((uint32_t)(w >> 32))) == tbin && w >= tstar) atomicOr(&keep[i >> 5], 1u << (i & 31));
-    }
-    __syncthreads();
-    // ordered compaction of the kept keys: thread t < mc / 32 takes flag word t (keys 32 t ..)
-    static_assert(kLongCap / 32 <= kTopkThreads, "one flag word per thread");
-    const int words = (mc + 31) / 32;
-    uint32_t wbits = tid < words ? keep[tid] : 0u;
-    const uint32_t cnt = (uint32_t)__popc(wbits);
-    uint32_t incl = cnt;
+    // kept: above the threshold bin, or in it and not below the need-th best
+    uint32_t kb = 0;
 #pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-        const uint32_t x = __shfl_up(incl, d);
-        if (lane >= d) incl += x;
+    for (int e = 0; e < kLongPerThread; ++e)
+        kb |= (s0 + e < mc && (bi[e] > tbin || (bi[e] == tbin && w[e] >= tstar))) ? 1u << e : 0u;
+    const uint32_t cnt = (uint32_t)__popc(kb);  // <= 8: four bits
+    uint32_t pre = 0, tot = 0;
+#pragma unroll
+    for (int bt = 0; bt < 4; ++bt) {
+        const uint64_t mb = __ballot((cnt >> bt) & 1u);
+        pre += __builtin_amdgcn_mbcnt_hi((uint32_t)(mb >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mb, 0u)) << bt;
+        tot += (uint32_t)__popcll(mb) << bt;
     }
-    if (lane == 63) sh.wsum[wv] = incl;
+    if (lane == 0) sh.wsum[wv] = tot;
     __syncthreads();
-    uint32_t pos = incl - cnt;
-    for (int w = 0; w < wv; ++w) pos += sh.wsum[w];
-    while (wbits) {
-        const int b = __builtin_ctz(wbits);
-        wbits &= wbits - 1;
-        if (pos < (uint32_t)k) o[pos] = (int)(0xFFFFFFFFu - (uint32_t)cl[32 * tid + b]);
-        ++pos;
-    }
+    uint32_t pos = pre;
+    for (int v = 0; v < wv; ++v) pos += sh.wsum[v];
+#pragma unroll
+    for (int e = 0; e < kLongPerThread; ++e)
+        if ((kb >> e) & 1u) {
+            if (pos < (uint32_t)k) o[pos] = (int)(0xFFFFFFFFu - (uint32_t)w[e]);
+            ++pos;
+        }
 }
 
 }  // namespace sa

@@ -186,6 +186,47 @@ def test_parity_small(dev, name):
     compare(w, run_gpu(dev, w), tag=name)
 
 
+def _key_rows(w, b, pos):
+    """(physical block, slot) of sequence b's logical positions pos."""
+    bs = w["shape"].block_size
+    pos = np.asarray(pos, dtype=np.int64)
+    return w["block_table"][b, pos // bs], pos % bs
+
+
+def long_branch_case(kind):
+    """Rows over 262144 keys whose scores defeat the sampled bound of the long-row
+    selection, or tie in bulk around the k-th best key (row 0; row 1 is plain)."""
+    w = synth.make(synth.small_decode(f"decode_long_{kind}", V64, [300_000, 270_000], seed=130))
+    ik = w["idx_k"].copy()
+    n, k = int(w["context_lens"][0]), w["shape"].topk
+    if kind == "sample_misses":
+        # the keys of the sampled tiles (the first 32 of every 2048) score 4x
+        # (integer entries stay exact in bf16): the bound lands among them and
+        # fewer than k keys of the row reach it
+        pos = np.arange(n)
+        blk, slot = _key_rows(w, 0, pos[pos % 2048 < 32])
+        ik[blk, slot] = synth.f32_to_bf16_bits(synth.bf16_bits_to_f32(ik[blk, slot]) * 4)
+    else:
+        # copies of the key ranked k - 200 at random positions: that many keys
+        # tie around the k-th best (500: ranked in LDS; 3000: more than the
+        # candidate list holds)
+        m = {"ties_500": 500, "ties_3000": 3000}[kind]
+        s = oracle.run(w, rows=[0], want_scores=True)["scores"][0][:n].astype(np.float64)
+        src = np.lexsort((np.arange(n), -s))[k - 200]
+        dst = np.random.default_rng(31).choice(np.setdiff1d(np.arange(n), [src]), m, replace=False)
+        sb, ss = _key_rows(w, 0, [src])
+        db, ds = _key_rows(w, 0, dst)
+        ik[db, ds] = ik[sb[0], ss[0]]
+    return dict(w, idx_k=ik)
+
+
+@pytest.mark.parametrize("kind", ["sample_misses", "ties_500", "ties_3000"])
+def test_decode_long_row_branches(dev, kind):
+    say(f"[gpu] long-row selection branch {kind}")
+    w = long_branch_case(kind)
+    compare(w, run_gpu(dev, w), tag=f"decode_long_{kind}")
+
+
 @pytest.mark.parametrize("name", ["decode_ragged", "prefill_2500", "tiny_prefill_L256"])
 def test_staged_equals_fused_and_deterministic(dev, name):
     spec = CASES[name]()
