@@ -1339,8 +1339,9 @@ sa_status sparse_attn_decode_noalloc(const sa_params *p, const sa_paged_cache *c
     void *ws = nullptr;
     if ((s = scratch_address(&ws)) != SA_OK) return s;
     // every kernel of the decode writes the scratch it reads (the many-workgroup
-    // top-k clears its histograms in its first launch), so the previous call's
-    // contents need no clearing
+    // top-k clears its histograms in its first launch; the long-row top-k's
+    // select reads only the counts its gathering launch wrote), so the previous
+    // call's contents need no clearing
     return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, ws, SA_NOALLOC_SCRATCH_BYTES,
                        stream, nullptr);
 }

@@ -972,7 +972,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_mb_emit_kernel(
 //     into the output, which is thus ascending without a sort.  Otherwise the
 //     row takes the radix path of one workgroup (exact; slow on such rows, and
 //     only where the sample misjudged the row or scores tie massively).
-// The segments take 8 bytes per key of the row: twice the scores' space.
+// The segments take 4 bytes per key of the row (8 per gathered key, room for
+// half of each chunk), as much as its scores.
 constexpr int kLongCap = 8192;        // gathered keys a row may select from
 constexpr int kMaxLongChunks = 1024;  // 16384-key chunks a row may have (16M keys)
 constexpr int kLongGap = 2048;        // keys from one sample tile to the next
