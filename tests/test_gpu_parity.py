@@ -348,6 +348,7 @@ FULL_ROWS = {
     "decode_b32_ctx8k": None,                        # every row
     "decode_b64_ctx16k_128k": None,                  # every row
     "decode_b4_ctx1m": None,                         # every row
+    "decode_b64_ctx128k_full": None,                 # every row
     "prefill_L32k": _prefill_rows(),
     "prefill_varlen_8x4k": _prefill_rows(seed=172),
 }
