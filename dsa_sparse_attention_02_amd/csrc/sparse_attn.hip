@@ -159,7 +159,7 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_spli
     // many-workgroup top-k state: per row a MbRowState, 3 digit histograms and
     // two counts per chunk
     // (or, for k <= kLongCap / 2 and rows of at most kMaxLongChunks chunks, the
-    // three-launch path's per-row state, per-chunk counts and key segments)
+    // two-launch path's per-row state, per-chunk counts and key segments)
     d.off_mb = off;
     d.mb_chunks = max_ctx > kBitmapKeys ? (max_ctx + kMbChunk - 1) / kMbChunk : 0;
     if (d.mb_chunks > 0) {

@@ -160,8 +160,8 @@ CASES = {
                                                        seed=119, topk=64, idx_int_max=0),
     "decode_all_ties": lambda: synth.small_decode("decode_all_ties", V64, [100, 5000, 9000, 3], seed=120, topk=64,
                                                   idx_int_max=0),
-    # rows over 262144 keys: the three-launch path (sampled bound, gathered
-    # positions, exact selection and an ascending sort of the kept positions),
+    # rows over 262144 keys: the two-launch path (per-chunk gather above a
+    # sampled bound, one exact selection per row with an ordered compaction),
     # with shorter rows of the same batch on it too; k not a power of two
     "decode_very_long": lambda: synth.small_decode("decode_very_long", V64, [300_000, 262_145, 70_001, 5, 0],
                                                    seed=126),
