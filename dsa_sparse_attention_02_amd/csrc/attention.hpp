@@ -221,29 +221,22 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
 
     const int head = 32 * (HB * hg + hb) + col;
     const bool hok = head < a.num_heads;
-    // q^T operand of step ks (of this partner's half) for this lane:
-    // q[head][16(KP px + ks) + 8half .. +7] (issued first: these loads overlap
-    // the row look-ups below).  Lanes of heads past num_heads load the last
-    // head instead: their S^T columns feed only their own, never stored, output
-    // columns.
-    bf16x8 qb[KP];
-    {
-        const int qhead = hok ? head : a.num_heads - 1;
-        const uint16_t *qp = a.q + ((int64_t)r * a.num_heads + qhead) * QK + 16 * KP * px + 8 * half;
-#pragma unroll
-        for (int ks = 0; ks < KP; ++ks) qb[ks] = as_bf16x8(load16(qp + 16 * ks));
-    }
-
     // Physical row of every kept token of this split (kNoRow = padding) and a
     // validity mask per 32-token tile.  Positions, then block-table entries, are
     // loaded 8 per thread at a time, so the look-ups cost two memory round trips.
-    for (int jb = 0; jb < ntiles * 32; jb += 8 * nthreads) {
-        int idx[8], blk[8];
+    // The first round's positions are loaded before the queries below: memory
+    // loads complete in issue order, so waiting for positions issued after the
+    // queries would also wait for the queries (73 KB per workgroup), while this
+    // way the queries arrive during the block-table round trip.
+    auto load_positions = [&](int jb, int (&idx)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = jb + u * nthreads + threadIdx.x;
             idx[u] = j < cnt ? sel[j] : -1;
         }
+    };
+    auto look_up = [&](int jb, const int (&idx)[8]) {
+        int blk[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const bool ok = idx[u] >= 0 && idx[u] < limit;
@@ -260,6 +253,27 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             if (lane == 0 && w0 < ntiles) vbits[w0] = (uint32_t)m;
             if (lane == 32 && w0 + 1 < ntiles) vbits[w0 + 1] = (uint32_t)(m >> 32);
         }
+    };
+    int idx0[8];
+    load_positions(0, idx0);
+
+    // q^T operand of step ks (of this partner's half) for this lane:
+    // q[head][16(KP px + ks) + 8half .. +7].  Lanes of heads past num_heads load
+    // the last head instead: their S^T columns feed only their own, never
+    // stored, output columns.
+    bf16x8 qb[KP];
+    {
+        const int qhead = hok ? head : a.num_heads - 1;
+        const uint16_t *qp = a.q + ((int64_t)r * a.num_heads + qhead) * QK + 16 * KP * px + 8 * half;
+#pragma unroll
+        for (int ks = 0; ks < KP; ++ks) qb[ks] = as_bf16x8(load16(qp + 16 * ks));
+    }
+
+    if (ntiles > 0) look_up(0, idx0);  // (block-uniform)
+    for (int jb = 8 * nthreads; jb < ntiles * 32; jb += 8 * nthreads) {  // (splits of more than 8 tokens per thread)
+        int idx[8];
+        load_positions(jb, idx);
+        look_up(jb, idx);
     }
     if (threadIdx.x == 0) {
         first_tile = kAttnMaxSplitTokens;
