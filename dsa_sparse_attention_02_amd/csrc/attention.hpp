@@ -55,6 +55,7 @@
 namespace sa {
 
 constexpr int kAttnMaxSplitTokens = 2048;
+constexpr uint32_t kNoRow = 0xFFFFFFFFu;
 // Rows keeping fewer keys than this multiply V by P as a hi/lo pair of bf16
 // values.  A row's output error from rounding P to bf16 alone is about
 // 2^-9 / sqrt(effective keys) of its values, which for rows of a few keys is
@@ -66,7 +67,6 @@ struct AttnArgs {
     const uint16_t *kv;          // [num_blocks][bs][QK]
     const int32_t *block_table;  // [seqs][max_blocks]
     const int32_t *topk_idx;     // [rows][k]
-    const uint32_t *rows_in;     // [rows][k] cache rows of the kept tokens (kNoRow: none), or null: from topk_idx
     const int32_t *ctx_lens;     // decode: [rows]
     float *part_o;               // splits > 1: [rows][splits][H][V]
     float *part_ml;              // splits > 1: [rows][splits][H][4]  (max in log2 units, rounded sum, exact sum, 0)
@@ -235,18 +235,6 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             idx[u] = j < cnt ? sel[j] : -1;
         }
     };
-    auto put_rows = [&](int jb, const uint32_t (&rw)[8]) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const int j = jb + u * nthreads + threadIdx.x;
-            const uint32_t row = rw[u];
-            const uint64_t m = __ballot(row != kNoRow);
-            if (j < ntiles * 32) rows[j] = row;
-            const int w0 = (j - lane) >> 5;  // this wave's 64 tokens are tiles w0, w0 + 1
-            if (lane == 0 && w0 < ntiles) vbits[w0] = (uint32_t)m;
-            if (lane == 32 && w0 + 1 < ntiles) vbits[w0 + 1] = (uint32_t)(m >> 32);
-        }
-    };
     auto look_up = [&](int jb, const int (&idx)[8]) {
         int blk[8];
 #pragma unroll
@@ -254,28 +242,20 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             const bool ok = idx[u] >= 0 && idx[u] < limit;
             blk[u] = ok ? tbl[idx[u] >> a.bs_log2] : -1;
         }
-        uint32_t rw[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool ok = blk[u] >= 0 && blk[u] < a.num_blocks;
-            rw[u] = ok ? ((uint32_t)blk[u] << a.bs_log2) | (uint32_t)(idx[u] & bmask) : kNoRow;
-        }
-        put_rows(jb, rw);
-    };
-    // Rows the decode top-k wrote for this call (one round trip), loaded before
-    // the queries as above.
-    const uint32_t *rin = a.rows_in ? a.rows_in + (int64_t)r * a.k + j0 : nullptr;
-    auto load_rows = [&](int jb, uint32_t (&rw)[8]) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             const int j = jb + u * nthreads + threadIdx.x;
-            rw[u] = j < cnt ? rin[j] : kNoRow;
+            const bool ok = blk[u] >= 0 && blk[u] < a.num_blocks;
+            const uint32_t row = ok ? ((uint32_t)blk[u] << a.bs_log2) | (uint32_t)(idx[u] & bmask) : kNoRow;
+            const uint64_t m = __ballot(row != kNoRow);
+            if (j < ntiles * 32) rows[j] = row;
+            const int w0 = (j - lane) >> 5;  // this wave's 64 tokens are tiles w0, w0 + 1
+            if (lane == 0 && w0 < ntiles) vbits[w0] = (uint32_t)m;
+            if (lane == 32 && w0 + 1 < ntiles) vbits[w0 + 1] = (uint32_t)(m >> 32);
         }
     };
     int idx0[8];
-    uint32_t rw0[8];
-    if (rin) load_rows(0, rw0);  // (launch-uniform)
-    else load_positions(0, idx0);
+    load_positions(0, idx0);
 
     // q^T operand of step ks (of this partner's half) for this lane:
     // q[head][16(KP px + ks) + 8half .. +7].  Lanes of heads past num_heads load
@@ -289,20 +269,11 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         for (int ks = 0; ks < KP; ++ks) qb[ks] = as_bf16x8(load16(qp + 16 * ks));
     }
 
-    if (rin) {
-        if (ntiles > 0) put_rows(0, rw0);  // (block-uniform)
-        for (int jb = 8 * nthreads; jb < ntiles * 32; jb += 8 * nthreads) {  // (more than 8 tokens per thread)
-            uint32_t rw[8];
-            load_rows(jb, rw);
-            put_rows(jb, rw);
-        }
-    } else {
-        if (ntiles > 0) look_up(0, idx0);  // (block-uniform)
-        for (int jb = 8 * nthreads; jb < ntiles * 32; jb += 8 * nthreads) {  // (more than 8 tokens per thread)
-            int idx[8];
-            load_positions(jb, idx);
-            look_up(jb, idx);
-        }
+    if (ntiles > 0) look_up(0, idx0);  // (block-uniform)
+    for (int jb = 8 * nthreads; jb < ntiles * 32; jb += 8 * nthreads) {  // (splits of more than 8 tokens per thread)
+        int idx[8];
+        load_positions(jb, idx);
+        look_up(jb, idx);
     }
     if (threadIdx.x == 0) {
         first_tile = kAttnMaxSplitTokens;

@@ -15,10 +15,6 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define SA_LDS __attribute__((address_space(3)))
 
-// A kept-token slot without a cache row (padding, or a position whose block is
-// not in the pool)
-constexpr uint32_t kNoRow = 0xFFFFFFFFu;
-
 constexpr int kWave = 64;
 
 // D(32x32 fp32) += A(32x16 bf16) * B(16x32 bf16).  Lane l supplies row l%32 of A

@@ -116,10 +116,9 @@ AttnLaunch attn_launch(const sa_params *p)
 struct DecodePlan {
     int64_t score_stride, mm_stride;  // floats per score row; tiles per min/max row
     int splits, tokens_per_split, scan_blocks;
-    size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, off_rows, total;
+    size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
     int topk_path;  // SA_TOPK_*: which decode rows take the one-pass top-k, and its unroll
-    bool emit_rows;  // the one-workgroup top-k writes the kept tokens' cache rows for the attention
 };
 
 // want_splits > 0 asks for that many attention splits per row (clamped to
@@ -168,10 +167,6 @@ DecodePlan plan_decode(const sa_params *p, int batch, int max_ctx, int want_spli
         const size_t lp = (size_t)batch * (sizeof(LongRowState) + (size_t)d.mb_chunks * (8 + (size_t)kLongSeg * 8));
         off = align_up(off + std::max(mb, lp), kAlign);
     }
-    // cache rows of the kept tokens [batch][k] (rows of at most kRowTableCap blocks)
-    d.off_rows = off;
-    d.emit_rows = d.mb_chunks == 0 && (int64_t)(std::max(max_ctx, 1) - 1) / p->block_size + 1 <= kRowTableCap;
-    if (d.emit_rows) off = align_up(off + (size_t)batch * k * 4, kAlign);
     d.total = std::max(off, kAlign);
     return d;
 }
@@ -555,29 +550,20 @@ void select_decode(const sa_params *p, const sa_paged_cache *c, int batch, int m
         const int k = p->topk;
         const int onepass_min = d.topk_path == SA_TOPK_THRESHOLD ? INT_MAX
                                 : d.topk_path == SA_TOPK_DEFAULT ? kOnePassMinPerK * k : 0;
-        uint32_t *rows = d.emit_rows ? (uint32_t *)((char *)ws + d.off_rows) : nullptr;
-        const int bsl = ilog2(p->block_size);
         if (d.topk_path == SA_TOPK_ONEPASS_U4)
             hipLaunchKernelGGL(topk_decode_kernel<4>, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
-                               mm, d.mm_stride, c->context_lens, k, onepass_min, topk_idx, ap, c->block_table,
-                               c->max_blocks_per_seq, bsl, c->num_blocks, rows);
+                               mm, d.mm_stride, c->context_lens, k, onepass_min, topk_idx, ap);
         else
             hipLaunchKernelGGL(topk_decode_kernel<2>, dim3(batch), dim3(kTopkThreads), 0, st, scores, d.score_stride,
-                               mm, d.mm_stride, c->context_lens, k, onepass_min, topk_idx, ap, c->block_table,
-                               c->max_blocks_per_seq, bsl, c->num_blocks, rows);
+                               mm, d.mm_stride, c->context_lens, k, onepass_min, topk_idx, ap);
     }
     if (mk) mk->mark();
 }
 
-// rows_from_topk: the select of this call ran just before on this workspace, so
-// the kept tokens' cache rows it wrote (when the plan emits them) stand for
-// topk_idx and the block table
 void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const void *q, const int32_t *topk_idx,
-                   void *out, float *lse, void *ws, const DecodePlan &d, hipStream_t st, StageMarks *mk,
-                   bool rows_from_topk = false)
+                   void *out, float *lse, void *ws, const DecodePlan &d, hipStream_t st, StageMarks *mk)
 {
     AttnArgs a = attn_args(p, c, q, topk_idx, out, lse);
-    if (rows_from_topk && d.emit_rows) a.rows_in = (const uint32_t *)((char *)ws + d.off_rows);
     a.decode = 1;
     a.tokens_per_split = d.tokens_per_split;
     a.splits = d.splits;
@@ -949,7 +935,7 @@ static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_
     }
     const AppendArgs ap = new_kv ? append_args(p, c, new_kv, new_idx_k) : no_append();
     select_decode(p, c, batch, max_ctx, idx_q, idx_w, topk_idx, workspace, d, st, mk, ap);
-    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, st, mk, true);
+    attend_decode(p, c, batch, q, topk_idx, out, lse, workspace, d, st, mk);
     return launched();
 }
 

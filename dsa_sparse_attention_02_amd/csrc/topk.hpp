@@ -83,31 +83,6 @@ struct TopkShared {
     uint64_t cand[kCandCap];
 };
 
-// Physical cache rows of the emitted positions, written beside them for the
-// attention that follows: it then finds its kept rows in one memory round trip
-// instead of two (positions, then block-table entries).  tbl: the sequence's
-// block-table entries, staged in LDS by LDS-DMA at the start of the row (the
-// first reader waits for the copies and a barrier).  ro == nullptr: no rows.
-constexpr int kRowTableCap = 4 * kTopkThreads;  // block-table entries a row may stage
-struct RowOut {
-    uint32_t *ro;
-    const int32_t *tbl;
-    int bs_log2;
-    int64_t num_blocks;
-    __device__ __forceinline__ void put(int slot, int pos) const
-    {
-        if (!ro) return;
-        const int blk = tbl[pos >> bs_log2];
-        ro[slot] = blk >= 0 && blk < num_blocks ? ((uint32_t)blk << bs_log2) | (uint32_t)(pos & ((1 << bs_log2) - 1))
-                                                : kNoRow;
-    }
-    // (before the barrier that precedes the first put)
-    __device__ __forceinline__ void wait_staged() const
-    {
-        if (ro) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    }
-};
-
 // Finds the bin at which the count of keys in higher bins reaches `need`:
 // returns (bin, keys strictly above that bin).  Thread u owns bins
 // [nbins - per*(u+1), nbins - per*u) so a prefix scan over u is a suffix scan over bins.
@@ -145,10 +120,9 @@ __device__ __forceinline__ void pick_bin(TopkShared &sh, int nbins, uint32_t nee
 // Radix path for one row: exact threshold key by three histogram passes, then
 // ordered compaction with the lowest-position tie-break.
 __device__ __forceinline__ void topk_radix_row(TopkShared &sh, const float *__restrict__ sr, int n, int k,
-                                               int32_t *__restrict__ o, const RowOut &rt = RowOut{})
+                                               int32_t *__restrict__ o)
 {
     const int tid = threadIdx.x;
-    rt.wait_staged();  // (the first pass's barrier follows)
     const int n4 = n & ~3;
     uint32_t prefix = 0, pmask = 0;
     uint32_t need = (uint32_t)k;
@@ -209,16 +183,10 @@ __device__ __forceinline__ void topk_radix_row(TopkShared &sh, const float *__re
             // inconsistent keys (NaN scores) ever broke the counting
             if (kk[e] > T) {
                 const uint32_t slot = G + min(E, need);
-                if (slot < (uint32_t)k) {
-                    o[slot] = i0 + e;
-                    rt.put(slot, i0 + e);
-                }
+                if (slot < (uint32_t)k) o[slot] = i0 + e;
                 ++G;
             } else if (kk[e] == T) {
-                if (E < need && G + E < (uint32_t)k) {
-                    o[G + E] = i0 + e;
-                    rt.put(G + E, i0 + e);
-                }
+                if (E < need && G + E < (uint32_t)k) o[G + E] = i0 + e;
                 ++E;
             }
         }
@@ -229,10 +197,8 @@ __device__ __forceinline__ void topk_radix_row(TopkShared &sh, const float *__re
 
 // 5. The kept positions (set bits of the bitmap) in ascending order: contiguous
 // words per thread, a block scan of their bit counts.
-__device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int32_t *o, int tid,
-                                          const RowOut &rt = RowOut{})
+__device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int32_t *o, int tid)
 {
-    rt.wait_staged();  // (the scan's barrier follows)
     const int per = (words + kTopkThreads - 1) / kTopkThreads;
     const int w0 = tid * per, w1 = min(words, w0 + per);
     uint32_t cnt = 0;
@@ -254,10 +220,7 @@ __device__ __forceinline__ void topk_emit(TopkShared &sh, int words, int k, int3
         while (bits) {
             const int b = __builtin_ctz(bits);
             bits &= bits - 1;
-            if (pos < (uint32_t)k) {
-                o[pos] = w * 32 + b;
-                rt.put(pos, w * 32 + b);
-            }
+            if (pos < (uint32_t)k) o[pos] = w * 32 + b;
             ++pos;
         }
     }
@@ -322,7 +285,7 @@ __device__ __forceinline__ uint64_t cand_word(float x, int i)
 // Up to 64 candidates: wave 0 ranks each against all (lane i holds candidate
 // i); more: a bitonic sort over the block.
 __device__ __forceinline__ void resolve_emit(TopkShared &sh, int m, uint32_t need, int words, int k,
-                                             int32_t *__restrict__ o, const RowOut &rt = RowOut{})
+                                             int32_t *__restrict__ o)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     if (m <= 64) {  // block-uniform
@@ -336,7 +299,7 @@ __device__ __forceinline__ void resolve_emit(TopkShared &sh, int m, uint32_t nee
             }
         }
         __syncthreads();
-        topk_emit(sh, words, k, o, tid, rt);
+        topk_emit(sh, words, k, o, tid);
         return;
     }
     int P = 1;
@@ -361,14 +324,13 @@ __device__ __forceinline__ void resolve_emit(TopkShared &sh, int m, uint32_t nee
         atomicOr(&sh.bitmap[pos >> 5], 1u << (pos & 31));
     }
     __syncthreads();
-    topk_emit(sh, words, k, o, tid, rt);
+    topk_emit(sh, words, k, o, tid);
 }
 
 // Steps 2-5 of the threshold path for a row of n keys (k < n <= kBitmapKeys)
 // whose score range is [lo, hi].
 __device__ __forceinline__ void threshold_row(TopkShared &sh, const float *__restrict__ sr, int n, int k,
-                                              int32_t *__restrict__ o, float lo, float hi,
-                                              const RowOut &rt = RowOut{})
+                                              int32_t *__restrict__ o, float lo, float hi)
 {
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int n4 = n & ~3;
@@ -399,7 +361,7 @@ __device__ __forceinline__ void threshold_row(TopkShared &sh, const float *__res
     pick_bin(sh, kBins, (uint32_t)k, tbin, above, m);
     const uint32_t need = (uint32_t)k - above;
     if (m > (uint32_t)kCandCap) {  // block-uniform
-        topk_radix_row(sh, sr, n, k, o, rt);
+        topk_radix_row(sh, sr, n, k, o);
         return;
     }
 
@@ -452,7 +414,7 @@ __device__ __forceinline__ void threshold_row(TopkShared &sh, const float *__res
             }
         }
     __syncthreads();
-    resolve_emit(sh, (int)m, need, words, k, o, rt);
+    resolve_emit(sh, (int)m, need, words, k, o);
 }
 
 // Rows r = blockIdx.x.  n = ctx_lens[r] when ctx_lens is non-null (decode),
@@ -525,7 +487,6 @@ struct TopkGatherShared {
     TopkShared sh;
     int32_t cp[kCompCap];
     uint32_t ngather, ncand;
-    int32_t tbl[kRowTableCap];  // the row's block-table entries (RowOut)
 };
 
 // pick_bin over kBins bins by wave 0 alone (lane l sums the 32 bins
@@ -583,15 +544,10 @@ __device__ __forceinline__ void pick_bin_wave(Shared &sh, uint32_t need, uint32_
 
 // Rows of fewer than onepass_min keys take the threshold path.  GR: gather
 // rounds whose loads are in flight together per wave (the loop's unroll).
-// With rows_out, the kept positions' cache rows are written beside them
-// ([rows][k], kNoRow for padding); the launch's rows then have at most
-// kRowTableCap blocks.
 template <int GR>
 __global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
     const float *__restrict__ scores, int64_t score_stride, const f32x2 *__restrict__ tile_mm, int64_t mm_stride,
-    const int32_t *__restrict__ ctx_lens, int k, int onepass_min, int32_t *__restrict__ out, const AppendArgs ap,
-    const int32_t *__restrict__ block_table, int max_blocks, int bs_log2, int64_t num_blocks,
-    uint32_t *__restrict__ rows_out)
+    const int32_t *__restrict__ ctx_lens, int k, int onepass_min, int32_t *__restrict__ out, const AppendArgs ap)
 {
     __shared__ TopkGatherShared g;
     TopkShared &sh = g.sh;
@@ -600,28 +556,13 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
     const int n = ctx_lens[r];
     int32_t *o = out + (int64_t)r * k;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    RowOut rt{nullptr, g.tbl, bs_log2, num_blocks};
-    if (rows_out) {  // (launch-uniform) the row's block-table entries into LDS, 4 per lane
-        rt.ro = rows_out + (int64_t)r * k;
-        const int nblk = n > 0 ? ((n - 1) >> bs_log2) + 1 : 0;  // <= kRowTableCap
-        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(block_table + (int64_t)r * max_blocks, (uint32_t)nblk * 4);
-        buf_dma16_to_lds(rs, 16 * tid, (SA_LDS void *)&g.tbl[4 * 64 * wv]);  // (entries past nblk read as 0)
-    }
     if (n <= k) {
-        rt.wait_staged();
-        __syncthreads();
-        for (int i = tid; i < k; i += kTopkThreads) {
-            o[i] = i < n ? i : -1;
-            if (rt.ro) {
-                if (i < n) rt.put(i, i);
-                else rt.ro[i] = kNoRow;
-            }
-        }
+        for (int i = tid; i < k; i += kTopkThreads) o[i] = i < n ? i : -1;
         return;
     }
     const float *sr = scores + (int64_t)r * score_stride;
     if (n > kBitmapKeys) {
-        topk_radix_row(sh, sr, n, k, o, rt);
+        topk_radix_row(sh, sr, n, k, o);
         return;
     }
     const f32x2 *mm = tile_mm + (int64_t)r * mm_stride;
@@ -629,7 +570,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
     if (n < onepass_min || n <= 2 * k || 2 * k > kCompCap) {  // (also where the gathered set would be large)
         float lo, hi;
         row_range(sh, mm, nmm, lo, hi);
-        threshold_row(sh, sr, n, k, o, lo, hi, rt);
+        threshold_row(sh, sr, n, k, o, lo, hi);
         return;
     }
 
@@ -761,7 +702,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
     __syncthreads();
     const int mc = (int)g.ngather;
     if (mc < k || mc > kCompCap) {  // (block-uniform) the sample misjudged the row
-        threshold_row(sh, sr, n, k, o, lo, hi, rt);
+        threshold_row(sh, sr, n, k, o, lo, hi);
         return;
     }
 
@@ -787,7 +728,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
     uint32_t tbin, m;
     pick_bin_wave(sh, (uint32_t)k, tbin, above, m);
     if (m > (uint32_t)kCandCap) {  // block-uniform
-        topk_radix_row(sh, sr, n, k, o, rt);
+        topk_radix_row(sh, sr, n, k, o);
         return;
     }
 #pragma unroll
@@ -802,7 +743,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_decode_kernel(
         }
     }
     __syncthreads();
-    resolve_emit(sh, (int)m, (uint32_t)k - above, words, k, o, rt);
+    resolve_emit(sh, (int)m, (uint32_t)k - above, words, k, o);
 }
 
 // ------------------------------------------------- many workgroups per row --
