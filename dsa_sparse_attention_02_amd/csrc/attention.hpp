@@ -286,7 +286,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     // m: reference max (log2 units); l: sum of the weights the MFMAs multiply
     // (output normaliser); le: sum of the unrounded weights (log-sum-exp)
     float m = -INFINITY, l = 0.0f, le = 0.0f;
-    bool ovf = false;
+    float runmax = -INFINITY;  // largest logit of this lane's tokens from the reference tile on
     __syncthreads();
     for (int t = threadIdx.x; t < ntiles; t += nthreads)
         if (vbits[t]) {
@@ -390,8 +390,8 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     // rescaling) and never moves afterwards: the output accumulators are only
     // ever touched by the MFMAs.  Weights are exp2(min(s - m, 64)), finite in
     // fp32 and bf16; a head whose logits outgrow its reference by more than 64
-    // raises `ovf`, and the split is then recomputed exactly with its true max
-    // (below).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and wl[k2],
+    // (found after the last tile from each lane's running max) has the split
+    // recomputed exactly with its true max (below).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and wl[k2],
     // the bf16 residues, for `precise` rows).
     struct SmState {
         f32x16 s;
@@ -430,8 +430,9 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mv = fmaxf(mv, valid_bit(st.vb, i) ? st.s[i] : -INFINITY);
                 m = halves_max(mv) * a.scale_log2;
+                runmax = -INFINITY;  // (earlier tiles hold padding only)
             }
-            ovf |= m != -INFINITY && halves_max(st.tmax) * a.scale_log2 > m + 64.0f;
+            runmax = fmaxf(runmax, st.tmax);
             st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every weight is 0
         } else if (step < kSmSteps) {
             const int j = step - 3;
@@ -575,7 +576,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         // Exact recompute of the split when some head's logits outgrew its reference
         // max by more than 64 (never for logits within a few dozen of each other):
         // pass 1 finds every head's true max, pass 2 redoes the weighted sum with it.
-        if (ovf) overflow_flag = 1;
+        if (m != -INFINITY && runmax * a.scale_log2 > m + 64.0f) overflow_flag = 1;
         __syncthreads();
         if (overflow_flag) {
             // S^T of tile t (both partners), through buffer 0 and the exchange

@@ -227,6 +227,38 @@ def test_decode_long_row_branches(dev, kind):
     compare(w, run_gpu(dev, w), tag=f"decode_long_{kind}")
 
 
+def outgrow_case():
+    """One kept token per row whose latent row is 8 q[row, head 0]: its head-0
+    logit (8 |q|^2 times the scale 1/8, about 64, times log2 e) exceeds the
+    reference max fixed by its split's first tile by far more than 64 in log2
+    units, so the attention recomputes that split exactly with its true max.
+    Row 0 keeps all its 300 keys (P as a hi/lo pair), row 1 keeps 2048 of 2500.
+    The token is the 41st kept one of its row: outside the first 32-token tile
+    of its split at 96, 704 and 2048 tokens per split."""
+    w = synth.make(synth.small_decode("decode_outgrow", V64, [300, 2500], seed=131))
+    kept1 = oracle.run(w, rows=[1])["topk"][0]  # (the latent rows do not change the selection)
+    q = synth.bf16_bits_to_f32(w["q"])
+    kv = w["kv"].copy()
+    for b, pos in ((0, 40), (1, int(kept1[40]))):
+        blk, slot = _key_rows(w, b, [pos])
+        kv[blk[0], slot[0]] = synth.f32_to_bf16_bits(8.0 * q[b, 0])
+    return dict(w, kv=kv)
+
+
+def test_attention_logit_outgrows_reference(dev):
+    torch, sa = dev
+    say("[gpu] attention exact recompute: a logit far above the split's reference max")
+    w = outgrow_case()
+    compare(w, run_gpu(dev, w), tag="decode_outgrow")
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"])
+    for splits in (1, 3):
+        res = sa.sparse_attn_decode_cfg(p, d["cache"], int(w["context_lens"].max()), splits, d["q"], d["idx_q"],
+                                        d["idx_w"])
+        torch.cuda.synchronize()
+        compare(w, res, tag=f"decode_outgrow splits {splits}")
+
+
 @pytest.mark.parametrize("name", ["decode_ragged", "prefill_2500", "tiny_prefill_L256"])
 def test_staged_equals_fused_and_deterministic(dev, name):
     spec = CASES[name]()
