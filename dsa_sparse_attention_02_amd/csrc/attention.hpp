@@ -286,7 +286,6 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     // m: reference max (log2 units); l: sum of the weights the MFMAs multiply
     // (output normaliser); le: sum of the unrounded weights (log-sum-exp)
     float m = -INFINITY, l = 0.0f, le = 0.0f;
-    float runmax = -INFINITY;  // largest logit of this lane's tokens from the reference tile on
     __syncthreads();
     for (int t = threadIdx.x; t < ntiles; t += nthreads)
         if (vbits[t]) {
@@ -382,25 +381,28 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     };
     auto no_fill = [](int) {};
     // Weights of a tile from its S^T in kSmSteps small steps, so that they can
-    // sit between the next tile's q.k MFMAs: steps 0-1 mask and reduce the max,
-    // 2 crosses the half-waves and sets the reference, 3-10 exponentiate, round
-    // and sum pair j = step - 3.  Register i of half hf holds token
-    // 16(i/8) + 8hf + i%8.  The reference max is fixed by the first tile with a
-    // valid token for this head (until then O and l are 0, so nothing needs
-    // rescaling) and never moves afterwards: the output accumulators are only
-    // ever touched by the MFMAs.  Weights are exp2(min(s - m, 64)), finite in
-    // fp32 and bf16; a head whose logits outgrow its reference by more than 64
-    // (found after the last tile from each lane's running max) has the split
-    // recomputed exactly with its true max (below).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and wl[k2],
-    // the bf16 residues, for `precise` rows).
+    // sit between the next tile's q.k MFMAs: step 0 sets the reference (on the
+    // tile that fixes it: the max of the valid tokens over both half-waves),
+    // 1-8 exponentiate, round and sum pair j = step - 1.  Register i of half hf
+    // holds token 16(i/8) + 8hf + i%8.  The reference max is fixed by the first
+    // tile with a valid token for this head (until then O and l are 0, so
+    // nothing needs rescaling) and never moves afterwards: the output
+    // accumulators are only ever touched by the MFMAs.  Weights are
+    // exp2(min(s - m, 64)), finite in fp32 and bf16.  A clamped weight is
+    // exactly 2^64 and the others are smaller, so a head whose logits outgrew
+    // its reference by more than 64 leaves a lane's sum of weights at 2^64 or
+    // more; after the last tile that recomputes the split exactly with its true
+    // max (below; a sum that large without a clamp only costs a needless
+    // recompute).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and
+    // wl[k2], the bf16 residues, for `precise` rows).
     struct SmState {
         f32x16 s;
-        float tmax, mref;
+        float mref;
         uint32_t vb;
         bool full, set_ref;  // (workgroup-uniform) every token valid; the tile fixes the reference
         u32x4 w[2], wl[2];
     };
-    constexpr int kSmSteps = 11;
+    constexpr int kSmSteps = 9;
     auto sm_begin = [&](SmState &st, int t, bool set_ref) {
         const uint32_t bits = vbits[t];
         st.full = __builtin_amdgcn_readfirstlane(bits) == 0xFFFFFFFFu;
@@ -408,17 +410,10 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         st.vb = bits >> (8 * half);
     };
     auto valid_bit = [&](uint32_t vb, int i) { return ((vb >> (16 * (i >> 3) + (i & 7))) & 1u) != 0; };
-    // Padding tokens have zero latent rows, so their logits are 0: the max
-    // that checks for overflow may include them (at worst a needless exact
-    // recompute when every valid logit lies far below 0), the reference max
-    // and the weights may not.
+    // Padding tokens have zero latent rows, so their logits are 0: the
+    // reference max and the weights leave them out.
     auto sm_step = [&](auto cfg, SmState &st, int step) {
-        if (step < 2) {
-            float mx = step == 0 ? -INFINITY : st.tmax;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, st.s[8 * step + e]);
-            st.tmax = mx;
-        } else if (step == 2) {
+        if (step == 0) {
             // max over the two half-waves (they hold the other 16 tokens)
             auto halves_max = [](float x) {
                 const uint32_t u = __float_as_uint(x);
@@ -430,12 +425,10 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) mv = fmaxf(mv, valid_bit(st.vb, i) ? st.s[i] : -INFINITY);
                 m = halves_max(mv) * a.scale_log2;
-                runmax = -INFINITY;  // (earlier tiles hold padding only)
             }
-            runmax = fmaxf(runmax, st.tmax);
             st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every weight is 0
         } else if (step < kSmSteps) {
-            const int j = step - 3;
+            const int j = step - 1;
             float e[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) e[h] = exp2_hw(fminf(fmaf(st.s[2 * j + h], a.scale_log2, -st.mref), 64.0f));
@@ -576,7 +569,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         // Exact recompute of the split when some head's logits outgrew its reference
         // max by more than 64 (never for logits within a few dozen of each other):
         // pass 1 finds every head's true max, pass 2 redoes the weighted sum with it.
-        if (m != -INFINITY && runmax * a.scale_log2 > m + 64.0f) overflow_flag = 1;
+        if (le >= 0x1p64f) overflow_flag = 1;
         __syncthreads();
         if (overflow_flag) {
             // S^T of tile t (both partners), through buffer 0 and the exchange
