@@ -96,6 +96,37 @@ def test_topk_bruteforce_rank_definition():
         assert np.all(np.diff(kept) > 0)
 
 
+def test_topk_composability():
+    """Under the strict order (score descending, position ascending), the top k
+    of a row equal the top k of the union of its chunks' own top k (the property
+    that lets a long row's selection run per chunk, then once over the
+    survivors).  Chunks are contiguous ranges or arbitrary subsets; scores take
+    few distinct values so ties cross chunk boundaries."""
+    rng = np.random.default_rng(23)
+    for trial in range(80):
+        n = int(rng.integers(1, 600))
+        k = int(rng.integers(1, 90))
+        scores = rng.integers(-4, 5, size=n).astype(np.float32) * np.float32(0.25)
+        if trial % 2 == 0:  # contiguous chunks
+            cuts = np.sort(rng.choice(np.arange(1, max(n, 2)), size=min(n - 1, int(rng.integers(0, 6))), replace=False))
+            parts = np.split(np.arange(n), cuts)
+        else:  # arbitrary subsets
+            lab = rng.integers(0, 4, size=n)
+            parts = [np.nonzero(lab == c)[0] for c in range(4)]
+        survivors = []
+        for part in parts:
+            if len(part) == 0:
+                continue
+            local = oracle.topk(scores[part], k)
+            survivors.extend(part[local[local >= 0]].tolist())
+        union = np.array(sorted(survivors), dtype=np.int64)  # ascending positions: array order = position order
+        sel = oracle.topk(scores[union], k)
+        got = union[sel[sel >= 0]]
+        want = oracle.topk(scores, k)
+        want = want[want >= 0]
+        assert np.array_equal(got, want), (trial, n, k)
+
+
 def test_topk_special_cases():
     rng = np.random.default_rng(9)
     s = rng.standard_normal(50).astype(np.float32)
