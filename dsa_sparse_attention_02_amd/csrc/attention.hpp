@@ -39,8 +39,9 @@
 //     steps), exchanged through LDS and summed;
 //   * softmax in base 2 in fp32 against a per-head reference max taken from
 //     the first tile with a valid token; it never moves, so the output
-//     accumulators are touched only by MFMAs (a split whose logits outgrow the
-//     reference by more than 64 is recomputed exactly with its true max);
+//     accumulators are touched only by MFMAs (a split whose weights reach 2^64,
+//     its logits outgrowing the reference, is recomputed exactly with its true
+//     max);
 //   * the S^T accumulator already has the register layout of the B operand of
 //     O^T[v][head] += V^T[v][token] . P^T[token][head]: P is only rounded to bf16.
 //     Rows that keep fewer than kPreciseBelow keys carry P as a pair of bf16
@@ -388,12 +389,11 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     // tile with a valid token for this head (until then O and l are 0, so
     // nothing needs rescaling) and never moves afterwards: the output
     // accumulators are only ever touched by the MFMAs.  Weights are
-    // exp2(min(s - m, 64)), finite in fp32 and bf16.  A clamped weight is
-    // exactly 2^64 and the others are smaller, so a head whose logits outgrew
-    // its reference by more than 64 leaves a lane's sum of weights at 2^64 or
-    // more; after the last tile that recomputes the split exactly with its true
-    // max (below; a sum that large without a clamp only costs a needless
-    // recompute).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and
+    // exp2(s - m).  A head whose logits outgrow its reference by 64 or more
+    // leaves a lane's sum of weights at 2^64 or more (+inf once a weight
+    // overflows fp32, with inf or NaN in its accumulators); after the last tile
+    // that recomputes the split exactly with its true max (below; a sum that
+    // large from many smaller weights only costs a needless recompute).  P^T operand k2 (tokens 16k2 + 8hf .. +7) is w[k2] (and
     // wl[k2], the bf16 residues, for `precise` rows).
     struct SmState {
         f32x16 s;
@@ -431,7 +431,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             const int j = step - 1;
             float e[2];
 #pragma unroll
-            for (int h = 0; h < 2; ++h) e[h] = exp2_hw(fminf(fmaf(st.s[2 * j + h], a.scale_log2, -st.mref), 64.0f));
+            for (int h = 0; h < 2; ++h) e[h] = exp2_hw(fmaf(st.s[2 * j + h], a.scale_log2, -st.mref));
             uint32_t hi = pack_bf16x2(e[0], e[1]);
             uint32_t keep = 0xFFFFFFFFu;
             if (!st.full) {
@@ -611,7 +611,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
                 st.s = full_s(t);
                 sm_begin(st, t, false);
 #pragma unroll
-                for (int step = 0; step < kSmSteps; ++step) sm_step(cfg, st, step);  // s <= m now: no clamping
+                for (int step = 0; step < kSmSteps; ++step) sm_step(cfg, st, step);  // (s <= m now)
                 pv(cfg, 0, st);
                 __syncthreads();
             }
