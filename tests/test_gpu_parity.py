@@ -172,6 +172,12 @@ CASES = {
     "decode_very_long_all_ties": lambda: synth.small_decode("decode_very_long_all_ties", V64,
                                                             [300_000, 262_145, 70_000, 5], seed=128, topk=64,
                                                             idx_int_max=0),
+    # small k on rows over 262144 keys: the two-launch path with a bound set
+    # from a handful of sample keys (k = 64, and k = 1)
+    "decode_very_long_k64": lambda: synth.small_decode("decode_very_long_k64", V64, [300_000, 270_001, 100], seed=132,
+                                                       topk=64),
+    "decode_very_long_k1": lambda: synth.small_decode("decode_very_long_k1", V64, [280_000, 262_200, 1, 0], seed=133,
+                                                      topk=1),
     # k over 4096: the many-workgroup radix select
     "decode_very_long_k5000": lambda: synth.small_decode("decode_very_long_k5000", V64, [270_000, 6000], seed=129,
                                                          topk=5000),
