@@ -265,6 +265,37 @@ def test_attention_logit_outgrows_reference(dev):
         compare(w, res, tag=f"decode_outgrow splits {splits}")
 
 
+def random_decode_spec(seed):
+    """A seeded mixed decode case: shape family, head count, k and a batch of
+    ragged context lengths (empty rows, rows at k and k + 1, short, medium and,
+    now and then, rows over 262144 keys)."""
+    rng = np.random.default_rng(1000 + seed)
+    family = ["mla", "v64", "tiny"][int(rng.integers(0, 3))]
+    if family == "mla":
+        shape = replace(MLA, num_heads=int(rng.choice([16, 20, 48, 64, 128])))
+    elif family == "v64":
+        shape = replace(V64, num_heads=int(rng.choice([4, 8, 24])))
+    else:
+        shape = replace(synth.TINY, num_heads=int(rng.choice([8, 12, 40])))
+    k = int(rng.choice([1, 7, 64, 100, 640, 2048, 3000]))
+    pool = [0, 1, k, k + 1, int(rng.integers(2, 300)), int(rng.integers(300, 9000)),
+            int(rng.integers(9000, 70000))]
+    if family != "mla" and rng.random() < 0.4:
+        pool.append(int(rng.integers(262_145, 300_000)))
+    batch = int(rng.integers(1, 7))
+    ctx = [int(rng.choice(pool)) for _ in range(batch)]
+    return synth.small_decode(f"decode_random_{seed}", shape, ctx, seed=2000 + seed, topk=k)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_parity_random_decode(dev, seed):
+    spec = random_decode_spec(seed)
+    say(f"[gpu] random decode {seed}: heads {spec.shape.num_heads} qk {spec.shape.qk_dim} k {spec.shape.topk} "
+        f"ctx {spec.ctx}")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w), tag=spec.name)
+
+
 @pytest.mark.parametrize("name", ["decode_ragged", "prefill_2500", "tiny_prefill_L256"])
 def test_staged_equals_fused_and_deterministic(dev, name):
     spec = CASES[name]()
