@@ -296,6 +296,38 @@ def test_parity_random_decode(dev, seed):
     compare(w, run_gpu(dev, w), tag=spec.name)
 
 
+def random_prefill_spec(seed):
+    """A seeded mixed prefill case: shape family, head count, k, rows and the
+    cached prefix (q_start), single-sequence or several sequences in one call."""
+    rng = np.random.default_rng(3000 + seed)
+    family = ["mla", "v64", "tiny"][int(rng.integers(0, 3))]
+    if family == "mla":
+        shape, max_rows = replace(MLA, num_heads=int(rng.choice([16, 48, 128]))), 24
+    elif family == "v64":
+        shape, max_rows = replace(V64, num_heads=int(rng.choice([4, 8]))), 300
+    else:
+        shape, max_rows = replace(synth.TINY, num_heads=int(rng.choice([8, 40]))), 300
+    k = int(rng.choice([1, 64, 640, 2048, 3000]))
+    if seed % 2 == 0:
+        rows = int(rng.integers(1, max_rows + 1))
+        q_start = int(rng.choice([0, int(rng.integers(1, 4000)), k, max(0, k - rows)]))
+        return synth.small_prefill(f"prefill_random_{seed}", shape, rows=rows, q_start=q_start, seed=4000 + seed,
+                                   topk=k)
+    nseq = int(rng.integers(1, 5))
+    seq_rows = [int(rng.integers(0, max_rows // 2 + 1)) for _ in range(nseq)]
+    q_starts = [int(rng.choice([0, int(rng.integers(1, 4000)), k])) for _ in range(nseq)]
+    return synth.small_varlen(f"varlen_random_{seed}", shape, seq_rows, q_starts, seed=4000 + seed, topk=k)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_parity_random_prefill(dev, seed):
+    spec = random_prefill_spec(seed)
+    say(f"[gpu] random prefill {seed}: mode {spec.mode} heads {spec.shape.num_heads} qk {spec.shape.qk_dim} "
+        f"k {spec.shape.topk} rows {spec.rows or spec.seq_rows} q_start {spec.q_start if spec.mode == 'prefill' else spec.q_starts}")
+    w = synth.make(spec)
+    compare(w, run_gpu(dev, w), tag=spec.name)
+
+
 @pytest.mark.parametrize("name", ["decode_ragged", "prefill_2500", "tiny_prefill_L256"])
 def test_staged_equals_fused_and_deterministic(dev, name):
     spec = CASES[name]()
