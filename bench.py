@@ -181,16 +181,17 @@ def supplementary_decode(args, torch, sa, synth, c):
         res["decode_append"] = {"ms_per_step": round(ms_app, 4), "tokens_per_s": round(B / (ms_app / 1e3), 1),
                                 "added_us": round((ms_app - ms_plain) * 1e3, 2)}
     if args.tune:
-        splits, path, tune_us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=10)
+        splits, path, partners, tune_us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"],
+                                                         reps=10)
         wst = torch.empty(sa.decode_workspace_size_cfg(p, B, max_ctx, splits, path), dtype=torch.uint8,
                           device="cuda")
         cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"],
-                                                topk_path=path, workspace=wst, outputs=outs)
+                                                topk_path=path, attn_partners=partners, workspace=wst, outputs=outs)
         ms = time_back_to_back(torch, cfg, 20, 20)
-        log(f"tuned: {splits} attention splits per row, top-k path {TOPK_PATHS[path]}, {ms:.3f} ms/step "
-            f"(tuner's own mean {tune_us:.1f} us)")
-        res["decode_tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "ms_per_step": round(ms, 4),
-                               "tokens_per_s": round(B / (ms / 1e3), 1)}
+        log(f"tuned: {splits} attention splits per row, top-k path {TOPK_PATHS[path]}, attention partners "
+            f"{partners or 'default'}, {ms:.3f} ms/step (tuner's own mean {tune_us:.1f} us)")
+        res["decode_tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "attn_partners": partners,
+                               "ms_per_step": round(ms, 4), "tokens_per_s": round(B / (ms / 1e3), 1)}
         del wst
     if args.blocks_steps > 0:
         from dataclasses import replace
@@ -224,14 +225,16 @@ def run_other_decode(args, torch, sa, synth, name):
         ", ".join(f"{k} {v * 1e3:.1f}us" for k, v in stages.items()))
     if args.tune:
         p, d = c["p"], c["d"]
-        splits, path, _ = sa.decode_tune(p, d["cache"], c["max_ctx"], d["q"], d["idx_q"], d["idx_w"], reps=10)
+        splits, path, partners, _ = sa.decode_tune(p, d["cache"], c["max_ctx"], d["q"], d["idx_q"], d["idx_w"],
+                                                   reps=10)
         wst = torch.empty(sa.decode_workspace_size_cfg(p, c["B"], c["max_ctx"], splits, path), dtype=torch.uint8,
                           device="cuda")
         cfg = lambda: sa.sparse_attn_decode_cfg(p, d["cache"], c["max_ctx"], splits, d["q"], d["idx_q"],
-                                                d["idx_w"], topk_path=path, workspace=wst, outputs=c["outs"])
+                                                d["idx_w"], topk_path=path, attn_partners=partners, workspace=wst,
+                                                outputs=c["outs"])
         mt = time_back_to_back(torch, cfg, 20, 20)
-        line["tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "ms_per_step": round(mt, 4),
-                         "tokens_per_s": round(c["B"] / (mt / 1e3), 1)}
+        line["tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "attn_partners": partners,
+                         "ms_per_step": round(mt, 4), "tokens_per_s": round(c["B"] / (mt / 1e3), 1)}
     del c
     torch.cuda.empty_cache()
     return line

@@ -79,6 +79,7 @@ struct AttnArgs {
     SeqMap rows_map;             // prefill: row r's sequence and position (limit = position + 1)
     int tokens_per_split, splits, out_bf16;
     float scale_log2;            // softmax_scale * log2(e)
+    int partners;                // (host side) partner waves per head block: 2 or 4
 };
 
 #ifndef SA_ATTN_KPF

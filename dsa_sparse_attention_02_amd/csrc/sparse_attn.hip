@@ -25,6 +25,7 @@
 
 #include "../../include/sparse_attn.h"
 #include "attention.hpp"
+#include "attention_p4.hpp"
 #include "blocks.hpp"
 #include "indexer.hpp"
 #include "topk.hpp"
@@ -102,11 +103,21 @@ struct AttnLaunch {
     int hb, partners, waves, groups;
 };
 
-AttnLaunch attn_launch(const sa_params *p)
+// Partner waves per 32-head block of the 576/512 attention: 2 (attend_kernel,
+// one wave per SIMD) or 4 (attend_p4_kernel, two waves per SIMD).
+#ifndef SA_DEFAULT_PARTNERS
+#define SA_DEFAULT_PARTNERS 2
+#endif
+constexpr int kDefaultPartners = SA_DEFAULT_PARTNERS;
+
+// SA_ATTN_PARTNERS_*: 0 takes the default
+static bool valid_partners(int v) { return v == SA_ATTN_PARTNERS_DEFAULT || v == SA_ATTN_PARTNERS_2 || v == SA_ATTN_PARTNERS_4; }
+
+AttnLaunch attn_launch(const sa_params *p, int partners = kDefaultPartners)
 {
     AttnLaunch L{};
     L.hb = p->qk_dim == 576 ? (p->num_heads <= 32 ? 1 : 2) : (p->num_heads <= 32 ? 1 : p->num_heads <= 64 ? 2 : 4);
-    L.partners = 2;
+    L.partners = p->qk_dim == 576 && partners == 4 ? 4 : 2;
     L.waves = L.hb * L.partners;
     L.groups = (p->num_heads + 32 * L.hb - 1) / (32 * L.hb);
     return L;
@@ -119,6 +130,7 @@ struct DecodePlan {
     size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
     int topk_path;  // SA_TOPK_*: which decode rows take the one-pass top-k, and its unroll
+    int partners = kDefaultPartners;  // attention partner waves per head block
 };
 
 // want_splits > 0 asks for that many attention splits per row (clamped to
@@ -178,6 +190,7 @@ struct PrefillPlan {
     int attn_chunk_rows;     // rows per attention launch when splits > 1
     size_t off_scores, off_mm, off_part_o, off_part_ml, off_mb, total;
     int mb_chunks;  // > 0: rows too long for one top-k workgroup take the many-workgroup path
+    int partners = kDefaultPartners;  // attention partner waves per head block
 };
 
 // num_rows: query rows of the call; max_ctx: the most keys any row sees;
@@ -434,9 +447,12 @@ void idx_prefill(const sa_params *p, const sa_paged_cache *c, const uint16_t *id
 
 void attend(const sa_params *p, AttnArgs a, int rows, hipStream_t st, StageMarks *mk)
 {
-    const AttnLaunch L = attn_launch(p);
+    const AttnLaunch L = attn_launch(p, a.partners);
     dim3 grid(a.splits * rows * L.groups), block(64 * L.waves);
-    if (p->qk_dim == 576) {
+    if (p->qk_dim == 576 && L.partners == 4) {
+        if (L.hb == 1) hipLaunchKernelGGL((attend_p4_kernel<576, 512, 1>), grid, block, 0, st, a);
+        else hipLaunchKernelGGL((attend_p4_kernel<576, 512, 2>), grid, block, 0, st, a);
+    } else if (p->qk_dim == 576) {
         if (L.hb == 1) hipLaunchKernelGGL((attend_kernel<576, 512, 1>), grid, block, 0, st, a);
         else hipLaunchKernelGGL((attend_kernel<576, 512, 2>), grid, block, 0, st, a);
     } else {
@@ -571,6 +587,7 @@ void attend_decode(const sa_params *p, const sa_paged_cache *c, int batch, const
     a.decode = 1;
     a.tokens_per_split = d.tokens_per_split;
     a.splits = d.splits;
+    a.partners = d.partners;
     a.part_o = (float *)((char *)ws + d.off_part_o);
     a.part_ml = (float *)((char *)ws + d.off_part_ml);
     attend(p, a, batch, st, mk);
@@ -629,6 +646,7 @@ void attend_prefill_rows(const sa_params *p, const sa_paged_cache *c, const Pref
         a.rows_map = rows_map(parts, r0);
         a.tokens_per_split = d.tokens_per_split;
         a.splits = d.splits;
+        a.partners = d.partners;
         a.part_o = (float *)((char *)ws + d.off_part_o);
         a.part_ml = (float *)((char *)ws + d.off_part_ml);
         attend(p, a, r1 - r0, st, mk);
@@ -924,12 +942,13 @@ static sa_status decode_impl(const sa_params *p, const sa_paged_cache *c, int32_
                              const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out,
                              float *lse, void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk,
                              const void *new_kv = nullptr, const void *new_idx_k = nullptr, int want_splits = 0,
-                             int topk_path = 0)
+                             int topk_path = 0, int partners = 0)
 {
     sa_status s = check_decode(p, c, batch, max_ctx, true, true);
     if (s != SA_OK) return s;
     if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
-    const DecodePlan d = plan_decode(p, batch, max_ctx, want_splits, topk_path);
+    DecodePlan d = plan_decode(p, batch, max_ctx, want_splits, topk_path);
+    if (partners) d.partners = partners;
     if ((s = check_ws(workspace, workspace_bytes, d.total)) != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
     clear_hip_error();
@@ -1009,10 +1028,11 @@ sa_status sparse_attn_attend_prefill(const sa_params *p, const sa_paged_cache *c
 static sa_status prefill_rows_impl(const sa_params *p, const sa_paged_cache *c, const PrefillRows &rows,
                                    const void *q, const void *idx_q, const float *idx_w, int32_t *topk_idx,
                                    void *out, float *lse, void *workspace, size_t workspace_bytes, void *stream,
-                                   StageMarks *mk, bool pipeline = false)
+                                   StageMarks *mk, bool pipeline = false, int partners = 0)
 {
     if (!q || !idx_q || !idx_w || !topk_idx || !out) return SA_ERR_NULL;
-    const PrefillPlan d = plan_prefill(p, rows.total, rows.max_ctx);
+    PrefillPlan d = plan_prefill(p, rows.total, rows.max_ctx);
+    if (partners) d.partners = partners;
     sa_status s = check_ws(workspace, workspace_bytes, d.total);
     if (s != SA_OK) return s;
     hipStream_t st = (hipStream_t)stream;
@@ -1042,7 +1062,7 @@ static sa_status prefill_varlen_impl(const sa_params *p, const sa_paged_cache *c
                                      const int32_t *cu_seqlens, const int32_t *q_starts, const void *q,
                                      const void *idx_q, const float *idx_w, int32_t *topk_idx, void *out, float *lse,
                                      void *workspace, size_t workspace_bytes, void *stream, StageMarks *mk,
-                                     bool pipeline = false)
+                                     bool pipeline = false, int partners = 0)
 {
     sa_status s = check_params(p);
     if (s != SA_OK) return s;
@@ -1053,7 +1073,7 @@ static sa_status prefill_varlen_impl(const sa_params *p, const sa_paged_cache *c
         SA_OK)
         return s;
     return prefill_rows_impl(p, c, rows, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
-                             mk, pipeline);
+                             mk, pipeline, partners);
 }
 
 sa_status sparse_attn_prefill_varlen_cfg(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
@@ -1063,10 +1083,11 @@ sa_status sparse_attn_prefill_varlen_cfg(const sa_params *p, const sa_paged_cach
                                          void *workspace, size_t workspace_bytes, void *stream)
 {
     if (cfg && ((cfg->pipeline != SA_PREFILL_SERIAL && cfg->pipeline != SA_PREFILL_PIPELINED) ||
-                cfg->reserved[0] != 0 || cfg->reserved[1] != 0 || cfg->reserved[2] != 0))
+                !valid_partners(cfg->attn_partners) || cfg->reserved[0] != 0 || cfg->reserved[1] != 0))
         return SA_ERR_SHAPE;
     return prefill_varlen_impl(p, c, num_seqs, cu_seqlens, q_starts, q, idx_q, idx_w, topk_idx, out, lse, workspace,
-                               workspace_bytes, stream, nullptr, cfg && cfg->pipeline == SA_PREFILL_PIPELINED);
+                               workspace_bytes, stream, nullptr, cfg && cfg->pipeline == SA_PREFILL_PIPELINED,
+                               cfg ? cfg->attn_partners : 0);
 }
 
 sa_status sparse_attn_prefill_varlen(const sa_params *p, const sa_paged_cache *c, int32_t num_seqs,
@@ -1123,7 +1144,7 @@ static sa_status check_cfg(const sa_decode_config *cfg)
 {
     if (cfg && (cfg->attn_splits < 0 || cfg->attn_splits > 1024)) return SA_ERR_SHAPE;
     if (cfg && (cfg->topk_path < SA_TOPK_DEFAULT || cfg->topk_path > SA_TOPK_ONEPASS_U4)) return SA_ERR_SHAPE;
-    if (cfg && (cfg->reserved[0] != 0 || cfg->reserved[1] != 0)) return SA_ERR_SHAPE;
+    if (cfg && (!valid_partners(cfg->attn_partners) || cfg->reserved[0] != 0)) return SA_ERR_SHAPE;
     return SA_OK;
 }
 
@@ -1147,7 +1168,8 @@ sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *c, in
     const sa_status s = check_cfg(cfg);
     if (s != SA_OK) return s;
     return decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace, workspace_bytes, stream,
-                       nullptr, nullptr, nullptr, cfg ? cfg->attn_splits : 0, cfg ? cfg->topk_path : 0);
+                       nullptr, nullptr, nullptr, cfg ? cfg->attn_splits : 0, cfg ? cfg->topk_path : 0,
+                       cfg ? cfg->attn_partners : 0);
 }
 
 // The split counts the tuner tries: every count the plan can realise (k is
@@ -1193,13 +1215,13 @@ sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *c, int32_t ba
         return SA_ERR_HIP;
     }
     // one untimed call, then reps timed back to back; microseconds per call
-    auto time_cfg = [&](int sp, int path, float &us) -> sa_status {
+    auto time_cfg = [&](int sp, int path, float &us, int partners = 0) -> sa_status {
         sa_status r = SA_OK;
         for (int i = 0; i <= reps && r == SA_OK; ++i) {
             if (i == 1 && hipEventRecord(e0, st) != hipSuccess) r = SA_ERR_HIP;
             if (r == SA_OK)
                 r = decode_impl(p, c, batch, max_ctx, q, idx_q, idx_w, topk_idx, out, lse, workspace,
-                                workspace_bytes, stream, nullptr, nullptr, nullptr, sp, path);
+                                workspace_bytes, stream, nullptr, nullptr, nullptr, sp, path, partners);
         }
         float ms = 0.0f;
         if (r == SA_OK && (hipEventRecord(e1, st) != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
@@ -1208,9 +1230,10 @@ sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *c, int32_t ba
         us = ms * 1000.0f / reps;
         return r;
     };
-    // the split count under the default top-k, then the top-k path under that count
+    // the split count under the default top-k, then the top-k path under that
+    // count, then (576/512 shape) the other attention kernel under both
     float best_t = INFINITY;
-    int best_sp = 0, best_path = SA_TOPK_DEFAULT;
+    int best_sp = 0, best_path = SA_TOPK_DEFAULT, best_partners = SA_ATTN_PARTNERS_DEFAULT;
     s = SA_OK;
     for (int sp : tune_candidates(p, batch, max_ctx)) {
         float us = 0.0f;
@@ -1228,12 +1251,21 @@ sa_status sa_decode_tune(const sa_params *p, const sa_paged_cache *c, int32_t ba
             best_path = path;
         }
     }
+    if (p->qk_dim == 576 && s == SA_OK) {
+        const int other = kDefaultPartners == 4 ? SA_ATTN_PARTNERS_2 : SA_ATTN_PARTNERS_4;
+        float us = 0.0f;
+        if ((s = time_cfg(best_sp, best_path, us, other)) == SA_OK && us < best_t) {
+            best_t = us;
+            best_partners = other;
+        }
+    }
     (void)hipEventDestroy(e0);
     (void)hipEventDestroy(e1);
     if (s != SA_OK) return s;
     *best = sa_decode_config{};
     best->attn_splits = best_sp;
     best->topk_path = best_path;
+    best->attn_partners = best_partners;
     if (best_us) *best_us = best_t;
     return SA_OK;
 }

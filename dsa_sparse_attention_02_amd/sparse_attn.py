@@ -34,17 +34,19 @@ EXPORTS = (
 
 
 class sa_decode_config(ctypes.Structure):
-    _fields_ = [("attn_splits", ctypes.c_int32), ("topk_path", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
+    _fields_ = [("attn_splits", ctypes.c_int32), ("topk_path", ctypes.c_int32), ("attn_partners", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 1)]
 
 
 SA_TOPK_DEFAULT, SA_TOPK_THRESHOLD, SA_TOPK_ONEPASS_U2, SA_TOPK_ONEPASS_U4 = 0, 1, 2, 3
 
 
 class sa_prefill_config(ctypes.Structure):
-    _fields_ = [("pipeline", ctypes.c_int32), ("reserved", ctypes.c_int32 * 3)]
+    _fields_ = [("pipeline", ctypes.c_int32), ("attn_partners", ctypes.c_int32), ("reserved", ctypes.c_int32 * 2)]
 
 
 SA_PREFILL_SERIAL, SA_PREFILL_PIPELINED = 0, 1
+SA_ATTN_PARTNERS_DEFAULT, SA_ATTN_PARTNERS_2, SA_ATTN_PARTNERS_4 = 0, 2, 4
 
 
 class sa_params(ctypes.Structure):
@@ -365,13 +367,14 @@ def prefill_varlen_workspace_size(p: Params, cu_seqlens, q_starts) -> int:
 
 def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_starts, q, idx_q, idx_w, *,
                                want_lse=True, workspace=None, outputs=None, stream=None, events=None,
-                               pipeline=None):
+                               pipeline=None, attn_partners=None):
     """Prefill of several sequences in one call: sequence s owns packed rows
     cu_seqlens[s] .. cu_seqlens[s+1]-1 (host int32 arrays), its row i at
     position q_starts[s] + i, block-table row s.  With `events`, the profiling
     entry point records them around the kernels and the mark count is returned
-    as a fourth value.  With `pipeline` (SA_PREFILL_*), the configured entry
-    point runs that schedule."""
+    as a fourth value.  With `pipeline` (SA_PREFILL_*) or `attn_partners`
+    (SA_ATTN_PARTNERS_*), the configured entry point runs that schedule and
+    attention kernel."""
     torch = _torch()
     q_starts = np.asarray(q_starts)
     cu = _host_i32(cu_seqlens, "cu_seqlens", len(q_starts) + 1)
@@ -387,10 +390,11 @@ def sparse_attn_prefill_varlen(p: Params, cache: PagedCache, cu_seqlens, q_start
     args = (ctypes.byref(p.c()), ctypes.byref(cache.c()), len(qs), cu.ctypes.data, qs.ctypes.data, q.data_ptr(),
             idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse), ws.data_ptr(),
             ws.numel(), _stream(stream))
-    if pipeline is not None:
+    if pipeline is not None or attn_partners is not None:
         if events is not None:
-            raise SparseAttnError(SA_ERR_SHAPE, "pipeline and events are exclusive")
-        cfg = sa_prefill_config(pipeline=pipeline)
+            raise SparseAttnError(SA_ERR_SHAPE, "a configuration and events are exclusive")
+        cfg = sa_prefill_config(pipeline=pipeline or SA_PREFILL_SERIAL,
+                                attn_partners=attn_partners or SA_ATTN_PARTNERS_DEFAULT)
         _check(lib().sparse_attn_prefill_varlen_cfg(*args[:5], ctypes.byref(cfg), *args[5:]),
                "sparse_attn_prefill_varlen_cfg")
         return topk_idx, out, lse
@@ -457,8 +461,8 @@ def sparse_attn_prefill_blocks(p: Params, cache: PagedCache, q_start: int, q_blo
     return blk, out, lse
 
 
-def _cfg(attn_splits: int, topk_path: int = SA_TOPK_DEFAULT):
-    return sa_decode_config(attn_splits=attn_splits, topk_path=topk_path)
+def _cfg(attn_splits: int, topk_path: int = SA_TOPK_DEFAULT, attn_partners: int = SA_ATTN_PARTNERS_DEFAULT):
+    return sa_decode_config(attn_splits=attn_splits, topk_path=topk_path, attn_partners=attn_partners)
 
 
 def decode_workspace_size_cfg(p: Params, batch: int, max_ctx: int, attn_splits: int = 0,
@@ -471,9 +475,10 @@ def decode_workspace_size_cfg(p: Params, batch: int, max_ctx: int, attn_splits: 
 
 
 def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_splits: int, q, idx_q, idx_w, *,
-                           topk_path=SA_TOPK_DEFAULT, want_lse=True, workspace=None, outputs=None, stream=None):
-    """sparse_attn_decode with attn_splits attention splits per row (0 = default)
-    and a top-k path (SA_TOPK_*)."""
+                           topk_path=SA_TOPK_DEFAULT, attn_partners=SA_ATTN_PARTNERS_DEFAULT, want_lse=True,
+                           workspace=None, outputs=None, stream=None):
+    """sparse_attn_decode with attn_splits attention splits per row (0 = default),
+    a top-k path (SA_TOPK_*) and an attention kernel (SA_ATTN_PARTNERS_*)."""
     torch = _torch()
     B = q.shape[0]
     _dev(q, "q", _bf16_types(), (B, p.num_heads, p.qk_dim))
@@ -483,15 +488,17 @@ def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_spli
     ws = workspace if workspace is not None else _workspace(
         decode_workspace_size_cfg(p, B, max_ctx, attn_splits, topk_path), q.device)
     _check(lib().sparse_attn_decode_cfg(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
-                                        ctypes.byref(_cfg(attn_splits, topk_path)), q.data_ptr(), idx_q.data_ptr(),
+                                        ctypes.byref(_cfg(attn_splits, topk_path, attn_partners)), q.data_ptr(),
+                                        idx_q.data_ptr(),
                                         idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
                                         ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode_cfg")
     return topk_idx, out, lse
 
 
 def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, reps=10, stream=None):
-    """Run-time tuning of the decode split count and top-k path on these
-    inputs (waits for the stream).  Returns (attn_splits, topk_path,
+    """Run-time tuning of the decode split count, top-k path and attention
+    kernel on these inputs (waits for the stream).  Returns (attn_splits,
+    topk_path, attn_partners,
     microseconds per call)."""
     torch = _torch()
     B = q.shape[0]
@@ -506,7 +513,7 @@ def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, 
                                 idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
                                 ws.data_ptr(), ws.numel(), _stream(stream), reps, ctypes.byref(best),
                                 ctypes.byref(us)), "sa_decode_tune")
-    return best.attn_splits, best.topk_path, us.value
+    return best.attn_splits, best.topk_path, best.attn_partners, us.value
 
 
 class HipEvent:

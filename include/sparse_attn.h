@@ -271,13 +271,26 @@ sa_status sparse_attn_prefill_varlen(const sa_params *p, const sa_paged_cache *c
  *             it gains nothing at the shapes measured: an attention workgroup
  *             holds a compute unit's LDS, so the stages alternate on each unit
  *             rather than share it.
- * SA_ERR_SHAPE for another pipeline value or nonzero reserved fields;
- * otherwise as sparse_attn_prefill_varlen (same workspace). */
+ *   attn_partners: the attention kernel (SA_ATTN_PARTNERS_*, below).
+ * SA_ERR_SHAPE for another pipeline or attn_partners value or nonzero
+ * reserved fields; otherwise as sparse_attn_prefill_varlen (same workspace). */
+/* Attention kernel of the 576/512 shape family, both compiled in: each
+ * 32-head block of a workgroup is worked by 2 partner waves (one wave per
+ * SIMD; each partner takes half of the q.k dims and half of the value
+ * columns, and both compute the tile's softmax) or by 4 (two waves per SIMD;
+ * a quarter of the dims and columns each, the logits reduce-scattered and the
+ * softmax split by token between the partners).  Both keep the same
+ * selected keys and agree with the oracle to the same tolerance; their
+ * outputs differ in rounding only.  Other shapes always take 2. */
+#define SA_ATTN_PARTNERS_DEFAULT 0
+#define SA_ATTN_PARTNERS_2 2
+#define SA_ATTN_PARTNERS_4 4
 #define SA_PREFILL_SERIAL 0
 #define SA_PREFILL_PIPELINED 1
 typedef struct {
     int32_t pipeline;
-    int32_t reserved[3];   /* zero */
+    int32_t attn_partners; /* SA_ATTN_PARTNERS_* */
+    int32_t reserved[2];   /* zero */
 } sa_prefill_config;
 sa_status sparse_attn_prefill_varlen_cfg(const sa_params *p, const sa_paged_cache *cache, int32_t num_seqs,
                                          const int32_t *cu_seqlens, const int32_t *q_starts,
@@ -324,12 +337,15 @@ sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged
 typedef struct {
     int32_t attn_splits;
     int32_t topk_path;     /* SA_TOPK_* */
-    int32_t reserved[2];   /* zero */
+    int32_t attn_partners; /* SA_ATTN_PARTNERS_* */
+    int32_t reserved[1];   /* zero */
 } sa_decode_config;
 
-/* sparse_attn_decode with a configuration (NULL = defaults).  SA_ERR_SHAPE
- * for attn_splits outside [0, 1024], topk_path outside the SA_TOPK_* values or
- * nonzero reserved fields; otherwise as sparse_attn_decode. */
+/* sparse_attn_decode with a configuration (NULL = defaults; attn_partners
+ * picks the attention kernel, SA_ATTN_PARTNERS_*).  SA_ERR_SHAPE for
+ * attn_splits outside [0, 1024], topk_path outside the SA_TOPK_* values,
+ * attn_partners outside the SA_ATTN_PARTNERS_* values or nonzero reserved
+ * fields; otherwise as sparse_attn_decode. */
 sa_status sa_decode_workspace_size_cfg(const sa_params *p, int32_t batch, int32_t max_ctx,
                                        const sa_decode_config *cfg, size_t *bytes /* host, out */);
 sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *cache, int32_t batch,

@@ -291,8 +291,12 @@ def test_prefill_varlen_cfg_validation(L):
     assert call(sa.sa_prefill_config(pipeline=2)) == sa.SA_ERR_SHAPE
     assert call(sa.sa_prefill_config(pipeline=-1)) == sa.SA_ERR_SHAPE
     bad = sa.sa_prefill_config()
-    bad.reserved[2] = 1
+    bad.reserved[1] = 1
     assert call(bad) == sa.SA_ERR_SHAPE
+    for partners in (-1, 1, 3, 8):
+        assert call(sa.sa_prefill_config(attn_partners=partners)) == sa.SA_ERR_SHAPE
+    for partners in (sa.SA_ATTN_PARTNERS_2, sa.SA_ATTN_PARTNERS_4):
+        assert call(sa.sa_prefill_config(attn_partners=partners), ws=16) == sa.SA_ERR_WORKSPACE
     assert call(sa.sa_prefill_config(pipeline=sa.SA_PREFILL_PIPELINED), ws=16) == sa.SA_ERR_WORKSPACE
     assert call(None, ws=16) == sa.SA_ERR_WORKSPACE
 
@@ -313,8 +317,12 @@ def test_decode_cfg_and_tune_validation(L):
     assert cfg_call(sa.sa_decode_config(topk_path=-1)) == sa.SA_ERR_SHAPE
     assert cfg_call(sa.sa_decode_config(topk_path=sa.SA_TOPK_ONEPASS_U4 + 1)) == sa.SA_ERR_SHAPE
     bad = sa.sa_decode_config()
-    bad.reserved[1] = 3
+    bad.reserved[0] = 3
     assert cfg_call(bad) == sa.SA_ERR_SHAPE
+    for partners in (-1, 1, 3, 8):
+        assert cfg_call(sa.sa_decode_config(attn_partners=partners)) == sa.SA_ERR_SHAPE
+    for partners in (sa.SA_ATTN_PARTNERS_2, sa.SA_ATTN_PARTNERS_4):
+        assert cfg_call(sa.sa_decode_config(attn_partners=partners), ws=16) == sa.SA_ERR_WORKSPACE
     assert cfg_call(sa.sa_decode_config(topk_path=sa.SA_TOPK_ONEPASS_U4), ws=16) == sa.SA_ERR_WORKSPACE
     assert cfg_call(None, ws=16) == sa.SA_ERR_WORKSPACE
     assert cfg_call(sa.sa_decode_config(attn_splits=7), ws=16) == sa.SA_ERR_WORKSPACE

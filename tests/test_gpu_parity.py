@@ -265,6 +265,67 @@ def test_attention_logit_outgrows_reference(dev):
         compare(w, res, tag=f"decode_outgrow splits {splits}")
 
 
+def run_partners(dev, w, partners, out_bf16=False):
+    """The fused call through the configured entry points with the given
+    attention kernel (SA_ATTN_PARTNERS_*)."""
+    torch, sa = dev
+    d = sa.to_device(w)
+    p = sa.Params.from_shape(w["shape"], out_bf16=out_bf16)
+    if w["mode"] == "decode":
+        res = sa.sparse_attn_decode_cfg(p, d["cache"], int(w["context_lens"].max()), 0, d["q"], d["idx_q"],
+                                        d["idx_w"], attn_partners=partners)
+    elif w["mode"] == "varlen":
+        res = sa.sparse_attn_prefill_varlen(p, d["cache"], w["cu_seqlens"], w["q_starts"], d["q"], d["idx_q"],
+                                            d["idx_w"], attn_partners=partners)
+    else:
+        L = w["q"].shape[0]
+        res = sa.sparse_attn_prefill_varlen(p, d["cache"], [0, L], [w["q_start"]], d["q"], d["idx_q"], d["idx_w"],
+                                            attn_partners=partners)
+    torch.cuda.synchronize()
+    return res
+
+
+def outgrow_case_mla():
+    """outgrow_case on the 576/512 shape: the kept token's latent row is
+    4 q[row, head 0], a head-0 logit of about 4 |q|^2 / 24 (near 100, 140 in
+    log2 units) against a reference max of a few units, so the split is
+    recomputed exactly (its weights overflow fp32 to +inf first)."""
+    w = synth.make(synth.small_decode("decode_outgrow_mla", MLA, [300, 2500], seed=131))
+    kept1 = oracle.run(w, rows=[1])["topk"][0]
+    q = synth.bf16_bits_to_f32(w["q"])
+    kv = w["kv"].copy()
+    for b, pos in ((0, 40), (1, int(kept1[40]))):
+        blk, slot = _key_rows(w, b, [pos])
+        kv[blk[0], slot[0]] = synth.f32_to_bf16_bits(4.0 * q[b, 0])
+    return dict(w, kv=kv)
+
+
+P4_CASES = ["decode_ragged", "decode_k1", "decode_k64_ties", "decode_k3000_splits", "decode_k256_bound",
+            "decode_h48", "decode_h96", "decode_h20", "prefill_2500", "prefill_qstart", "prefill_k4100"]
+
+
+@pytest.mark.parametrize("name", P4_CASES + ["outgrow_mla"])
+def test_attention_partner_kernels(dev, name):
+    """Both attention kernels of the 576/512 shape (two and four partner waves
+    per head block) against the oracle: ragged and empty rows, k = 1 and
+    k > 2048 (several splits), padding tiles, head counts that leave waves
+    without heads (20, 48, 96), rows that carry P as hi + lo, and the exact
+    recompute of a split whose logits outgrow the reference max."""
+    w = outgrow_case_mla() if name == "outgrow_mla" else synth.make(CASES[name]())
+    for partners in (2, 4):
+        say(f"[gpu] attention kernel with {partners} partners: {name}")
+        compare(w, run_partners(dev, w, partners), tag=f"{name} partners {partners}")
+
+
+@pytest.mark.parametrize("name", ["decode_b32_ctx8k", "decode_b64_ctx16k_128k", "decode_b4_ctx1m", "prefill_L32k"])
+def test_attention_four_partners_full_size(dev, name):
+    """The four-partner attention at the benchmark's sizes: every decode row,
+    and the stratified prefill rows (chunk boundaries included)."""
+    say(f"[gpu] four-partner attention, full size {name}")
+    w = synth.make(synth.WORKLOADS[name])
+    compare(w, run_partners(dev, w, 4), rows=FULL_ROWS[name], tag=f"{name} partners 4")
+
+
 def random_decode_spec(seed):
     """A seeded mixed decode case: shape family, head count, k and a batch of
     ragged context lengths (empty rows, rows at k and k + 1, short, medium and,
@@ -677,13 +738,15 @@ def test_decode_tune_then_run(dev):
     d = sa.to_device(w)
     p = sa.Params.from_shape(w["shape"])
     max_ctx = int(w["context_lens"].max())
-    splits, path, us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=3)
-    say(f"  tuned: {splits} splits, top-k path {path}, {us:.1f} us per call")
+    splits, path, partners, us = sa.decode_tune(p, d["cache"], max_ctx, d["q"], d["idx_q"], d["idx_w"], reps=3)
+    say(f"  tuned: {splits} splits, top-k path {path}, attention partners {partners}, {us:.1f} us per call")
     assert 1 <= splits <= 64 and us > 0
     assert path in (sa.SA_TOPK_DEFAULT, sa.SA_TOPK_THRESHOLD, sa.SA_TOPK_ONEPASS_U2, sa.SA_TOPK_ONEPASS_U4)
-    res = sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"], topk_path=path)
+    assert partners in (sa.SA_ATTN_PARTNERS_DEFAULT, sa.SA_ATTN_PARTNERS_2, sa.SA_ATTN_PARTNERS_4)
+    res = sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, splits, d["q"], d["idx_q"], d["idx_w"], topk_path=path,
+                                    attn_partners=partners)
     torch.cuda.synchronize()
-    compare(w, res, tag=f"decode_ragged tuned splits={splits} topk_path={path}")
+    compare(w, res, tag=f"decode_ragged tuned splits={splits} topk_path={path} partners={partners}")
 
 
 TOPK_PATH_CASES = ["decode_ragged", "decode_k1", "decode_k64_ties", "decode_k3000_splits", "decode_tiny_shape",
