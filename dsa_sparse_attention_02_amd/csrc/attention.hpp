@@ -108,13 +108,20 @@ struct AttnShape {
     // LDS image of a 32-token tile.  Main rows: pieces 0..63 of each token
     // (one 1 KiB copy per token), MAIN_STRIDE bytes apart, piece p of token t
     // stored at position p ^ main_swizzle(t).  Tail: the remaining 8 pieces
-    // (128 bytes) of each token, TAIL_STRIDE bytes apart (the extra 16 bytes
-    // move consecutive tokens to different 16-byte bank groups).  Rows shorter
-    // than 64 pieces live in the tail only.
+    // (128 bytes) of each token.  Behind main rows the tail rows are packed
+    // (32 x 128 bytes, so eight tokens' tails are one contiguous kilobyte) with
+    // piece p of token t at position p ^ (t & 7); rows shorter than 64 pieces
+    // live in the tail only, TAIL_STRIDE = 144 bytes apart, unswizzled (the
+    // extra 16 bytes move consecutive tokens to different 16-byte bank groups).
+    // Either way the 16 tokens of a K operand read touch 16 distinct bank
+    // groups.
     static constexpr int MAIN = PIECES >= 64 ? 64 : 0;
     static constexpr int TAIL = PIECES - MAIN;
     static constexpr int MAIN_STRIDE = MAIN * 16;
-    static constexpr int TAIL_STRIDE = TAIL * 16 + 16;
+    static constexpr bool TSWZ = MAIN > 0;
+    static constexpr int TAIL_STRIDE = TSWZ ? TAIL * 16 : TAIL * 16 + 16;
+    // position of tail piece p of tile token t (an involution in p)
+    static __device__ __forceinline__ constexpr int tail_pos(int p, int t) { return TSWZ ? p ^ (t & 7) : p; }
     static constexpr int TAIL_BASE = 32 * MAIN_STRIDE;
     static constexpr int TILE_BYTES = TAIL_BASE + 32 * TAIL_STRIDE;
     static constexpr int COPIES_PER_TOKEN = (MAIN ? 1 : 0) + 1;  // main row, tail
@@ -302,34 +309,62 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     // Per token: a buffer resource over its latent row (a zero row for padding
     // tokens and for tiles at or past nt_eff), then the main-row copy (64 lanes
     // x 16 bytes) and the tail copy (lanes 0..7 x 16 bytes), both buffer-form
-    // LDS-DMA.  The memory counter of every wave thus advances by DMA_W per
-    // tile.
-    constexpr int DMA_W = TOK_W * S::COPIES_PER_TOKEN;
+    // LDS-DMA.  With packed tail rows (TLOAD), the tile loop moves the tails
+    // differently: wave w loads those of tokens TOK_W w .. TOK_W w + TOK_W - 1
+    // into registers, eight tokens per 64-lane load (lane L: token 8 j + L / 8,
+    // position L % 8), and stores them into LDS one tile later; its copies then
+    // move main rows only, so a tile costs TOK_W + TOK_W / 8 memory instructions
+    // per wave instead of 2 TOK_W and the tails need no per-token lane mask.
+    // Every wave's memory counter thus advances by DMA_W per loop tile (PDMA_W
+    // per tile copied whole: the first three and the exact recompute's).
+    constexpr bool TLOAD = S::TSWZ && TOK_W % 8 == 0;
+    constexpr int NTL = TLOAD ? TOK_W / 8 : 0;
+    constexpr int PDMA_W = TOK_W * S::COPIES_PER_TOKEN;
+    constexpr int DMA_W = TLOAD ? TOK_W + NTL : PDMA_W;
     const uint64_t kv_addr = reinterpret_cast<uint64_t>(a.kv);
     uint64_t zero_addr = reinterpret_cast<uint64_t>(kZeroLatentRow);
     asm volatile("" : "+s"(zero_addr));  // keep the address in registers, out of the copy code
     // 64-bit address of the latent row of token lane % 32 of tile tn (the zero
     // row for padding and for tiles at or past nt_eff), computed for all 32
     // tokens at once; each copy then reads its token's address from a lane.
-    auto tile_base = [&](int tn) -> uint64_t {
-        const uint32_t v = rows[max(0, min(tn, kAttnMaxSplitTokens / 32 - 1)) * 32 + (lane & 31)];
+    // tile_row reads the tile's table entries (ahead of use), row_base forms the
+    // addresses.
+    auto tile_row = [&](int tn, int tok) -> uint32_t {
+        return rows[max(0, min(tn, kAttnMaxSplitTokens / 32 - 1)) * 32 + tok];
+    };
+    auto row_base = [&](int tn, uint32_t v) -> uint64_t {
         const uint32_t row = tn >= 0 && tn < nt_eff ? v : kNoRow;
         return row != kNoRow ? kv_addr + (uint64_t)row * (QK * 2) : zero_addr;
     };
+    auto tile_base = [&](int tn) -> uint64_t { return row_base(tn, tile_row(tn, lane & 31)); };
     auto buffer_base = [&](int buf) { return (SA_LDS uint8_t *)opaque_lds((SA_LDS uint8_t *)&tile[buf][0]); };
-    auto copy_token = [&](uint64_t mybase, int n, SA_LDS uint8_t *dstb) {
+    auto copy_token = [&](uint64_t mybase, int n, SA_LDS uint8_t *dstb, auto with_tail) {
         const int ii = wave + NW * n;  // wave-uniform
         const uint64_t base = ((uint64_t)lane_read((uint32_t)(mybase >> 32), ii) << 32) | lane_read((uint32_t)mybase, ii);
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const void *>(base), QK * 2);
         if constexpr (S::MAIN > 0)  // lane i fetches the piece stored at position i
             buf_dma16_to_lds(rs, (lane * 16) ^ (16 * main_swizzle(ii)), dstb + ii * S::MAIN_STRIDE);
-        if (lane < 8) buf_dma16_to_lds(rs, S::MAIN * 16 + lane * 16, dstb + S::TAIL_BASE + ii * S::TAIL_STRIDE);
+        if constexpr (decltype(with_tail)::value)
+            if (lane < 8)  // lane i fetches the tail piece stored at position i
+                buf_dma16_to_lds(rs, S::MAIN * 16 + 16 * S::tail_pos(lane, ii),
+                                 dstb + S::TAIL_BASE + ii * S::TAIL_STRIDE);
     };
+    constexpr std::true_type kWithTail{};
+    constexpr std::integral_constant<bool, !TLOAD> kLoopTail{};
     auto issue_tile = [&](int tn, int buf) {
         const uint64_t mybase = tile_base(tn);
         SA_LDS uint8_t *dstb = buffer_base(buf);
 #pragma unroll
-        for (int n = 0; n < TOK_W; ++n) copy_token(mybase, n, dstb);
+        for (int n = 0; n < TOK_W; ++n) copy_token(mybase, n, dstb, kWithTail);
+    };
+    // packed tails (TLOAD): table entry, source and LDS slot of load j
+    auto tail_tok = [&](int j) { return TOK_W * wave + 8 * j + (lane >> 3); };
+    auto tail_src = [&](int tn, uint32_t v) -> uint64_t {
+        return row_base(tn, v) + S::MAIN * 16 + 16 * S::tail_pos(lane & 7, lane >> 3);
+    };
+    auto tail_slot = [&](int buf, int j) -> SA_LDS u32x4 * {
+        return (SA_LDS u32x4 *)((SA_LDS uint8_t *)&tile[buf][0] + S::TAIL_BASE + (TOK_W * wave + 8 * j) * S::TAIL_STRIDE) +
+               lane;
     };
 
     // Exchange slot j (of 4, 16 bytes per lane) of the partial that wave `reader`
@@ -355,7 +390,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         const int tok = row_token(c);
         return 2 * ks < S::MAIN
                    ? tok * S::MAIN_STRIDE + ((32 * (ks & 7) + 16 * hf) ^ (16 * main_swizzle(tok))) + 256 * (ks >> 3)
-                   : S::TAIL_BASE + tok * S::TAIL_STRIDE + 16 * (2 * ks - S::MAIN + hf);
+                   : S::TAIL_BASE + tok * S::TAIL_STRIDE + 16 * S::tail_pos(2 * ks - S::MAIN + hf, tok);
     };
     constexpr int KPF = SA_ATTN_KPF, VPF = SA_ATTN_VPF;
     auto lane_id = [&]() { return lane; };
@@ -422,9 +457,13 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
                 return fmaxf(__uint_as_float(rr[0]), __uint_as_float(rr[1]));
             };
             if (st.set_ref) {
+                // (each branch tests the bits of its own opaque copy of vb, so
+                // that the tests stay inside the rarely taken branches)
+                uint32_t vbx = st.vb;
+                asm volatile("" : "+v"(vbx));
                 float mv = -INFINITY;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) mv = fmaxf(mv, valid_bit(st.vb, i) ? st.s[i] : -INFINITY);
+                for (int i = 0; i < 16; ++i) mv = fmaxf(mv, valid_bit(vbx, i) ? st.s[i] : -INFINITY);
                 m = halves_max(mv) * a.scale_log2;
             }
             st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every weight is 0
@@ -436,9 +475,12 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             uint32_t hi = pack_bf16x2(e[0], e[1]);
             uint32_t keep = 0xFFFFFFFFu;
             if (!st.full) {
-                keep = (valid_bit(st.vb, 2 * j) ? 0x0000FFFFu : 0u) | (valid_bit(st.vb, 2 * j + 1) ? 0xFFFF0000u : 0u);
-                e[0] = valid_bit(st.vb, 2 * j) ? e[0] : 0.0f;
-                e[1] = valid_bit(st.vb, 2 * j + 1) ? e[1] : 0.0f;
+                uint32_t vbx = st.vb;
+                asm volatile("" : "+v"(vbx));
+                const bool v0 = valid_bit(vbx, 2 * j), v1 = valid_bit(vbx, 2 * j + 1);
+                keep = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
+                e[0] = v0 ? e[0] : 0.0f;
+                e[1] = v1 ? e[1] : 0.0f;
                 hi &= keep;
             }
             st.w[j >> 2][j & 3] = hi;
@@ -511,27 +553,35 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
     //     partials, tile t's weights, and the copies of tile t+3 into the
     //     buffer of tile t-1 (each wave refills only rows it has just read);
     //   O += V P of tile t;
-    //   wait for this wave's copies of tile t+2 (only tile t+3's are younger:
-    //     every wave issues DMA_W per tile, and copies complete in order);
+    //   wait for this wave's copies of tile t+2 (only tile t+3's main-row
+    //     copies are younger: memory operations complete in order);
+    //   with packed tails, store tile t+2's tails and load tile t+3's;
     //   barrier B: every wave is done with tile t, whose buffer then takes the
     //     partials of tile t+1.
     // Tiles of padding only are not computed (block-uniform); the last
     // iteration computes the (unused) partial of an all-padding tile.
     auto tiles = [&](auto cfg) {
         static_assert(NB == 4, "the ring below holds two read tiles and two in flight");
-        constexpr int W1 = DMA_W < 63 ? DMA_W : 63;
-        constexpr int W2 = 2 * DMA_W < 63 ? 2 * DMA_W : 63;
+        // W1: the copies younger than tile t+2's at the ring wait (tile t+3's
+        // main rows; its packed tails are loaded after that wait)
+        constexpr int W1 = (TLOAD ? TOK_W : DMA_W) < 63 ? (TLOAD ? TOK_W : DMA_W) : 63;
+        constexpr int P1 = PDMA_W < 63 ? PDMA_W : 63, P2 = 2 * PDMA_W < 63 ? 2 * PDMA_W : 63;
         issue_tile(0, 0);
         issue_tile(1, 1);
         issue_tile(2, 2);
         f32x16 sp = f32x16{};
         if (nt_eff > 0) {
-            attn_wait_vmcnt<W2>();
+            attn_wait_vmcnt<P2>();
             barrier_lds();
             sp = qk_half(cfg, 0, no_fill);
             xch_write(NB - 1, sp);
-            attn_wait_vmcnt<W1>();
+            attn_wait_vmcnt<P1>();
         }
+        // table entries of the next tile to copy, read a tile ahead
+        uint32_t vnext = tile_row(3, lane & 31), vtail[NTL > 0 ? NTL : 1];
+        u32x4 tails[NTL > 0 ? NTL : 1];  // packed tails loaded in the previous iteration
+#pragma unroll
+        for (int j = 0; j < NTL; ++j) vtail[j] = tile_row(3, tail_tok(j));
         for (int t = 0; t < nt_eff; ++t) {
             barrier_lds();  // A
             const int xb = (t + NB - 1) % NB;
@@ -540,7 +590,8 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             for (int j = 0; j < 4; ++j) pr[j] = *xslot(xb, wave, j);
             SmState st;
             sm_begin(st, t, t == t_ref);
-            const uint64_t nbase = tile_base(t + 3);
+            const uint64_t nbase = row_base(t + 3, vnext);
+            vnext = tile_row(t + 4, lane & 31);
             SA_LDS uint8_t *dstb = buffer_base(xb);
             constexpr int kAdd = KP > 2 ? 2 : 0;  // q.k step after which the partials are summed
             f32x16 sn = qk_half(cfg, (t + 1) % NB, [&](int ks) {
@@ -551,17 +602,30 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
                         st.s[i] = decltype(cfg)::PX == 0 ? sp[i] + pr[i >> 2][i & 3] : pr[i >> 2][i & 3] + sp[i];
                 }
                 // the copies of tile t+3, after the partials have been read
-                if (ks > kAdd && ks - kAdd - 1 < TOK_W) copy_token(nbase, ks - kAdd - 1, dstb);
+                if (ks > kAdd && ks - kAdd - 1 < TOK_W) copy_token(nbase, ks - kAdd - 1, dstb, kLoopTail);
                 if (ks > kAdd && ks - kAdd - 1 < kSmSteps) sm_step(cfg, st, ks - kAdd - 1);
             });
             // (q.k steps too few to hold every copy or softmax step: the rest here)
 #pragma unroll
-            for (int n = KP - kAdd - 1; n < TOK_W; ++n) copy_token(nbase, n, dstb);
+            for (int n = KP - kAdd - 1; n < TOK_W; ++n) copy_token(nbase, n, dstb, kLoopTail);
 #pragma unroll
             for (int step = KP - kAdd - 1; step < kSmSteps; ++step) sm_step(cfg, st, step);
             pv(cfg, t % NB, st);
             sp = sn;
             attn_wait_vmcnt<W1>();
+            // the packed tails of tile t+2 (loaded at the end of the previous
+            // iteration; the first three tiles were copied whole) into its
+            // buffer, read from the next iteration on; then the loads of tile
+            // t+3's, which have a whole iteration to arrive
+            if (t > 0) {
+#pragma unroll
+                for (int j = 0; j < NTL; ++j) *tail_slot((t + 2) % NB, j) = tails[j];
+            }
+#pragma unroll
+            for (int j = 0; j < NTL; ++j) {
+                tails[j] = load16_global(tail_src(t + 3, vtail[j]));
+                vtail[j] = tile_row(t + 4, tail_tok(j));
+            }
             barrier_lds();  // B
             xch_write(t % NB, sp);
         }

@@ -180,7 +180,8 @@ __global__ __launch_bounds__(256 * HB, 1) void attend_p4_kernel(const AttnArgs a
         const uint64_t base = ((uint64_t)lane_read((uint32_t)(mybase >> 32), ii) << 32) | lane_read((uint32_t)mybase, ii);
         const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(reinterpret_cast<const void *>(base), QK * 2);
         buf_dma16_to_lds(rs, (lane * 16) ^ (16 * main_swizzle(ii)), dstb + ii * S::MAIN_STRIDE);
-        if (lane < 8) buf_dma16_to_lds(rs, S::MAIN * 16 + lane * 16, dstb + S::TAIL_BASE + ii * S::TAIL_STRIDE);
+        if (lane < 8)
+            buf_dma16_to_lds(rs, S::MAIN * 16 + 16 * S::tail_pos(lane, ii), dstb + S::TAIL_BASE + ii * S::TAIL_STRIDE);
     };
     auto issue_tile = [&](int tn, int buf) {
         const uint64_t mybase = tile_base(tn);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(256 * HB, 1) void attend_p4_kernel(const AttnArgs a
         const int tok = row_token(c);
         return 2 * ks < S::MAIN
                    ? tok * S::MAIN_STRIDE + ((32 * (ks & 7) + 16 * hf) ^ (16 * main_swizzle(tok))) + 256 * (ks >> 3)
-                   : S::TAIL_BASE + tok * S::TAIL_STRIDE + 16 * (2 * ks - S::MAIN + hf);
+                   : S::TAIL_BASE + tok * S::TAIL_STRIDE + 16 * S::tail_pos(2 * ks - S::MAIN + hf, tok);
     };
     constexpr int KPF = SA_ATTN_KPF < KP ? SA_ATTN_KPF : KP, VPF = SA_ATTN_VPF;
     auto lane_id = [&]() { return lane; };
