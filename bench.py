@@ -193,6 +193,17 @@ def supplementary_decode(args, torch, sa, synth, c):
         res["decode_tuned"] = {"attn_splits": splits, "topk_path": TOPK_PATHS[path], "attn_partners": partners,
                                "ms_per_step": round(ms, 4), "tokens_per_s": round(B / (ms / 1e3), 1)}
         del wst
+    if args.partners_steps > 0:
+        # both attention kernels (two or four partner waves per head block),
+        # interleaved over three rounds
+        times = {2: [], 4: []}
+        for _ in range(3):
+            for n in times:
+                f = lambda n=n: sa.sparse_attn_decode_cfg(p, d["cache"], max_ctx, 0, d["q"], d["idx_q"], d["idx_w"],
+                                                          attn_partners=n, workspace=ws, outputs=outs)
+                times[n].append(time_back_to_back(torch, f, args.partners_steps, 10))
+        res["decode_partners"] = {f"{n}_partners_ms_per_step": round(sorted(v)[1], 4) for n, v in times.items()}
+        log(f"attention kernels (median of 3 rounds): {res['decode_partners']}")
     if args.blocks_steps > 0:
         from dataclasses import replace
         sh = w["shape"]
@@ -332,6 +343,13 @@ def run_prefill(args, torch, sa, synth, name="prefill_L32k"):
                                                             workspace=wsv, outputs=outs, pipeline=code)
         sched[sname] = round(time_back_to_back(torch, f, steps, 1), 3)
     res["schedules_ms_per_step"] = sched
+    if args.partners_steps > 0:
+        part = {}
+        for n in (2, 4):
+            f = lambda n=n: sa.sparse_attn_prefill_varlen(p, d["cache"], cu, qs, d["q"], d["idx_q"], d["idx_w"],
+                                                          workspace=wsv, outputs=outs, attn_partners=n)
+            part[f"{n}_partners"] = round(time_back_to_back(torch, f, steps, 1), 3)
+        res["attention_partners_ms_per_step"] = part
     log(f"{spec.name}: {ms:.2f} ms/step, stages {res['stages_ms']}; plain calls {sched}")
     return res
 
@@ -463,6 +481,8 @@ def main():
     ap.add_argument("--no-tune", dest="tune", action="store_false",
                     help="skip the run-time tuning of the attention split count and top-k path (sa_decode_tune)")
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--partners-steps", type=int, default=20,
+                    help="steps per round timing both attention kernels (two or four partner waves), 0 = skip")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-peaks", action="store_true", help="skip the HBM / MFMA / LDS peak probe")
     ap.add_argument("--other-workloads", default="decode_b32_ctx8k,decode_b4_ctx1m,decode_b64_ctx128k_full",
