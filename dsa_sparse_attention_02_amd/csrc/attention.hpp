@@ -437,6 +437,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         uint32_t vb;
         bool full, set_ref;  // (workgroup-uniform) every token valid; the tile fixes the reference
         u32x4 w[2], wl[2];
+        float lt, let;       // the tile's sums of the rounded and of the unrounded weights
     };
     constexpr int kSmSteps = 9;
     auto sm_begin = [&](SmState &st, int t, bool set_ref) {
@@ -444,8 +445,36 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
         st.full = __builtin_amdgcn_readfirstlane(bits) == 0xFFFFFFFFu;
         st.set_ref = set_ref;
         st.vb = bits >> (8 * half);
+        st.lt = 0.0f;
+        st.let = 0.0f;
     };
     auto valid_bit = [&](uint32_t vb, int i) { return ((vb >> (16 * (i >> 3) + (i & 7))) & 1u) != 0; };
+    // Weights of pair j (registers 2j, 2j + 1): exponentiated, rounded, summed
+    // into the tile's sums; with `masked`, padding tokens weigh 0.  The
+    // normaliser sums the same rounded weights the MFMA multiplies V by, so the
+    // output is an exact weighted mean of the kept rows up to fp32 accumulation.
+    auto sm_pair = [&](auto cfg, SmState &st, int j, bool masked) {
+        float e[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) e[h] = exp2_hw(fmaf(st.s[2 * j + h], a.scale_log2, -st.mref));
+        uint32_t hi = pack_bf16x2(e[0], e[1]);
+        uint32_t keep = 0xFFFFFFFFu;
+        if (masked) {
+            const bool v0 = valid_bit(st.vb, 2 * j), v1 = valid_bit(st.vb, 2 * j + 1);
+            keep = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
+            e[0] = v0 ? e[0] : 0.0f;
+            e[1] = v1 ? e[1] : 0.0f;
+            hi &= keep;
+        }
+        st.w[j >> 2][j & 3] = hi;
+        st.let += e[0] + e[1];
+        if constexpr (decltype(cfg)::PREC) {
+            const uint32_t lo = pack_bf16x2(e[0] - bf16_lo_to_f32(hi), e[1] - bf16_hi_to_f32(hi)) & keep;
+            st.wl[j >> 2][j & 3] = lo;
+            st.lt = add_bf16_pair(lo, st.lt);
+        }
+        st.lt = add_bf16_pair(hi, st.lt);
+    };
     // Padding tokens have zero latent rows, so their logits are 0: the
     // reference max and the weights leave them out.
     auto sm_step = [&](auto cfg, SmState &st, int step) {
@@ -468,33 +497,24 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             }
             st.mref = m == -INFINITY ? 0.0f : m;  // still no valid token: every weight is 0
         } else if (step < kSmSteps) {
-            const int j = step - 1;
-            float e[2];
-#pragma unroll
-            for (int h = 0; h < 2; ++h) e[h] = exp2_hw(fmaf(st.s[2 * j + h], a.scale_log2, -st.mref));
-            uint32_t hi = pack_bf16x2(e[0], e[1]);
-            uint32_t keep = 0xFFFFFFFFu;
-            if (!st.full) {
-                uint32_t vbx = st.vb;
-                asm volatile("" : "+v"(vbx));
-                const bool v0 = valid_bit(vbx, 2 * j), v1 = valid_bit(vbx, 2 * j + 1);
-                keep = (v0 ? 0x0000FFFFu : 0u) | (v1 ? 0xFFFF0000u : 0u);
-                e[0] = v0 ? e[0] : 0.0f;
-                e[1] = v1 ? e[1] : 0.0f;
-                hi &= keep;
-            }
-            st.w[j >> 2][j & 3] = hi;
-            le += e[0] + e[1];
-            if constexpr (decltype(cfg)::PREC) {
-                const uint32_t lo = pack_bf16x2(e[0] - bf16_lo_to_f32(hi), e[1] - bf16_hi_to_f32(hi)) & keep;
-                st.wl[j >> 2][j & 3] = lo;
-                l = add_bf16_pair(lo, l);
-            }
-            // the normaliser sums the same rounded weights the MFMA multiplies V
-            // by, so the output is an exact weighted mean of the kept rows up to
-            // fp32 accumulation
-            l = add_bf16_pair(hi, l);
+            sm_pair(cfg, st, step - 1, false);
         }
+    };
+    // Steps 1..8 take every token as valid; sm_end redoes a tile holding
+    // padding with the validity mask (one uniform branch per tile instead of
+    // one per pair), then adds the tile's sums to the wave's.
+    auto sm_end = [&](auto cfg, SmState &st) {
+        if (!st.full) {
+            uint32_t vbx = st.vb;  // (opaque: the bit tests stay inside this branch)
+            asm volatile("" : "+v"(vbx));
+            st.vb = vbx;
+            st.lt = 0.0f;
+            st.let = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) sm_pair(cfg, st, j, true);
+        }
+        l += st.lt;
+        le += st.let;
     };
     // O^T += V^T P^T over the tile's two 16-token halves: step q = (k2, vt)
     // multiplies output tile vt (value columns 32vt..32vt+31 of this partner's
@@ -610,6 +630,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
             for (int n = KP - kAdd - 1; n < TOK_W; ++n) copy_token(nbase, n, dstb, kLoopTail);
 #pragma unroll
             for (int step = KP - kAdd - 1; step < kSmSteps; ++step) sm_step(cfg, st, step);
+            sm_end(cfg, st);
             pv(cfg, t % NB, st);
             sp = sn;
             attn_wait_vmcnt<W1>();
@@ -677,6 +698,7 @@ __global__ __launch_bounds__(128 * HB, 1) void attend_kernel(const AttnArgs a)
                 sm_begin(st, t, false);
 #pragma unroll
                 for (int step = 0; step < kSmSteps; ++step) sm_step(cfg, st, step);  // (s <= m now)
+                sm_end(cfg, st);
                 pv(cfg, 0, st);
                 __syncthreads();
             }
