@@ -27,13 +27,15 @@
 // per (row, split), one wave per SIMD (the tile ring takes 158 KB of LDS).  Per
 // tile of 32 kept tokens:
 //   * the 32 latent rows are copied HBM -> LDS by buffer-form LDS-DMA, one
-//     resource per token row: a 64-lane copy of its first 1 KiB and an 8-lane
-//     copy of its 128-byte tail; the main rows' 16-byte pieces are XOR-swizzled
-//     by token (through the copy's per-lane source offsets) so that MFMA
-//     operand reads do not collide on LDS banks; a ring of 4 tile buffers keeps
-//     two tiles' copies in flight while one tile's values and the next tile's
-//     keys are read, and the copies of tile t + 3 are issued between the q.k
-//     MFMAs of tile t + 1, beside the softmax of tile t;
+//     resource per token row and a 64-lane copy of its first 1 KiB; the 128-byte
+//     rope tails go with each token's copy (an 8-lane copy) for tiles copied
+//     whole, and in the tile loop as one 64-lane vector load per eight tokens,
+//     stored into LDS a tile later; the main rows' and the tails' 16-byte pieces
+//     are XOR-swizzled by token (through the per-lane source offsets) so that
+//     MFMA operand reads do not collide on LDS banks; a ring of 4 tile buffers
+//     keeps two tiles' copies in flight while one tile's values and the next
+//     tile's keys are read, and the copies of tile t + 3 are issued between the
+//     q.k MFMAs of tile t + 1, beside the softmax of tile t;
 //   * partial S^T[token][head] = K . Q^T on 32x32x16 bf16 MFMAs (K from LDS,
 //     Q^T from registers, contraction over the partner's QK half in 16-wide
 //     steps), exchanged through LDS and summed;
