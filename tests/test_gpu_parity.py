@@ -304,14 +304,20 @@ P4_CASES = ["decode_ragged", "decode_k1", "decode_k64_ties", "decode_k3000_split
             "decode_h48", "decode_h96", "decode_h20", "prefill_2500", "prefill_qstart", "prefill_k4100"]
 
 
-@pytest.mark.parametrize("name", P4_CASES + ["outgrow_mla"])
+@pytest.mark.parametrize("name", P4_CASES + ["outgrow_mla", "varlen_mla_mixed", "varlen_k3000_splits"])
 def test_attention_partner_kernels(dev, name):
     """Both attention kernels of the 576/512 shape (two and four partner waves
     per head block) against the oracle: ragged and empty rows, k = 1 and
     k > 2048 (several splits), padding tiles, head counts that leave waves
-    without heads (20, 48, 96), rows that carry P as hi + lo, and the exact
-    recompute of a split whose logits outgrow the reference max."""
-    w = outgrow_case_mla() if name == "outgrow_mla" else synth.make(CASES[name]())
+    without heads (20, 48, 96), rows that carry P as hi + lo, the exact
+    recompute of a split whose logits outgrow the reference max, and several
+    sequences in one prefill call (with and without split attention)."""
+    if name == "outgrow_mla":
+        w = outgrow_case_mla()
+    elif name.startswith("varlen"):
+        w = synth.make(VARLEN_CASES[name]())
+    else:
+        w = synth.make(CASES[name]())
     for partners in (2, 4):
         say(f"[gpu] attention kernel with {partners} partners: {name}")
         compare(w, run_partners(dev, w, partners), tag=f"{name} partners {partners}")
