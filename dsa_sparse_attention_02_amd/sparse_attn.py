@@ -489,8 +489,7 @@ def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_spli
         decode_workspace_size_cfg(p, B, max_ctx, attn_splits, topk_path), q.device)
     _check(lib().sparse_attn_decode_cfg(ctypes.byref(p.c()), ctypes.byref(cache.c()), B, max_ctx,
                                         ctypes.byref(_cfg(attn_splits, topk_path, attn_partners)), q.data_ptr(),
-                                        idx_q.data_ptr(),
-                                        idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
+                                        idx_q.data_ptr(), idx_w.data_ptr(), topk_idx.data_ptr(), out.data_ptr(), _ptr(lse),
                                         ws.data_ptr(), ws.numel(), _stream(stream)), "sparse_attn_decode_cfg")
     return topk_idx, out, lse
 
@@ -498,8 +497,7 @@ def sparse_attn_decode_cfg(p: Params, cache: PagedCache, max_ctx: int, attn_spli
 def decode_tune(p: Params, cache: PagedCache, max_ctx: int, q, idx_q, idx_w, *, reps=10, stream=None):
     """Run-time tuning of the decode split count, top-k path and attention
     kernel on these inputs (waits for the stream).  Returns (attn_splits,
-    topk_path, attn_partners,
-    microseconds per call)."""
+    topk_path, attn_partners, microseconds per call)."""
     torch = _torch()
     B = q.shape[0]
     n = ctypes.c_size_t()

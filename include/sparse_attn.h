@@ -309,7 +309,7 @@ sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged
 /* ----------------------------------------------------- run-time tuning --
  * Kernel tuning at run time (the page on the compute software stack names
  * auto-tuning of block sizes and unrolling at run time as the next step for
- * sparse attention operators).  Two tunables:
+ * sparse attention operators).  Three tunables:
  *   attn_splits: the number of splits of each decode row's k keys across
  *                attention workgroups (merged afterwards).  0 = the library's
  *                choice (one attention workgroup per compute unit over the
@@ -327,6 +327,8 @@ sa_status sparse_attn_prefill_varlen_profiled(const sa_params *p, const sa_paged
  *                selected; 2 or 4 rounds of 4 KB loads in flight per wave, two
  *                compiled variants of the gather loop).  The kept indices are
  *                the same, bit for bit, on every path.
+ *   attn_partners: the attention kernel (SA_ATTN_PARTNERS_*, above); results
+ *                differ only in floating-point rounding.
  * The best choice depends on the context lengths, the batch and the cache's
  * placement, which only a run on the caller's data measures.
  */
@@ -354,7 +356,8 @@ sa_status sparse_attn_decode_cfg(const sa_params *p, const sa_paged_cache *cache
                                  float *lse, void *workspace, size_t workspace_bytes, void *stream);
 /* Times sparse_attn_decode_cfg on the given inputs for every split count the
  * plan can realise (up to 64) under the default top-k, then every top-k path
- * under the fastest count: one untimed call, then `reps` (1..1000) calls
+ * under the fastest count, then (576/512 shape) the other attention kernel
+ * under both: one untimed call, then `reps` (1..1000) calls
  * between two HIP events on `stream`, per configuration; writes the fastest
  * into *best (and its mean microseconds per call into *best_us when non-NULL).
  * Unlike every other call it creates two HIP events, waits for the stream
