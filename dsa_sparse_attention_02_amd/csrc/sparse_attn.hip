@@ -111,7 +111,10 @@ struct AttnLaunch {
 constexpr int kDefaultPartners = SA_DEFAULT_PARTNERS;
 
 // SA_ATTN_PARTNERS_*: 0 takes the default
-static bool valid_partners(int v) { return v == SA_ATTN_PARTNERS_DEFAULT || v == SA_ATTN_PARTNERS_2 || v == SA_ATTN_PARTNERS_4; }
+static bool valid_partners(int v)
+{
+    return v == SA_ATTN_PARTNERS_DEFAULT || v == SA_ATTN_PARTNERS_2 || v == SA_ATTN_PARTNERS_4;
+}
 
 AttnLaunch attn_launch(const sa_params *p, int partners = kDefaultPartners)
 {
